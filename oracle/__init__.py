@@ -1,0 +1,143 @@
+"""fp64 CPU oracle for the scalar-decay multi-head SSM forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+CPU-baseline leg of the benchmark may import this package.  The GPU product path
+never calls it and shares no code with it.
+
+The heavy lifting is the C recurrence in ``ssd_oracle.c`` (loaded with ctypes);
+this module only converts arrays to contiguous fp64 and back.  Inputs given in
+bf16 or fp32 are upcast exactly, so the oracle sees the very values the GPU
+sees.
+
+``forward`` follows the literal recurrence of the "Mamba 2 -- Transformers are
+SSMs" paper story (ai.tomabc.com), section 3.1: ``h_t = a_t h_{t-1} +
+Delta_t B_t x_t^T``, ``y_t = C_t^T h_t`` (+ ``D x_t``), with ``a_t =
+exp(Delta_t A)``; ``chunk_cumsum`` gives Delta and the within-chunk cumulative
+log-decay.  See ``ssd_oracle.c`` for every reading taken where the pages are
+silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .build import LIB, build_oracle
+
+_lib = None
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("dt_softplus", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+        ("initial_states", ctypes.c_void_p), ("seq_idx", ctypes.c_void_p),
+        ("nseq", ctypes.c_int64), ("unit_mask", ctypes.c_void_p),
+        ("chunk", ctypes.c_int64), ("chunk_local", ctypes.c_int32),
+        ("y", ctypes.c_void_p), ("final_states", ctypes.c_void_p),
+        ("chunk_end_states", ctypes.c_void_p),
+    ]
+
+
+def load():
+    """Load ``libssd_oracle.so``, compiling it first only if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build_oracle()
+        lib = ctypes.CDLL(LIB)
+        lib.ssd_oracle_forward.argtypes = [ctypes.POINTER(_Args)]
+        lib.ssd_oracle_forward.restype = ctypes.c_int
+        lib.ssd_oracle_chunk_cumsum.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 4
+        lib.ssd_oracle_chunk_cumsum.restype = ctypes.c_int
+        lib.ssd_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(load().ssd_oracle_max_threads())
+
+
+def _f64(a) -> np.ndarray:
+    """Exact upcast of a numpy array or CPU torch tensor (any float dtype) to fp64."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor (bf16 has no numpy dtype: go through fp32, exact)
+        import torch
+        a = a.detach().to("cpu")
+        if a.dtype == torch.bfloat16 or a.dtype == torch.float16:
+            a = a.to(torch.float32)
+        a = a.numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+@dataclass
+class OracleResult:
+    y: np.ndarray                      # [b,T,H,P]
+    final_states: Optional[np.ndarray]  # [b,H,P,N] or [nseq,H,P,N]
+    chunk_end_states: Optional[np.ndarray]  # [b,nc,H,P,N]
+
+
+def forward(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, nseq=None,
+            dt_softplus=True, chunk=0, chunk_local=False, want_chunk_states=False,
+            unit_mask=None) -> OracleResult:
+    """Run the recurrence.  Shapes: x[b,T,H,P], dt[b,T,H], A[H], B,C[b,T,G,N].
+
+    ``unit_mask`` ([b,H] bool, optional) restricts the work to sampled (b, h)
+    pairs; outputs of the others are left at zero.
+    """
+    x, dt, A, B, C = map(_f64, (x, dt, A, B, C))
+    D = _f64(D)
+    init = _f64(initial_states)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, T, H) and A.shape == (H,)
+    assert B.shape == (b, T, G, N) and C.shape == (b, T, G, N)
+    sidx = None
+    if seq_idx is not None:
+        if hasattr(seq_idx, "detach"):
+            seq_idx = seq_idx.detach().cpu().numpy()
+        sidx = np.ascontiguousarray(np.asarray(seq_idx).reshape(-1), dtype=np.int32)
+        assert sidx.shape == (T,) and b == 1
+        if nseq is None:
+            nseq = int(sidx.max()) + 1
+    mask = None
+    if unit_mask is not None:
+        mask = np.ascontiguousarray(np.asarray(unit_mask, dtype=np.uint8).reshape(b * H))
+    y = np.zeros((b, T, H, P), np.float64)
+    fs = np.zeros(((nseq if sidx is not None else b), H, P, N), np.float64)
+    nc = (T + chunk - 1) // chunk if chunk > 0 else 0
+    ces = np.zeros((b, nc, H, P, N), np.float64) if want_chunk_states else None
+    args = _Args(b, T, H, P, N, G, int(bool(dt_softplus)),
+                 _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(sidx),
+                 int(nseq or 0), _ptr(mask), int(chunk), int(bool(chunk_local)),
+                 _ptr(y), _ptr(fs), _ptr(ces))
+    rc = load().ssd_oracle_forward(ctypes.byref(args))
+    if rc != 0:
+        raise ValueError(f"ssd_oracle_forward failed with status {rc}")
+    return OracleResult(y, fs, ces)
+
+
+def chunk_cumsum(dt, A, chunk, dt_softplus=True):
+    """Delta and within-chunk inclusive cumsum of Delta*A, both [b,H,nc,Q] fp64."""
+    dt, A = _f64(dt), _f64(A)
+    b, T, H = dt.shape
+    nc = (T + chunk - 1) // chunk
+    delta = np.zeros((b, H, nc, chunk), np.float64)
+    cs = np.zeros((b, H, nc, chunk), np.float64)
+    rc = load().ssd_oracle_chunk_cumsum(b, T, H, chunk, int(bool(dt_softplus)),
+                                        _ptr(dt), _ptr(A), _ptr(delta), _ptr(cs))
+    if rc != 0:
+        raise ValueError(f"ssd_oracle_chunk_cumsum failed with status {rc}")
+    return delta, cs
