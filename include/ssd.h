@@ -1,0 +1,168 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) chunked SSD forward library, libssd.so.
+ *
+ * The operation is the Mamba-2 "structured state space duality" forward pass for
+ * a scalar-decay, multi-head SSM.  Per batch row, head h (group g = h*G/H) and
+ * token t:
+ *
+ *     Delta_t = softplus(dt_t)   (or dt_t when dt_softplus == 0)
+ *     a_t     = exp(Delta_t * A_h)
+ *     h_t     = a_t * h_{t-1} + Delta_t * x_t B_t^T        state [P][N]
+ *     y_t     = h_t C_t + D_h * x_t                        output [P]
+ *
+ * with h_{-1} = initial_states (or zero).  Sources: the recurrence and output are
+ * section 3.1 (scalar A) of the "Mamba 2 -- Transformers are SSMs" paper story
+ * (ai.tomabc.com); heads are its section 5.1; a_t = exp(Delta_t A) is the
+ * zero-order-hold decay of the Transformer->Mamba page (answer.freetools.me,
+ * "连续到离散：零阶保持") and of "SSM 家族全景图（下）：Mamba-2 与 Jamba"
+ * (scwacadex); the D skip term is the continuous SSM equation of the
+ * answer.freetools.me page; packed sequences reset the state at boundaries
+ * (A_t = 0) per section 4.2 of "Transformers与SSMs的隐藏联系" (jsqmd.com).
+ *
+ * It is computed with the four-step chunked (block-decomposition) algorithm of
+ * "SSM 家族全景图（下）" section 3.4 and "Mamba 2 -- Transformers are SSMs"
+ * section 4.1: chunk outputs as a short masked quadratic form, each chunk's end
+ * state from its own inputs, a short scan over the chunk states, and a
+ * correction of every chunk's outputs by its true initial state.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, contiguous row-major in the
+ *     layouts stated below, 16-byte aligned.  The caller owns every buffer.
+ *   - The library never allocates or frees memory, never synchronises and never
+ *     reads device memory from the host.  All work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the null stream) and the call returns after enqueue.
+ *   - Validation is host-only and runs before any HIP call: an invalid argument
+ *     returns an error code and enqueues nothing.  A failed launch returns
+ *     SSD_ERR_HIP; asynchronous faults surface at the caller's next sync.
+ *   - The library is stateless and reentrant.
+ *
+ * Shapes: b = batch, T = seqlen, H = nheads, P = headdim, N = dstate,
+ * G = ngroups, Q = chunk, nc = ceil(T / Q).  Supported: b >= 1, T >= 0,
+ * H % G == 0, P % 16 == 0, N % 16 == 0, Q in {64, 128, 256}.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    SSD_ERR_BAD_SHAPE = 2,           /* a size is out of the supported range */
+    SSD_ERR_BAD_DTYPE = 3,           /* dtype is not an ssd_dtype */
+    SSD_ERR_BAD_CHUNK = 4,           /* chunk not in {64, 128, 256} */
+    SSD_ERR_GROUPS = 5,              /* nheads % ngroups != 0 */
+    SSD_ERR_SEQ_IDX = 6,             /* seq_idx given with batch != 1 or nseq < 1 */
+    SSD_ERR_WORKSPACE_TOO_SMALL = 7, /* workspace_bytes below ssd_fwd_workspace_size */
+    SSD_ERR_MISALIGNED = 8,          /* a tensor pointer is not 16-byte aligned */
+    SSD_ERR_ALIASING = 9,            /* an output overlaps an input or another output */
+    SSD_ERR_HIP = 10                 /* a kernel launch failed */
+} ssd_status;
+
+typedef enum {
+    SSD_DTYPE_F32 = 0,   /* x, dt, B, C, y and the chunk intermediates in fp32 */
+    SSD_DTYPE_BF16 = 1   /* x, dt, B, C, y and the chunk intermediates in bf16;
+                            all accumulation in fp32 */
+} ssd_dtype;
+
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk; /* b, T, H, P, N, G, Q */
+    int32_t dtype;                /* ssd_dtype of x, dt, B, C and y */
+    int32_t dt_softplus;          /* 1: Delta = softplus(dt); 0: Delta = dt */
+    const void *x;                /* [b,T,H,P] dtype */
+    const void *dt;               /* [b,T,H]   dtype */
+    const float *A;               /* [H] fp32 (A <= 0 is the supported domain) */
+    const void *B;                /* [b,T,G,N] dtype */
+    const void *C;                /* [b,T,G,N] dtype */
+    const float *D;               /* [H] fp32, or NULL for no skip term */
+    const float *initial_states;  /* [b,H,P,N] fp32, or NULL for zeros */
+    const int32_t *seq_idx;       /* [T] int32 segment ids, or NULL.  Requires batch == 1;
+                                     precondition (not checked): non-decreasing values in
+                                     [0, nseq).  A position t > 0 whose id differs from
+                                     t-1's starts a new segment: the carried state is
+                                     replaced by zero there. */
+    int64_t nseq;                 /* number of segment ids when seq_idx != NULL */
+    void *y;                      /* [b,T,H,P] dtype, out */
+    float *final_states;          /* out, or NULL: [b,H,P,N] fp32 (the state after token
+                                     T-1), or with seq_idx [nseq,H,P,N] fp32 (the state
+                                     after each segment's last token; zero for an id
+                                     that never occurs) */
+    void *workspace;              /* device scratch for ssd_fwd, >= ssd_fwd_workspace_size */
+    size_t workspace_bytes;
+} ssd_fwd_args;
+
+/* SSD_ABI_VERSION of the loaded library. */
+int ssd_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *ssd_status_string(int32_t status);
+
+/* Workspace bytes ssd_fwd needs for these shapes (only the shape and dtype fields
+ * and seq_idx != NULL are read).  Returns a status; *bytes is set on SSD_OK. */
+ssd_status ssd_fwd_workspace_size(const ssd_fwd_args *args, size_t *bytes);
+
+/* The whole forward pass: y and final_states from the inputs in `args`. */
+ssd_status ssd_fwd(const ssd_fwd_args *args, void *stream);
+
+/*
+ * Per-step entry points.  Each runs one step of the chunked algorithm with
+ * explicit intermediate buffers (device, caller-owned), for per-step checks and
+ * timing.  The shape, dtype and input fields of `args` are read as by ssd_fwd;
+ * its workspace fields are ignored.  Intermediate layouts ("E" = the dtype's
+ * element type, fp32 or bf16):
+ *   delta, cs : [b,H,nc,Q] fp32
+ *   cb        : [b,nc,G,Q,Q] E        (only the lower block triangle is written)
+ *   states    : [b,nc,H,P,N] E
+ */
+
+/* Step 0 ("chunk_cumsum").  delta[t] = softplus(dt[t]) (or dt[t]);
+ * cs[t] = sum of delta*A from the later of the chunk start and t's segment start
+ * through t (inclusive), so exp(cs_t - cs_s) = a_{s+1}...a_t for s <= t in one
+ * segment of one chunk (the decay mask L of section 3.2 of "Mamba 2 --
+ * Transformers are SSMs").  Positions past T get delta = 0 and keep cs. */
+ssd_status ssd_chunk_cumsum(const ssd_fwd_args *args, float *delta, float *cs, void *stream);
+
+/* C B^T of every chunk and group: cb[b,c,g,t,s] = sum_n C[cQ+t,g,n] B[cQ+s,g,n]
+ * (the Q K^T of the dual form, formula 1 of "Mamba 2 -- Transformers are SSMs",
+ * shared by the heads of a group). */
+ssd_status ssd_chunk_cb(const ssd_fwd_args *args, void *cb, void *stream);
+
+/* Step 2 ("chunk_state", step 2 of the four-step algorithm): every chunk's end
+ * state from its own inputs with a zero start,
+ * states[b,c,h,p,n] = sum_{s in chunk c, same segment as the chunk's last token}
+ *                      exp(cs_last - cs_s) * delta_s * x_s[p] * B_s[n]. */
+ssd_status ssd_chunk_state(const ssd_fwd_args *args, const float *delta, const float *cs,
+                           void *states, void *stream);
+
+/* Step 3 ("state_passing", the short scan over chunk states): in place,
+ * states[c] := h_{c-1} (the state entering chunk c; h_{-1} = initial_states) where
+ * h_c = exp(cs_last(c)) * h_{c-1} + S_c, with the carry replaced by zero when chunk
+ * c holds a segment boundary.  Without seq_idx it also writes final_states
+ * (= h_{nc-1}) when args->final_states != NULL. */
+ssd_status ssd_state_passing(const ssd_fwd_args *args, const float *cs, void *states,
+                             void *stream);
+
+/* With seq_idx only: final_states[s] = the state after segment s's last token,
+ * from that token's chunk inputs and the state entering the chunk (`states` as
+ * left by ssd_state_passing).  `seg_end` is caller scratch of nseq int32. */
+ssd_status ssd_seq_final_states(const ssd_fwd_args *args, const float *delta, const float *cs,
+                                const void *states, int32_t *seg_end, void *stream);
+
+/* Steps 1 and 4 ("chunk_scan"): y = intra-chunk masked quadratic form plus the
+ * decayed contribution of the state entering each chunk plus D*x.  `states` holds
+ * the entering states as left by ssd_state_passing. */
+ssd_status ssd_chunk_scan(const ssd_fwd_args *args, const float *delta, const float *cs,
+                          const void *cb, const void *states, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

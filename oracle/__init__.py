@@ -54,7 +54,7 @@ def load():
         lib = ctypes.CDLL(LIB)
         lib.ssd_oracle_forward.argtypes = [ctypes.POINTER(_Args)]
         lib.ssd_oracle_forward.restype = ctypes.c_int
-        lib.ssd_oracle_chunk_cumsum.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 4
+        lib.ssd_oracle_chunk_cumsum.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 5
         lib.ssd_oracle_chunk_cumsum.restype = ctypes.c_int
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -129,15 +129,21 @@ def forward(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, nseq=None
     return OracleResult(y, fs, ces)
 
 
-def chunk_cumsum(dt, A, chunk, dt_softplus=True):
-    """Delta and within-chunk inclusive cumsum of Delta*A, both [b,H,nc,Q] fp64."""
+def chunk_cumsum(dt, A, chunk, dt_softplus=True, seq_idx=None):
+    """Delta and the within-chunk (and within-segment) inclusive cumsum of
+    Delta*A, both [b,H,nc,Q] fp64."""
     dt, A = _f64(dt), _f64(A)
+    sidx = None
+    if seq_idx is not None:
+        if hasattr(seq_idx, "detach"):
+            seq_idx = seq_idx.detach().cpu().numpy()
+        sidx = np.ascontiguousarray(np.asarray(seq_idx).reshape(-1), dtype=np.int32)
     b, T, H = dt.shape
     nc = (T + chunk - 1) // chunk
     delta = np.zeros((b, H, nc, chunk), np.float64)
     cs = np.zeros((b, H, nc, chunk), np.float64)
     rc = load().ssd_oracle_chunk_cumsum(b, T, H, chunk, int(bool(dt_softplus)),
-                                        _ptr(dt), _ptr(A), _ptr(delta), _ptr(cs))
+                                        _ptr(dt), _ptr(A), _ptr(sidx), _ptr(delta), _ptr(cs))
     if rc != 0:
         raise ValueError(f"ssd_oracle_chunk_cumsum failed with status {rc}")
     return delta, cs

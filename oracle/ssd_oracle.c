@@ -176,14 +176,19 @@ int ssd_oracle_forward(const ssd_oracle_args *a)
  *
  * so exp(cs_t - cs_s) = a_{s+1} ... a_t is the decay mask entry between two
  * tokens of one chunk ("Mamba 2 -- Transformers are SSMs" paper story,
- * section 3.2, the mask L as a product of a's).  Positions past the end of the
- * sequence (t >= T in the last chunk) get Delta = 0 and l = 0, so cs keeps its
- * last value there.  Outputs are laid out [b][H][nc][Q].
+ * section 3.2, the mask L as a product of a's).  With packed sequences the sum
+ * also restarts at every segment boundary inside a chunk, so cs_t is the log of
+ * the decay from the later of the chunk start and t's segment start through t;
+ * the decay across a boundary is zero and is never formed from cs.  Positions
+ * past the end of the sequence (t >= T in the last chunk) get Delta = 0 and
+ * l = 0, so cs keeps its last value there.  Outputs are laid out [b][H][nc][Q].
  */
 int ssd_oracle_chunk_cumsum(int64_t batch, int64_t T, int64_t H, int64_t Q, int32_t dt_softplus,
-                            const double *dt, const double *A, double *delta_out, double *cs_out)
+                            const double *dt, const double *A, const int32_t *seq_idx,
+                            double *delta_out, double *cs_out)
 {
     if (batch < 1 || T < 1 || H < 1 || Q < 1 || !dt || !A || !delta_out || !cs_out) return ORACLE_BAD_ARGS;
+    if (seq_idx && batch != 1) return ORACLE_BAD_ARGS;
     const int64_t nc = (T + Q - 1) / Q;
     for (int64_t b = 0; b < batch; ++b)
         for (int64_t h = 0; h < H; ++h)
@@ -195,6 +200,7 @@ int ssd_oracle_chunk_cumsum(int64_t batch, int64_t T, int64_t H, int64_t Q, int3
                     if (t < T) {
                         const double z = dt[(b * T + t) * H + h];
                         delta = dt_softplus ? softplus(z) : z;
+                        if (seq_idx && t > 0 && seq_idx[t] != seq_idx[t - 1]) run = 0.0;
                     }
                     run += delta * A[h];
                     const int64_t o = ((b * H + h) * nc + c) * Q + i;

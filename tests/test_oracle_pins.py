@@ -367,6 +367,25 @@ def test_chunk_cumsum(T, Q):
                         np.prod(a[s + 1: t + 1]), rel=1e-12)
 
 
+def test_chunk_cumsum_restarts_at_segments():
+    """Packed: exp(cs_t) is the decay product from the later of the chunk start and
+    t's segment start, so exp(cs_t - cs_s) = a_{s+1}...a_t for s, t in one segment."""
+    inp = _packed(seed=57, chunk=8)
+    dt, A = _np(inp.dt), _np(inp.A)
+    sid = inp.seq_idx.numpy()
+    T, Q = dt.shape[1], 8
+    delta, cs = oracle.chunk_cumsum(dt, A, Q, seq_idx=sid)
+    sp = _softplus_ref(dt)
+    for h in range(dt.shape[2]):
+        a = np.exp(sp[0, :, h] * A[h])
+        for t in range(T):
+            c, i = divmod(t, Q)
+            start = t
+            while start > c * Q and sid[start - 1] == sid[t]:
+                start -= 1
+            assert math.exp(cs[0, h, c, i]) == pytest.approx(np.prod(a[start: t + 1]), rel=1e-12)
+
+
 @pytest.mark.parametrize("packed", [False, True])
 def test_chunk_end_states(packed):
     """Normal mode: the state after chunk c equals the final state of a run over the
