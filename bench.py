@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked SSD forward pass on one MI355X.
+
+One step = one full forward pass (chunk_cumsum, chunk_cb, chunk_state,
+state_passing, [seq_final], chunk_scan) over one batch of seeded synthetic
+input already resident in HBM.  Prints ONE JSON line:
+
+  value        whole-job tokens/s over the K timed steps (wall clock, synchronised)
+  roofline     the dominant kernel's achieved algorithmic FLOP/s (or bytes/s) per
+               launch, from HIP events recorded on the launch stream, against
+               MI355X's published peak
+  cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same workload
+  kernels      per-kernel breakdown (average ms per launch, achieved rate, fraction)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/sec on 1 MI355X + % of bf16 MFMA / HBM roofline per kernel"
+PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
+DEFAULT_WORKLOAD = 3   # 16K tokens, N = 256: the configuration the roofline targets are quoted on
+
+
+def algorithmic_work(shape, esz, packed):
+    """Per-launch algorithmic FLOPs (multiply-add = 2) and HBM bytes of each kernel.
+
+    FLOPs count only what the method needs (the causal half of each Q x Q
+    block); bytes count each tensor a kernel must read or write once."""
+    b, T, H, P, N, G, Q = (shape[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
+                                             "ngroups", "chunk"))
+    nc = (T + Q - 1) // Q
+    causal = (Q + 1) / (2.0 * Q)
+    st = b * nc * H * P * N * esz            # chunk states (stored in the compute dtype)
+    dcs = 2 * b * H * nc * Q * 4             # delta + cs
+    cbb = b * nc * G * Q * Q * esz * (Q // 64 + 1) / (2 * (Q // 64))  # lower block triangle
+    w = {
+        "chunk_cumsum": dict(bound="hbm", bytes=b * T * H * esz + H * 4 + dcs),
+        "chunk_cb": dict(bound="mfma", flops=2.0 * b * nc * Q * G * Q * N * causal,
+                         bytes=2 * b * T * G * N * esz + cbb),
+        "chunk_state": dict(bound="mfma", flops=2.0 * b * T * H * P * N,
+                            bytes=b * T * H * P * esz + b * T * G * N * esz + dcs + st),
+        "state_passing": dict(bound="hbm", bytes=2 * st + b * H * nc * 4 + 2 * b * H * P * N * 4),
+        "chunk_scan": dict(bound="mfma",
+                           flops=2.0 * b * T * H * P * Q * causal + 2.0 * b * T * H * N * P,
+                           bytes=2 * b * T * H * P * esz + b * T * G * N * esz + dcs + st + cbb),
+    }
+    if packed:
+        w["seq_final"] = dict(bound="mfma", flops=0.0, bytes=0)
+    return w
+
+
+def run_cpu_baseline(inp, budget_s=20.0):
+    """Time the fp64 oracle on sampled (batch, head) units of the same workload and
+    extrapolate to the whole workload's tokens/s."""
+    import numpy as np
+    import oracle
+
+    b, T, H, P = inp.x.shape
+    units = b * H
+    # one unit first, to size the sample to the time budget
+    order = np.random.default_rng(0).permutation(units)
+    mask = np.zeros(units, bool)
+    mask[order[0]] = True
+    t0 = time.perf_counter()
+    oracle.forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.initial_states, inp.seq_idx,
+                   inp.nseq or None, inp.dt_softplus, unit_mask=mask.reshape(b, H))
+    one = time.perf_counter() - t0
+    k = int(max(1, min(units, budget_s / max(one, 1e-3))))
+    mask[:] = False
+    mask[order[:k]] = True
+    t0 = time.perf_counter()
+    oracle.forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.initial_states, inp.seq_idx,
+                   inp.nseq or None, inp.dt_softplus, unit_mask=mask.reshape(b, H))
+    dt = time.perf_counter() - t0
+    full_time = dt * units / k
+    return {"value": inp.real_tokens / full_time, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{k} of {units} (batch, head) units, all {T} tokens each; "
+                      f"{dt:.1f} s measured, extrapolated x{units / k:.1f}",
+            "seconds_measured": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU path is a design, not code", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ssd_chunked_scan_amd import ssd
+    from ssd_chunked_scan_amd import workloads as wl
+
+    ssd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = wl.WORKLOADS[args.workload]
+    inp = wl.workload(args.workload)
+    g = inp.to(dev)
+    nseq = inp.nseq if inp.seq_idx is not None else None
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states, g.seq_idx, nseq)
+    ws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(g.x)
+    fin = torch.empty(p.final_shape(), dtype=torch.float32, device=dev)
+
+    def step():
+        ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states,
+                seq_idx=g.seq_idx, nseq=nseq, y=y, final_states=fin, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = inp.real_tokens * args.steps / elapsed
+
+    # per-kernel breakdown: the same kernels through the per-step entry points,
+    # bracketed by HIP events on the stream they are launched on
+    stream = torch.cuda.current_stream(dev)
+    names = ["chunk_cumsum", "chunk_cb", "chunk_state", "state_passing"]
+    if inp.seq_idx is not None:
+        names.append("seq_final")
+    names.append("chunk_scan")
+    delta = torch.empty((p.b, p.H, p.nc, p.Q), dtype=torch.float32, device=dev)
+    cs = torch.empty_like(delta)
+    cb = torch.empty((p.b, p.nc, p.G, p.Q, p.Q), dtype=g.x.dtype, device=dev)
+    states = torch.empty((p.b, p.nc, p.H, p.P, p.N), dtype=g.x.dtype, device=dev)
+    seg_end = torch.empty((max(p.nseq, 1),), dtype=torch.int32, device=dev)
+    ybuf = torch.empty_like(g.x)
+    calls = {
+        "chunk_cumsum": lambda: ssd.chunk_cumsum(p, delta, cs),
+        "chunk_cb": lambda: ssd.chunk_cb(p, cb),
+        "chunk_state": lambda: ssd.chunk_state(p, delta, cs, states),
+        "state_passing": lambda: ssd.state_passing(p, cs, states, None if inp.seq_idx is not None else fin),
+        "seq_final": lambda: ssd.seq_final_states(p, delta, cs, states, fin, seg_end),
+        "chunk_scan": lambda: ssd.chunk_scan(p, delta, cs, cb, states, ybuf),
+    }
+    reps = max(5, min(args.steps, 50))
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)] for n in names}
+    for _ in range(2):
+        for n in names:
+            calls[n]()
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for n in names:
+            ev[n][r][0].record(stream)
+            calls[n]()
+            ev[n][r][1].record(stream)
+    torch.cuda.synchronize()
+    kms = {n: sum(a.elapsed_time(b_) for a, b_ in ev[n]) / reps for n in names}
+
+    esz = 2 if g.x.dtype == torch.bfloat16 else 4
+    work = algorithmic_work(inp.shape, esz, inp.seq_idx is not None)
+    mfma_peak = PEAK["bf16_mfma_tflops"] if esz == 2 else PEAK["fp32_mfma_tflops"]
+    kernels = {}
+    for n in names:
+        wk = work[n]
+        sec = kms[n] / 1e3
+        if wk["bound"] == "mfma" and wk.get("flops"):
+            ach = wk["flops"] / sec / 1e12
+            kernels[n] = dict(ms=round(kms[n], 5), bound="mfma", achieved=round(ach, 2),
+                              peak=mfma_peak, unit="TFLOP/s", frac=round(ach / mfma_peak, 4),
+                              hbm_gbs=round(wk["bytes"] / sec / 1e9, 1))
+        else:
+            ach = wk["bytes"] / sec / 1e9
+            kernels[n] = dict(ms=round(kms[n], 5), bound="hbm", achieved=round(ach, 1),
+                              peak=PEAK["hbm_gbs"], unit="GB/s", frac=round(ach / PEAK["hbm_gbs"], 4))
+    dom = max(names, key=lambda n: kms[n])
+    kd = kernels[dom]
+    roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
+                "unit": kd["unit"], "frac": kd["frac"], "traffic": None}
+    total_flops = sum(w.get("flops", 0.0) for w in work.values())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(inp, args.cpu_budget)
+
+    b, T, H, P = inp.x.shape
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if esz == 2 else "f32", "data": "synthetic (seeded, see workloads.py)",
+        "config": {"workload": cfg["name"], "batch": b, "seqlen": T, "nheads": H, "headdim": P,
+                   "dstate": inp.B.shape[3], "ngroups": inp.B.shape[2], "chunk": inp.chunk,
+                   "real_tokens": inp.real_tokens},
+        "tflops": round(total_flops / (ms_per_step / 1e3) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

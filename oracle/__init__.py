@@ -147,3 +147,16 @@ def chunk_cumsum(dt, A, chunk, dt_softplus=True, seq_idx=None):
     if rc != 0:
         raise ValueError(f"ssd_oracle_chunk_cumsum failed with status {rc}")
     return delta, cs
+
+
+def chunk_cb(B, C, chunk):
+    """cb[b,c,g,t,s] = sum_n C[cQ+t,g,n] B[cQ+s,g,n] in fp64 (rows past T are zero):
+    the Q K^T of the dual form ("Mamba 2 -- Transformers are SSMs" paper story,
+    section 3.2, formula 1) restricted to one chunk, written as a plain matmul."""
+    B, C = _f64(B), _f64(C)
+    b, T, G, N = B.shape
+    nc = (T + chunk - 1) // chunk
+    pad = nc * chunk - T
+    Bp = np.pad(B, ((0, 0), (0, pad), (0, 0), (0, 0))).reshape(b, nc, chunk, G, N)
+    Cp = np.pad(C, ((0, 0), (0, pad), (0, 0), (0, 0))).reshape(b, nc, chunk, G, N)
+    return np.einsum("bctgn,bcsgn->bcgts", Cp, Bp)

@@ -1,0 +1,453 @@
+// ssd_api.hip -- host side of libssd.so: argument validation, workspace layout
+// and kernel launches behind the C ABI declared in include/ssd.h.
+//
+// Validation is pure host code and runs before any HIP call.  Nothing here
+// allocates, frees or synchronises; every launch goes to the caller's stream.
+#include "ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "ssd_kernels.hpp"
+
+using namespace ssd;
+
+namespace {
+
+struct Shape {
+    int64_t b, T, H, P, N, G, Q, nc;
+    int dtype;
+    size_t esz;   // bytes per element of x, dt, B, C, y and the chunk intermediates
+    bool packed;
+    int64_t nseq;
+};
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxState = 256;
+
+ssd_status parse_shape(const ssd_fwd_args *a, Shape *s)
+{
+    if (!a) return SSD_ERR_NULL_POINTER;
+    if (a->dtype != SSD_DTYPE_F32 && a->dtype != SSD_DTYPE_BF16) return SSD_ERR_BAD_DTYPE;
+    if (a->batch < 1 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 16 || a->dstate < 16 ||
+        a->ngroups < 1)
+        return SSD_ERR_BAD_SHAPE;
+    if (a->headdim % 16 != 0 || a->dstate % 16 != 0 || a->dstate > kMaxState) return SSD_ERR_BAD_SHAPE;
+    if (a->batch > kMaxDim || a->seqlen > kMaxDim || a->nheads > kMaxDim || a->headdim > 4096)
+        return SSD_ERR_BAD_SHAPE;
+    if (a->nheads % a->ngroups != 0) return SSD_ERR_GROUPS;
+    if (a->chunk != 64 && a->chunk != 128 && a->chunk != 256) return SSD_ERR_BAD_CHUNK;
+    if (a->seq_idx && (a->batch != 1 || a->nseq < 1 || a->nseq > kMaxDim)) return SSD_ERR_SEQ_IDX;
+    s->b = a->batch;
+    s->T = a->seqlen;
+    s->H = a->nheads;
+    s->P = a->headdim;
+    s->N = a->dstate;
+    s->G = a->ngroups;
+    s->Q = a->chunk;
+    s->nc = (a->seqlen + a->chunk - 1) / a->chunk;
+    s->dtype = a->dtype;
+    s->esz = a->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    s->packed = a->seq_idx != nullptr;
+    s->nseq = a->seq_idx ? a->nseq : 0;
+    // every grid dimension and every int32 index used inside the kernels must fit
+    const int64_t units = s->nc * s->H * ((s->P + 63) / 64) * ((s->N + 63) / 64);
+    if (units > INT32_MAX || s->nc * s->Q > INT32_MAX) return SSD_ERR_BAD_SHAPE;
+    return SSD_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const void *p;
+    size_t n;
+};
+
+bool overlaps(Range a, Range b)
+{
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Sizes in bytes of the tensors in the args struct.
+struct Sizes {
+    size_t x, dt, A, bc, D, init, seq, y, fin;
+};
+
+Sizes tensor_sizes(const Shape &s)
+{
+    Sizes z;
+    z.x = (size_t)(s.b * s.T * s.H * s.P) * s.esz;
+    z.dt = (size_t)(s.b * s.T * s.H) * s.esz;
+    z.A = (size_t)s.H * 4;
+    z.bc = (size_t)(s.b * s.T * s.G * s.N) * s.esz;
+    z.D = (size_t)s.H * 4;
+    z.init = (size_t)(s.b * s.H * s.P * s.N) * 4;
+    z.seq = (size_t)s.T * 4;
+    z.y = z.x;
+    z.fin = (size_t)((s.packed ? s.nseq : s.b) * s.H * s.P * s.N) * 4;
+    return z;
+}
+
+// Which pointers an entry point reads or writes.
+enum : unsigned {
+    kNeedX = 1u << 0,
+    kNeedDt = 1u << 1,
+    kNeedB = 1u << 2,
+    kNeedC = 1u << 3,
+    kNeedY = 1u << 4,
+    kCheckFinal = 1u << 5,   // final_states written if non-NULL
+};
+
+ssd_status check_pointers(const ssd_fwd_args *a, const Shape &s, unsigned need)
+{
+    const bool empty = s.T == 0;
+    if (!a->A) return SSD_ERR_NULL_POINTER;
+    if (!empty) {
+        if ((need & kNeedX) && !a->x) return SSD_ERR_NULL_POINTER;
+        if ((need & kNeedDt) && !a->dt) return SSD_ERR_NULL_POINTER;
+        if ((need & kNeedB) && !a->B) return SSD_ERR_NULL_POINTER;
+        if ((need & kNeedC) && !a->C) return SSD_ERR_NULL_POINTER;
+        if ((need & kNeedY) && !a->y) return SSD_ERR_NULL_POINTER;
+    }
+    const void *ptrs[] = {a->x, a->dt, a->A, a->B, a->C, a->D, a->initial_states, a->seq_idx, a->y,
+                          a->final_states, a->workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+    const Sizes z = tensor_sizes(s);
+    const Range ins[] = {{a->x, z.x}, {a->dt, z.dt}, {a->A, z.A}, {a->B, z.bc}, {a->C, z.bc},
+                         {a->D, z.D}, {a->initial_states, z.init}, {a->seq_idx, z.seq}};
+    const Range outs[] = {{(need & kNeedY) ? a->y : nullptr, z.y},
+                          {(need & kCheckFinal) ? a->final_states : nullptr, z.fin}};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i)) return SSD_ERR_ALIASING;
+    if (overlaps(outs[0], outs[1])) return SSD_ERR_ALIASING;
+    return SSD_OK;
+}
+
+// Workspace carve-up for ssd_fwd (256-byte aligned pieces).
+struct Workspace {
+    size_t delta, cs, cb, states, seg_end, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace workspace_layout(const Shape &s)
+{
+    Workspace w;
+    const size_t dcs = (size_t)(s.b * s.H * s.nc * s.Q) * 4;
+    const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * s.Q) * s.esz;
+    const size_t sts = (size_t)(s.b * s.nc * s.H * s.P * s.N) * s.esz;
+    w.delta = 0;
+    w.cs = align256(w.delta + dcs);
+    w.cb = align256(w.cs + dcs);
+    w.states = align256(w.cb + cbs);
+    w.seg_end = align256(w.states + sts);
+    w.total = align256(w.seg_end + (s.packed ? (size_t)s.nseq * 4 : 0));
+    return w;
+}
+
+ssd_status launched() { return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+unsigned grid1(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+// ---- per-step launches (typed) ----
+
+template <typename E>
+ssd_status run_cumsum(const Shape &s, const ssd_fwd_args *a, float *delta, float *cs, hipStream_t st)
+{
+    dim3 grid((unsigned)s.nc, (unsigned)((s.H + kCumsumHeads - 1) / kCumsumHeads), (unsigned)s.b);
+    hipLaunchKernelGGL(k_chunk_cumsum<E>, grid, dim3(kThreads), 0, st, (const E *)a->dt, a->A, a->seq_idx,
+                       delta, cs, (int)s.T, (int)s.H, (int)s.Q, (int)s.nc, (int)a->dt_softplus);
+    return launched();
+}
+
+template <typename E>
+ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
+{
+    const int nt = (int)(s.Q / 64), ntri = nt * (nt + 1) / 2;
+    dim3 grid((unsigned)(ntri * s.nc * s.G), (unsigned)s.b);
+    hipLaunchKernelGGL(k_chunk_cb<E>, grid, dim3(kThreads), 0, st, (const E *)a->B, (const E *)a->C, cb,
+                       (int)s.T, (int)s.G, (int)s.N, (int)s.Q, (int)s.nc, ntri);
+    return launched();
+}
+
+template <typename E, int Q>
+ssd_status run_state_q(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, E *states,
+                       hipStream_t st)
+{
+    const int ntp = (int)((s.P + 63) / 64), ntn = (int)((s.N + 63) / 64);
+    dim3 grid((unsigned)(s.nc * s.H * ntp * ntn), (unsigned)s.b);
+    hipLaunchKernelGGL((k_chunk_state<E, Q>), grid, dim3(kThreads), 0, st, (const E *)a->x, (const E *)a->B,
+                       delta, cs, a->seq_idx, states, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
+                       (int)s.nc, ntp, ntn);
+    return launched();
+}
+
+template <typename E>
+ssd_status run_state(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, E *states,
+                     hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return run_state_q<E, 64>(s, a, delta, cs, states, st);
+    case 128: return run_state_q<E, 128>(s, a, delta, cs, states, st);
+    default: return run_state_q<E, 256>(s, a, delta, cs, states, st);
+    }
+}
+
+template <typename E>
+ssd_status run_passing(const Shape &s, const ssd_fwd_args *a, const float *cs, E *states, float *final_states,
+                       hipStream_t st)
+{
+    const int64_t PN = s.P * s.N;
+    const int64_t vecs = s.b * s.H * PN / kVec16<E>;
+    hipLaunchKernelGGL(k_state_passing<E>, dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, states, cs,
+                       a->initial_states, final_states, a->seq_idx, (int)s.T, (int)s.H, PN, (int)s.nc,
+                       (int)s.Q, vecs);
+    return launched();
+}
+
+template <typename E, int Q>
+ssd_status run_seq_final_q(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs,
+                           const E *hin, int32_t *seg_end, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_seg_end_init, dim3(grid1(s.nseq, 256)), dim3(256), 0, st, seg_end, (int)s.nseq);
+    if (launched() != SSD_OK) return SSD_ERR_HIP;
+    hipLaunchKernelGGL(k_seg_end, dim3(grid1(s.T, 256)), dim3(256), 0, st, a->seq_idx, seg_end, (int)s.T,
+                       (int)s.nseq);
+    if (launched() != SSD_OK) return SSD_ERR_HIP;
+    const int ntp = (int)((s.P + 63) / 64), ntn = (int)((s.N + 63) / 64);
+    dim3 grid((unsigned)(s.nseq * s.H * ntp * ntn));
+    hipLaunchKernelGGL((k_seq_final<E, Q>), grid, dim3(kThreads), 0, st, (const E *)a->x, (const E *)a->B,
+                       delta, cs, a->seq_idx, hin, seg_end, a->final_states, (int)s.T, (int)s.H, (int)s.G,
+                       (int)s.P, (int)s.N, (int)s.nc, (int)s.nseq, ntp, ntn);
+    return launched();
+}
+
+template <typename E>
+ssd_status run_seq_final(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs,
+                         const E *hin, int32_t *seg_end, hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return run_seq_final_q<E, 64>(s, a, delta, cs, hin, seg_end, st);
+    case 128: return run_seq_final_q<E, 128>(s, a, delta, cs, hin, seg_end, st);
+    default: return run_seq_final_q<E, 256>(s, a, delta, cs, hin, seg_end, st);
+    }
+}
+
+template <typename E, int Q>
+ssd_status run_scan_q(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
+                      const E *hin, hipStream_t st)
+{
+    const int ntp = (int)((s.P + 63) / 64);
+    const size_t dyn = (size_t)64 * (size_t)(s.N + kVec16<E>) * sizeof(E);
+    static bool attr_set = false;   // raising the dynamic-LDS cap is idempotent
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)k_chunk_scan<E, Q>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(64 * (kMaxState + kVec16<E>) * sizeof(E))) != hipSuccess)
+            return SSD_ERR_HIP;
+        attr_set = true;
+    }
+    dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
+    hipLaunchKernelGGL((k_chunk_scan<E, Q>), grid, dim3(kThreads), dyn, st, (const E *)a->x, (const E *)a->C,
+                       delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T, (int)s.H, (int)s.G,
+                       (int)s.P, (int)s.N, (int)s.nc, ntp);
+    return launched();
+}
+
+template <typename E>
+ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
+                    const E *hin, hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return run_scan_q<E, 64>(s, a, delta, cs, cb, hin, st);
+    case 128: return run_scan_q<E, 128>(s, a, delta, cs, cb, hin, st);
+    default: return run_scan_q<E, 256>(s, a, delta, cs, cb, hin, st);
+    }
+}
+
+ssd_status fill_final(const Shape &s, const ssd_fwd_args *a, hipStream_t st)
+{
+    if (!a->final_states) return SSD_OK;
+    const int64_t n = (s.packed ? s.nseq : s.b) * s.H * s.P * s.N;
+    // an empty packed stream has no segment that could receive the initial state
+    const float *init = s.packed ? nullptr : a->initial_states;
+    hipLaunchKernelGGL(k_fill_final, dim3(grid1(n, 256)), dim3(256), 0, st, a->final_states, init, n);
+    return launched();
+}
+
+template <typename E>
+ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, hipStream_t st)
+{
+    char *ws = static_cast<char *>(a->workspace);
+    float *delta = reinterpret_cast<float *>(ws + w.delta);
+    float *cs = reinterpret_cast<float *>(ws + w.cs);
+    E *cb = reinterpret_cast<E *>(ws + w.cb);
+    E *states = reinterpret_cast<E *>(ws + w.states);
+    int32_t *seg_end = reinterpret_cast<int32_t *>(ws + w.seg_end);
+    ssd_status r;
+    if ((r = run_cumsum<E>(s, a, delta, cs, st)) != SSD_OK) return r;
+    if ((r = run_cb<E>(s, a, cb, st)) != SSD_OK) return r;
+    if ((r = run_state<E>(s, a, delta, cs, states, st)) != SSD_OK) return r;
+    if ((r = run_passing<E>(s, a, cs, states, s.packed ? nullptr : a->final_states, st)) != SSD_OK) return r;
+    if (s.packed && a->final_states)
+        if ((r = run_seq_final<E>(s, a, delta, cs, states, seg_end, st)) != SSD_OK) return r;
+    return run_scan<E>(s, a, delta, cs, cb, states, st);
+}
+
+const char *const kStatusText[] = {
+    "ok",
+    "a required pointer is NULL",
+    "a size is outside the supported range (P and N multiples of 16, N <= 256)",
+    "dtype must be SSD_DTYPE_F32 or SSD_DTYPE_BF16",
+    "chunk must be 64, 128 or 256",
+    "nheads must be a multiple of ngroups",
+    "seq_idx requires batch == 1 and nseq >= 1",
+    "workspace is smaller than ssd_fwd_workspace_size",
+    "a tensor pointer is not 16-byte aligned",
+    "an output overlaps an input or another output",
+    "a HIP kernel launch failed",
+};
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char *ssd_status_string(int32_t status)
+{
+    if (status < 0 || status >= (int32_t)(sizeof(kStatusText) / sizeof(kStatusText[0]))) return "unknown status";
+    return kStatusText[status];
+}
+
+ssd_status ssd_fwd_workspace_size(const ssd_fwd_args *args, size_t *bytes)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if (!bytes) return SSD_ERR_NULL_POINTER;
+    *bytes = workspace_layout(s).total;
+    return SSD_OK;
+}
+
+ssd_status ssd_fwd(const ssd_fwd_args *args, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB | kNeedC | kNeedY | kCheckFinal)) != SSD_OK)
+        return r;
+    const Workspace w = workspace_layout(s);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.T == 0) return fill_final(s, args, st);
+    if (!args->workspace) return SSD_ERR_NULL_POINTER;
+    if (args->workspace_bytes < w.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    const Sizes z = tensor_sizes(s);
+    const Range ws{args->workspace, w.total};
+    const Range others[] = {{args->x, z.x}, {args->dt, z.dt}, {args->A, z.A}, {args->B, z.bc}, {args->C, z.bc},
+                            {args->D, z.D}, {args->initial_states, z.init}, {args->seq_idx, z.seq},
+                            {args->y, z.y}, {args->final_states, z.fin}};
+    for (const Range &o : others)
+        if (overlaps(ws, o)) return SSD_ERR_ALIASING;
+    return s.dtype == SSD_DTYPE_BF16 ? fwd_typed<bf16>(s, args, w, st) : fwd_typed<float>(s, args, w, st);
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_fwd_args *args, float *delta, float *cs, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedDt)) != SSD_OK) return r;
+    if (s.T == 0) return SSD_OK;
+    if (!delta || !cs) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(delta) || !aligned16(cs)) return SSD_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return s.dtype == SSD_DTYPE_BF16 ? run_cumsum<bf16>(s, args, delta, cs, st)
+                                     : run_cumsum<float>(s, args, delta, cs, st);
+}
+
+ssd_status ssd_chunk_cb(const ssd_fwd_args *args, void *cb, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedB | kNeedC)) != SSD_OK) return r;
+    if (s.T == 0) return SSD_OK;
+    if (!cb) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(cb)) return SSD_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return s.dtype == SSD_DTYPE_BF16 ? run_cb<bf16>(s, args, (bf16 *)cb, st)
+                                     : run_cb<float>(s, args, (float *)cb, st);
+}
+
+ssd_status ssd_chunk_state(const ssd_fwd_args *args, const float *delta, const float *cs, void *states,
+                           void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedX | kNeedB)) != SSD_OK) return r;
+    if (s.T == 0) return SSD_OK;
+    if (!delta || !cs || !states) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(delta) || !aligned16(cs) || !aligned16(states)) return SSD_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return s.dtype == SSD_DTYPE_BF16 ? run_state<bf16>(s, args, delta, cs, (bf16 *)states, st)
+                                     : run_state<float>(s, args, delta, cs, (float *)states, st);
+}
+
+ssd_status ssd_state_passing(const ssd_fwd_args *args, const float *cs, void *states, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kCheckFinal)) != SSD_OK) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.T == 0) return s.packed ? SSD_OK : fill_final(s, args, st);
+    if (!cs || !states) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(cs) || !aligned16(states)) return SSD_ERR_MISALIGNED;
+    float *fin = s.packed ? nullptr : args->final_states;
+    return s.dtype == SSD_DTYPE_BF16 ? run_passing<bf16>(s, args, cs, (bf16 *)states, fin, st)
+                                     : run_passing<float>(s, args, cs, (float *)states, fin, st);
+}
+
+ssd_status ssd_seq_final_states(const ssd_fwd_args *args, const float *delta, const float *cs,
+                                const void *states, int32_t *seg_end, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if (!s.packed) return SSD_ERR_SEQ_IDX;
+    if ((r = check_pointers(args, s, kNeedX | kNeedB | kCheckFinal)) != SSD_OK) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!args->final_states) return SSD_ERR_NULL_POINTER;
+    if (s.T == 0) return fill_final(s, args, st);
+    if (!delta || !cs || !states || !seg_end) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(delta) || !aligned16(cs) || !aligned16(states) || !aligned16(seg_end))
+        return SSD_ERR_MISALIGNED;
+    return s.dtype == SSD_DTYPE_BF16
+               ? run_seq_final<bf16>(s, args, delta, cs, (const bf16 *)states, seg_end, st)
+               : run_seq_final<float>(s, args, delta, cs, (const float *)states, seg_end, st);
+}
+
+ssd_status ssd_chunk_scan(const ssd_fwd_args *args, const float *delta, const float *cs, const void *cb,
+                          const void *states, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedX | kNeedC | kNeedY)) != SSD_OK) return r;
+    if (s.T == 0) return SSD_OK;
+    if (!delta || !cs || !cb || !states) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(delta) || !aligned16(cs) || !aligned16(cb) || !aligned16(states)) return SSD_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return s.dtype == SSD_DTYPE_BF16
+               ? run_scan<bf16>(s, args, delta, cs, (const bf16 *)cb, (const bf16 *)states, st)
+               : run_scan<float>(s, args, delta, cs, (const float *)cb, (const float *)states, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// ssd_device.hpp -- device-side building blocks shared by the SSD kernels (gfx950).
+//
+// Matrix-core convention used by every kernel.  One "fragment" is what a lane
+// feeds one 16x16 output block per 32-wide K step:
+//   lane l holds row (l % 16) of its operand and the 8 K-slots 8*(l/16) .. 8*(l/16)+7.
+// For bf16 the fragment is 8 bf16 and one v_mfma_f32_16x16x32_bf16 consumes it.
+// For fp32 it is 8 floats consumed by eight v_mfma_f32_16x16x4_f32, the j-th of
+// which takes K-slot (l/16) <-> k = 8*(l/16) + j; A and B use the same map, so
+// the sum over k is unchanged.  The 16x16 fp32 result sits in 4 registers per
+// lane: acc[r] = D[row 4*(l/16) + r][col l % 16].
+// Operands therefore need their K index contiguous per row; tiles whose K index
+// is the slow axis in memory (time, for x and B in the state step) are
+// transposed in registers on their way into LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;   // every kernel runs 4 waves of 64 lanes
+constexpr float kLog2e = 1.4426950408889634f;
+
+// e^x through the hardware base-2 exponential (v_exp_f32).  Used only for
+// arguments <= 0 (decays) where the result is in [0, 1].
+__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+template <typename E> struct Frag;
+template <> struct Frag<bf16> { using type = bf16x8; };
+template <> struct Frag<float> { using type = floatx8; };
+template <typename E> using frag_t = typename Frag<E>::type;
+
+// Elements per 16-byte vector.
+template <typename E> constexpr int kVec16 = 16 / (int)sizeof(E);
+
+__device__ __forceinline__ void mma(floatx4 &acc, const bf16x8 &a, const bf16x8 &b)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(floatx4 &acc, const floatx8 &a, const floatx8 &b)
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+// Fragment loads from a 16-byte aligned address (LDS or global).
+__device__ __forceinline__ bf16x8 load_frag(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ floatx8 load_frag(const float *p)
+{
+    const floatx4 lo = *reinterpret_cast<const floatx4 *>(p);
+    const floatx4 hi = *reinterpret_cast<const floatx4 *>(p + 4);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ floatx8 to_f32(const bf16x8 &v) { return __builtin_convertvector(v, floatx8); }
+__device__ __forceinline__ floatx8 to_f32(const floatx8 &v) { return v; }
+
+template <typename F> __device__ __forceinline__ F from_f32(const floatx8 &v);
+template <> __device__ __forceinline__ bf16x8 from_f32<bf16x8>(const floatx8 &v)
+{
+    return __builtin_convertvector(v, bf16x8);   // round to nearest even
+}
+template <> __device__ __forceinline__ floatx8 from_f32<floatx8>(const floatx8 &v) { return v; }
+
+__device__ __forceinline__ float to_float(float v) { return v; }
+__device__ __forceinline__ float to_float(bf16 v) { return (float)v; }
+template <typename E> __device__ __forceinline__ E from_float(float v) { return (E)v; }
+
+// 16-byte vector <-> 4 or 8 floats.
+__device__ __forceinline__ void load16_f32(const float *p, float *out)
+{
+    const floatx4 v = *reinterpret_cast<const floatx4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = v[i];
+}
+__device__ __forceinline__ void load16_f32(const bf16 *p, float *out)
+{
+    const floatx8 v = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p), floatx8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = v[i];
+}
+__device__ __forceinline__ void store16_f32(float *p, const float *in)
+{
+    *reinterpret_cast<floatx4 *>(p) = floatx4{in[0], in[1], in[2], in[3]};
+}
+__device__ __forceinline__ void store16_f32(bf16 *p, const float *in)
+{
+    const floatx8 v{in[0], in[1], in[2], in[3], in[4], in[5], in[6], in[7]};
+    *reinterpret_cast<bf16x8 *>(p) = __builtin_convertvector(v, bf16x8);
+}
+
+// Four consecutive elements <-> floats (8-byte bf16 or 16-byte fp32 access).
+__device__ __forceinline__ void load4_f32(const float *p, float *out)
+{
+    const floatx4 v = *reinterpret_cast<const floatx4 *>(p);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+}
+__device__ __forceinline__ void load4_f32(const bf16 *p, float *out)
+{
+    const floatx4 v = __builtin_convertvector(*reinterpret_cast<const bf16x4 *>(p), floatx4);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+}
+__device__ __forceinline__ void store4_f32(float *p, const float *in)
+{
+    *reinterpret_cast<floatx4 *>(p) = floatx4{in[0], in[1], in[2], in[3]};
+}
+__device__ __forceinline__ void store4_f32(bf16 *p, const float *in)
+{
+    *reinterpret_cast<bf16x4 *>(p) = __builtin_convertvector(floatx4{in[0], in[1], in[2], in[3]}, bf16x4);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (XCD = id % 8), each with
+// its own L2.  Map the hardware id to a logical id so that every XCD works on one
+// contiguous range of logical ids: neighbouring tiles (same chunk, same B/C
+// group) then share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks)
+{
+    const int x = bid & 7, k = bid >> 3;
+    const int q = nblocks >> 3, r = nblocks & 7;
+    return x * q + (x < r ? x : r) + k;
+}
+
+}  // namespace ssd

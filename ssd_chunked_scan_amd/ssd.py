@@ -1,0 +1,262 @@
+"""Python binding of ``libssd.so`` (the C ABI in ``include/ssd.h``).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of ``libssd.so``.  PyTorch provides device memory (``torch.empty``) and
+the current HIP stream.  Tensors must already be contiguous, on the GPU and of
+the documented dtypes; nothing is copied or converted silently.  If the library
+is missing the first call raises, there is no fallback.
+
+Names follow the C ABI: ``fwd`` (= ``ssd_fwd``) and the per-step entry points
+``chunk_cumsum``, ``chunk_cb``, ``chunk_state``, ``state_passing``,
+``seq_final_states``, ``chunk_scan``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+_DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+EXPORTED = ["ssd_abi_version", "ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd",
+            "ssd_chunk_cumsum", "ssd_chunk_cb", "ssd_chunk_state", "ssd_state_passing",
+            "ssd_seq_final_states", "ssd_chunk_scan"]
+
+
+class FwdArgs(ctypes.Structure):
+    """Mirror of ``ssd_fwd_args``."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("dt_softplus", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+        ("initial_states", ctypes.c_void_p), ("seq_idx", ctypes.c_void_p), ("nseq", ctypes.c_int64),
+        ("y", ctypes.c_void_p), ("final_states", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load ``libssd.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(hipcc for gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(FwdArgs)
+    vp = ctypes.c_void_p
+    lib.ssd_abi_version.restype = ctypes.c_int
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_status_string.argtypes = [ctypes.c_int32]
+    lib.ssd_fwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_fwd.argtypes = [P, vp]
+    lib.ssd_chunk_cumsum.argtypes = [P, vp, vp, vp]
+    lib.ssd_chunk_cb.argtypes = [P, vp, vp]
+    lib.ssd_chunk_state.argtypes = [P, vp, vp, vp, vp]
+    lib.ssd_state_passing.argtypes = [P, vp, vp, vp]
+    lib.ssd_seq_final_states.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.ssd_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp]
+    for name in EXPORTED[2:]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssd_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (no silent copies)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class Problem:
+    """Validated tensors and the matching ``FwdArgs`` for one call."""
+
+    def __init__(self, x, dt, A, B, C, chunk, D=None, initial_states=None, seq_idx=None,
+                 nseq=None, dt_softplus=True):
+        if x.dim() != 4:
+            raise ValueError("x must be [batch, seqlen, nheads, headdim]")
+        b, T, H, P = x.shape
+        if B.dim() != 4:
+            raise ValueError("B must be [batch, seqlen, ngroups, dstate]")
+        G, N = B.shape[2], B.shape[3]
+        if x.dtype not in _DTYPES:
+            raise TypeError("x must be float32 or bfloat16")
+        dev = x.device
+        _check(x, "x", device=dev)
+        _check(dt, "dt", x.dtype, (b, T, H), dev)
+        _check(A, "A", torch.float32, (H,), dev)
+        _check(B, "B", x.dtype, (b, T, G, N), dev)
+        _check(C, "C", x.dtype, (b, T, G, N), dev)
+        _check(D, "D", torch.float32, (H,), dev)
+        _check(initial_states, "initial_states", torch.float32, (b, H, P, N), dev)
+        if seq_idx is not None:
+            _check(seq_idx, "seq_idx", torch.int32, None, dev)
+            if seq_idx.numel() != T:
+                raise ValueError("seq_idx must hold seqlen int32 ids")
+            if nseq is None:
+                raise ValueError("nseq is required with seq_idx (no device->host read)")
+        self.x, self.dt, self.A, self.B, self.C = x, dt, A, B, C
+        self.D, self.initial_states, self.seq_idx = D, initial_states, seq_idx
+        self.b, self.T, self.H, self.P, self.N, self.G, self.Q = b, T, H, P, N, G, int(chunk)
+        self.nc = (T + self.Q - 1) // self.Q
+        self.nseq = int(nseq) if seq_idx is not None else 0
+        self.dtype = x.dtype
+        self.device = dev
+        self.args = FwdArgs(b, T, H, P, N, G, self.Q, _DTYPES[x.dtype], int(bool(dt_softplus)),
+                            _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                            _ptr(initial_states), _ptr(seq_idx), self.nseq,
+                            None, None, None, 0)
+
+    # shapes of the outputs and intermediates
+    def final_shape(self):
+        return (self.nseq if self.seq_idx is not None else self.b, self.H, self.P, self.N)
+
+    def empty(self, shape, dtype=None):
+        return torch.empty(shape, dtype=dtype or self.dtype, device=self.device)
+
+    def call(self, name, *ptrs, stream=None):
+        lib = load_library()
+        st = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        rc = getattr(lib, name)(ctypes.byref(self.args), *ptrs, ctypes.c_void_p(st))
+        if rc != 0:
+            raise SSDError(rc, name)
+
+
+def workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().ssd_fwd_workspace_size(ctypes.byref(p.args), ctypes.byref(n))
+    if rc != 0:
+        raise SSDError(rc, "ssd_fwd_workspace_size")
+    return int(n.value)
+
+
+def fwd(x, dt, A, B, C, chunk, D=None, initial_states=None, seq_idx=None, nseq=None,
+        dt_softplus=True, y=None, final_states=None, workspace=None, stream=None,
+        want_final=True):
+    """y, final_states = SSD forward (see ``include/ssd.h``).
+
+    ``y``, ``final_states`` and ``workspace`` may be passed pre-allocated (e.g.
+    for timing loops); otherwise they are allocated with ``torch.empty``.
+    """
+    p = Problem(x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus)
+    if y is None:
+        y = p.empty(x.shape)
+    _check(y, "y", x.dtype, x.shape, p.device)
+    if want_final and final_states is None:
+        final_states = p.empty(p.final_shape(), torch.float32)
+    _check(final_states, "final_states", torch.float32, p.final_shape(), p.device)
+    need = workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=p.device)
+    _check(workspace, "workspace", torch.uint8, None, p.device)
+    p.args.y = _ptr(y)
+    p.args.final_states = _ptr(final_states)
+    p.args.workspace = _ptr(workspace)
+    p.args.workspace_bytes = workspace.numel()
+    p.call("ssd_fwd", stream=stream)
+    return y, final_states
+
+
+# ---------------------------------------------------------------------------
+# per-step entry points (explicit intermediates; used for per-kernel checks and
+# per-kernel timing)
+# ---------------------------------------------------------------------------
+
+def chunk_cumsum(p: Problem, delta=None, cs=None, stream=None):
+    shape = (p.b, p.H, p.nc, p.Q)
+    delta = p.empty(shape, torch.float32) if delta is None else delta
+    cs = p.empty(shape, torch.float32) if cs is None else cs
+    _check(delta, "delta", torch.float32, shape, p.device)
+    _check(cs, "cs", torch.float32, shape, p.device)
+    p.call("ssd_chunk_cumsum", _ptr(delta), _ptr(cs), stream=stream)
+    return delta, cs
+
+
+def chunk_cb(p: Problem, cb=None, stream=None):
+    shape = (p.b, p.nc, p.G, p.Q, p.Q)
+    cb = p.empty(shape) if cb is None else cb
+    _check(cb, "cb", p.dtype, shape, p.device)
+    p.call("ssd_chunk_cb", _ptr(cb), stream=stream)
+    return cb
+
+
+def chunk_state(p: Problem, delta, cs, states=None, stream=None):
+    shape = (p.b, p.nc, p.H, p.P, p.N)
+    states = p.empty(shape) if states is None else states
+    _check(states, "states", p.dtype, shape, p.device)
+    p.call("ssd_chunk_state", _ptr(delta), _ptr(cs), _ptr(states), stream=stream)
+    return states
+
+
+def state_passing(p: Problem, cs, states, final_states=None, stream=None):
+    """In place: ``states`` (chunk-local end states) becomes the entering states."""
+    _check(states, "states", p.dtype, (p.b, p.nc, p.H, p.P, p.N), p.device)
+    if final_states is not None:
+        _check(final_states, "final_states", torch.float32, p.final_shape(), p.device)
+    p.args.final_states = _ptr(final_states)
+    try:
+        p.call("ssd_state_passing", _ptr(cs), _ptr(states), stream=stream)
+    finally:
+        p.args.final_states = None
+    return states, final_states
+
+
+def seq_final_states(p: Problem, delta, cs, states, final_states=None, seg_end=None, stream=None):
+    final_states = p.empty(p.final_shape(), torch.float32) if final_states is None else final_states
+    _check(final_states, "final_states", torch.float32, p.final_shape(), p.device)
+    seg_end = p.empty((max(p.nseq, 1),), torch.int32) if seg_end is None else seg_end
+    p.args.final_states = _ptr(final_states)
+    try:
+        p.call("ssd_seq_final_states", _ptr(delta), _ptr(cs), _ptr(states), _ptr(seg_end),
+               stream=stream)
+    finally:
+        p.args.final_states = None
+    return final_states
+
+
+def chunk_scan(p: Problem, delta, cs, cb, states, y=None, stream=None):
+    y = p.empty(p.x.shape) if y is None else y
+    _check(y, "y", p.dtype, p.x.shape, p.device)
+    p.args.y = _ptr(y)
+    try:
+        p.call("ssd_chunk_scan", _ptr(delta), _ptr(cs), _ptr(cb), _ptr(states), stream=stream)
+    finally:
+        p.args.y = None
+    return y

@@ -1,0 +1,118 @@
+"""Host-only checks of the C ABI (no GPU work): the library loads, exports every
+entry point that include/ssd.h declares, and rejects invalid arguments with the
+documented status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from ssd_chunked_scan_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, NULLP, SHAPE, DTYPE, CHUNK, GROUPS, SEQ, WS, MISAL, ALIAS, HIP = range(11)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssd_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        pytest.skip("libssd.so not built")
+    return ssd.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(ssd.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ssd_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(11):
+        s = ssd.status_string(code)
+        assert s and s != "unknown status"
+    assert ssd.status_string(99) == "unknown status"
+
+
+def _args(**kw):
+    base = dict(batch=1, seqlen=256, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64,
+                dtype=1, dt_softplus=1)
+    base.update({k: v for k, v in kw.items() if k in base})
+    a = ssd.FwdArgs(base["batch"], base["seqlen"], base["nheads"], base["headdim"], base["dstate"],
+                    base["ngroups"], base["chunk"], base["dtype"], base["dt_softplus"])
+    # fake, 16-byte aligned, non-overlapping host addresses: validation never dereferences them
+    addr = 0x10000000
+    for name in ("x", "dt", "A", "B", "C", "D", "y", "final_states", "workspace"):
+        setattr(a, name, kw.get(name, addr))
+        addr += 0x10000000
+    a.workspace_bytes = kw.get("workspace_bytes", 1 << 40)
+    if "seq_idx" in kw:
+        a.seq_idx = kw["seq_idx"]
+        a.nseq = kw.get("nseq", 1)
+    return a
+
+
+def _fwd(lib, a):
+    return lib.ssd_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), DTYPE),
+    (dict(chunk=32), CHUNK), (dict(chunk=100), CHUNK), (dict(chunk=512), CHUNK),
+    (dict(nheads=6, ngroups=4), GROUPS),
+    (dict(headdim=24), SHAPE), (dict(dstate=40), SHAPE), (dict(dstate=512), SHAPE),
+    (dict(batch=0), SHAPE), (dict(seqlen=-1), SHAPE), (dict(headdim=8), SHAPE),
+    (dict(batch=2, seq_idx=0x90000000, nseq=3), SEQ),
+    (dict(seq_idx=0x90000000, nseq=0), SEQ),
+    (dict(x=0), NULLP), (dict(A=0), NULLP), (dict(y=0), NULLP), (dict(workspace=0), NULLP),
+    (dict(x=0x10000008), MISAL), (dict(D=0x60000004), MISAL),
+    (dict(workspace_bytes=16), WS),
+    (dict(y=0x10000000), ALIAS),                 # y == x
+    (dict(final_states=0x70000000 + 64), ALIAS),  # overlaps y
+    (dict(workspace=0x10000000), ALIAS),
+])
+def test_fwd_rejects_invalid_arguments(lib, kw, code):
+    assert _fwd(lib, _args(**kw)) == code
+
+
+def test_workspace_size(lib):
+    a = _args(batch=2, seqlen=2048, nheads=24, headdim=64, dstate=64, chunk=64)
+    n = ctypes.c_size_t()
+    assert lib.ssd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == OK
+    nc = 32
+    al = lambda v: (v + 255) // 256 * 256
+    want = al(2 * 24 * nc * 64 * 4) * 2 + al(2 * nc * 1 * 64 * 64 * 2) + al(2 * nc * 24 * 64 * 64 * 2)
+    assert n.value == want
+    bad = _args(chunk=48)
+    assert lib.ssd_fwd_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == CHUNK
+
+
+def test_step_entry_points_validate(lib):
+    a = _args()
+    p = ctypes.c_void_p
+    assert lib.ssd_chunk_cumsum(ctypes.byref(a), None, p(0x90000000), None) == NULLP
+    assert lib.ssd_chunk_cumsum(ctypes.byref(a), p(0x90000004), p(0x90000000), None) == MISAL
+    assert lib.ssd_chunk_cb(ctypes.byref(a), None, None) == NULLP
+    assert lib.ssd_chunk_state(ctypes.byref(a), p(0x90000000), None, p(0xa0000000), None) == NULLP
+    assert lib.ssd_state_passing(ctypes.byref(a), None, p(0xa0000000), None) == NULLP
+    assert lib.ssd_chunk_scan(ctypes.byref(a), p(1 << 33), p(2 << 33), None, p(3 << 33), None) == NULLP
+    # seq_final_states only makes sense for a packed stream
+    assert lib.ssd_seq_final_states(ctypes.byref(a), p(1 << 33), p(2 << 33), p(3 << 33), p(4 << 33),
+                                    None) == SEQ
+    bad = _args(chunk=96)
+    assert lib.ssd_chunk_cb(ctypes.byref(bad), p(1 << 33), None) == CHUNK
+
+
+def test_binding_rejects_host_tensors_and_copies():
+    x = torch.zeros(1, 64, 2, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        ssd.Problem(x, x[..., 0], torch.zeros(2), x[:, :, :1], x[:, :, :1], 64)
