@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of this many MiB (3 times), as the "
+                         "reference kernel for scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -110,6 +113,14 @@ def main():
     ssd.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = wl.WORKLOADS[args.workload]
     inp = wl.workload(args.workload)
     g = inp.to(dev)

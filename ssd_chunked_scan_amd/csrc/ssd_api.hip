@@ -9,6 +9,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "ssd_kernels.hpp"
 
@@ -25,7 +26,6 @@ struct Shape {
 };
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
-constexpr int64_t kMaxState = 256;
 
 ssd_status parse_shape(const ssd_fwd_args *a, Shape *s)
 {
@@ -34,7 +34,7 @@ ssd_status parse_shape(const ssd_fwd_args *a, Shape *s)
     if (a->batch < 1 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 16 || a->dstate < 16 ||
         a->ngroups < 1)
         return SSD_ERR_BAD_SHAPE;
-    if (a->headdim % 16 != 0 || a->dstate % 16 != 0 || a->dstate > kMaxState) return SSD_ERR_BAD_SHAPE;
+    if (a->headdim % 16 != 0 || a->dstate % 16 != 0 || a->dstate > kMaxStateDim) return SSD_ERR_BAD_SHAPE;
     if (a->batch > kMaxDim || a->seqlen > kMaxDim || a->nheads > kMaxDim || a->headdim > 4096)
         return SSD_ERR_BAD_SHAPE;
     if (a->nheads % a->ngroups != 0) return SSD_ERR_GROUPS;
@@ -176,27 +176,43 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
     return launched();
 }
 
-template <typename E, int Q>
-ssd_status run_state_q(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, E *states,
-                       hipStream_t st)
+// The state kernels cover all of N in one workgroup: NT = N rounded up to 64.
+template <typename F>
+ssd_status with_nt(int64_t N, F &&f)
 {
-    const int ntp = (int)((s.P + 63) / 64), ntn = (int)((s.N + 63) / 64);
-    dim3 grid((unsigned)(s.nc * s.H * ntp * ntn), (unsigned)s.b);
-    hipLaunchKernelGGL((k_chunk_state<E, Q>), grid, dim3(kThreads), 0, st, (const E *)a->x, (const E *)a->B,
-                       delta, cs, a->seq_idx, states, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
-                       (int)s.nc, ntp, ntn);
-    return launched();
+    if (N <= 64) return f(std::integral_constant<int, 64>{});
+    if (N <= 128) return f(std::integral_constant<int, 128>{});
+    return f(std::integral_constant<int, 256>{});
+}
+
+template <typename F>
+ssd_status with_q(int64_t Q, F &&f)
+{
+    if (Q == 64) return f(std::integral_constant<int, 64>{});
+    if (Q == 128) return f(std::integral_constant<int, 128>{});
+    return f(std::integral_constant<int, 256>{});
 }
 
 template <typename E>
 ssd_status run_state(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, E *states,
                      hipStream_t st)
 {
-    switch (s.Q) {
-    case 64: return run_state_q<E, 64>(s, a, delta, cs, states, st);
-    case 128: return run_state_q<E, 128>(s, a, delta, cs, states, st);
-    default: return run_state_q<E, 256>(s, a, delta, cs, states, st);
-    }
+    const int ntp = (int)((s.P + 63) / 64);
+    dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
+    return with_q(s.Q, [&](auto q) {
+        return with_nt(s.N, [&](auto nt) {
+            constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+            if (s.packed)
+                hipLaunchKernelGGL((k_chunk_state<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->x,
+                                   (const E *)a->B, delta, cs, a->seq_idx, states, (int)s.T, (int)s.H, (int)s.G,
+                                   (int)s.P, (int)s.N, (int)s.nc, ntp);
+            else
+                hipLaunchKernelGGL((k_chunk_state<E, Q, NT, false>), grid, dim3(kThreads), 0, st,
+                                   (const E *)a->x, (const E *)a->B, delta, cs, a->seq_idx, states, (int)s.T,
+                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
+            return launched();
+        });
+    });
 }
 
 template <typename E>
@@ -204,27 +220,10 @@ ssd_status run_passing(const Shape &s, const ssd_fwd_args *a, const float *cs, E
                        hipStream_t st)
 {
     const int64_t PN = s.P * s.N;
-    const int64_t vecs = s.b * s.H * PN / kVec16<E>;
+    const int64_t vecs = s.b * s.H * PN / 4;   // 4 elements per thread
     hipLaunchKernelGGL(k_state_passing<E>, dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, states, cs,
                        a->initial_states, final_states, a->seq_idx, (int)s.T, (int)s.H, PN, (int)s.nc,
                        (int)s.Q, vecs);
-    return launched();
-}
-
-template <typename E, int Q>
-ssd_status run_seq_final_q(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs,
-                           const E *hin, int32_t *seg_end, hipStream_t st)
-{
-    hipLaunchKernelGGL(k_seg_end_init, dim3(grid1(s.nseq, 256)), dim3(256), 0, st, seg_end, (int)s.nseq);
-    if (launched() != SSD_OK) return SSD_ERR_HIP;
-    hipLaunchKernelGGL(k_seg_end, dim3(grid1(s.T, 256)), dim3(256), 0, st, a->seq_idx, seg_end, (int)s.T,
-                       (int)s.nseq);
-    if (launched() != SSD_OK) return SSD_ERR_HIP;
-    const int ntp = (int)((s.P + 63) / 64), ntn = (int)((s.N + 63) / 64);
-    dim3 grid((unsigned)(s.nseq * s.H * ntp * ntn));
-    hipLaunchKernelGGL((k_seq_final<E, Q>), grid, dim3(kThreads), 0, st, (const E *)a->x, (const E *)a->B,
-                       delta, cs, a->seq_idx, hin, seg_end, a->final_states, (int)s.T, (int)s.H, (int)s.G,
-                       (int)s.P, (int)s.N, (int)s.nc, (int)s.nseq, ntp, ntn);
     return launched();
 }
 
@@ -232,30 +231,42 @@ template <typename E>
 ssd_status run_seq_final(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs,
                          const E *hin, int32_t *seg_end, hipStream_t st)
 {
-    switch (s.Q) {
-    case 64: return run_seq_final_q<E, 64>(s, a, delta, cs, hin, seg_end, st);
-    case 128: return run_seq_final_q<E, 128>(s, a, delta, cs, hin, seg_end, st);
-    default: return run_seq_final_q<E, 256>(s, a, delta, cs, hin, seg_end, st);
-    }
+    hipLaunchKernelGGL(k_seg_end_init, dim3(grid1(s.nseq, 256)), dim3(256), 0, st, seg_end, (int)s.nseq);
+    if (launched() != SSD_OK) return SSD_ERR_HIP;
+    hipLaunchKernelGGL(k_seg_end, dim3(grid1(s.T, 256)), dim3(256), 0, st, a->seq_idx, seg_end, (int)s.T,
+                       (int)s.nseq);
+    if (launched() != SSD_OK) return SSD_ERR_HIP;
+    const int ntp = (int)((s.P + 63) / 64);
+    dim3 grid((unsigned)(s.nseq * s.H * ntp));
+    return with_q(s.Q, [&](auto q) {
+        return with_nt(s.N, [&](auto nt) {
+            constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+            hipLaunchKernelGGL((k_seq_final<E, Q, NT>), grid, dim3(kThreads), 0, st, (const E *)a->x,
+                               (const E *)a->B, delta, cs, a->seq_idx, hin, seg_end, a->final_states, (int)s.T,
+                               (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, (int)s.nseq, ntp);
+            return launched();
+        });
+    });
 }
 
-template <typename E, int Q>
-ssd_status run_scan_q(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
-                      const E *hin, hipStream_t st)
+template <typename E, int Q, bool PACKED>
+ssd_status run_scan_qp(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
+                       const E *hin, hipStream_t st)
 {
     const int ntp = (int)((s.P + 63) / 64);
-    const size_t dyn = (size_t)64 * (size_t)(s.N + kVec16<E>) * sizeof(E);
     static bool attr_set = false;   // raising the dynamic-LDS cap is idempotent
     if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)k_chunk_scan<E, Q>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(64 * (kMaxState + kVec16<E>) * sizeof(E))) != hipSuccess)
+        if (hipFuncSetAttribute((const void *)k_chunk_scan<E, Q, PACKED>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)scan_region_bytes<E, Q>(kMaxStateDim)) != hipSuccess)
             return SSD_ERR_HIP;
         attr_set = true;
     }
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
-    hipLaunchKernelGGL((k_chunk_scan<E, Q>), grid, dim3(kThreads), dyn, st, (const E *)a->x, (const E *)a->C,
-                       delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T, (int)s.H, (int)s.G,
-                       (int)s.P, (int)s.N, (int)s.nc, ntp);
+    const size_t dyn = scan_region_bytes<E, Q>((int)s.N);
+    hipLaunchKernelGGL((k_chunk_scan<E, Q, PACKED>), grid, dim3(kThreads), dyn, st,
+                       (const E *)a->x, (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y,
+                       (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
     return launched();
 }
 
@@ -263,11 +274,11 @@ template <typename E>
 ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
                     const E *hin, hipStream_t st)
 {
-    switch (s.Q) {
-    case 64: return run_scan_q<E, 64>(s, a, delta, cs, cb, hin, st);
-    case 128: return run_scan_q<E, 128>(s, a, delta, cs, cb, hin, st);
-    default: return run_scan_q<E, 256>(s, a, delta, cs, cb, hin, st);
-    }
+    return with_q(s.Q, [&](auto q) {
+        constexpr int Q = decltype(q)::value;
+        return s.packed ? run_scan_qp<E, Q, true>(s, a, delta, cs, cb, hin, st)
+                        : run_scan_qp<E, Q, false>(s, a, delta, cs, cb, hin, st);
+    });
 }
 
 ssd_status fill_final(const Shape &s, const ssd_fwd_args *a, hipStream_t st)

@@ -25,8 +25,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // every kernel runs 4 waves of 64 lanes
+constexpr int kMaxStateDim = 256;   // largest supported N (state size per head)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // e^x through the hardware base-2 exponential (v_exp_f32).  Used only for
@@ -70,6 +72,12 @@ template <> __device__ __forceinline__ bf16x8 from_f32<bf16x8>(const floatx8 &v)
     return __builtin_convertvector(v, bf16x8);   // round to nearest even
 }
 template <> __device__ __forceinline__ floatx8 from_f32<floatx8>(const floatx8 &v) { return v; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const bf16x2 v = __builtin_convertvector(floatx2{lo, hi}, bf16x2);   // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ float to_float(float v) { return v; }
 __device__ __forceinline__ float to_float(bf16 v) { return (float)v; }
@@ -116,6 +124,31 @@ __device__ __forceinline__ void store4_f32(float *p, const float *in)
 __device__ __forceinline__ void store4_f32(bf16 *p, const float *in)
 {
     *reinterpret_cast<bf16x4 *>(p) = __builtin_convertvector(floatx4{in[0], in[1], in[2], in[3]}, bf16x4);
+}
+
+// Raw buffer resource over [base, base + bytes) (base must be wave-uniform).
+// A load whose offset falls outside the range returns zero, so masked or
+// out-of-range lanes need no branch: they use kOffNone.
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// Fragment (16 or 32 bytes) from a buffer at a byte offset.
+__device__ __forceinline__ void bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 &f)
+{
+    f = __builtin_bit_cast(bf16x8, bload16(r, off));
+}
+__device__ __forceinline__ void bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx8 &f)
+{
+    const floatx4 lo = __builtin_bit_cast(floatx4, bload16(r, off));
+    const floatx4 hi = __builtin_bit_cast(floatx4, bload16(r, off == kOffNone ? kOffNone : off + 16));
+    f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (XCD = id % 8), each with

@@ -22,7 +22,7 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 // chunk_cumsum
 // ---------------------------------------------------------------------------
-constexpr int kCumsumHeads = 16;   // heads per workgroup
+constexpr int kCumsumHeads = 4;   // one wave per head
 
 __device__ __forceinline__ float softplus_f(float z)
 {
@@ -30,75 +30,79 @@ __device__ __forceinline__ float softplus_f(float z)
     return z > 20.f ? z : log1pf(expf(z));
 }
 
-// Grid (nc, ceil(H/16), b).  The workgroup reads the chunk's dt rows for 16
-// heads (coalesced along heads), applies softplus, and each wave then runs one
-// head at a time: every lane owns Q/64 consecutive tokens, sums them
-// sequentially, and a segmented wave scan (a segment restarts at a packed
-// sequence boundary) combines the lanes.  Sums run in fp64 and are rounded
-// once, so a stored cs carries a single rounding.
+// Grid (nc, ceil(H/4), b): one wave per (chunk, head).  Every lane owns Q/64
+// consecutive tokens, sums them sequentially, and a segmented wave scan (a
+// segment restarts at a packed-sequence boundary) combines the lanes.  Sums run
+// in fp64 and are rounded once, so a stored cs carries a single rounding.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
     const E *__restrict__ dt, const float *__restrict__ A, const int32_t *__restrict__ seq_idx,
     float *__restrict__ delta, float *__restrict__ cs, int T, int H, int Q, int nc, int softplus)
 {
-    __shared__ float tile[256][kCumsumHeads + 1];
-    __shared__ int sq[256];
-    const int c = blockIdx.x, h0 = blockIdx.y * kCumsumHeads, b = blockIdx.z;
-    const int t0 = c * Q;
-    const int nh = min(kCumsumHeads, H - h0);
-    for (int idx = threadIdx.x; idx < Q * kCumsumHeads; idx += kThreads) {
-        const int i = idx / kCumsumHeads, hh = idx % kCumsumHeads;
-        const int t = t0 + i;
-        float v = 0.f;
-        if (t < T && hh < nh) {
-            const float z = to_float(dt[((int64_t)b * T + t) * H + h0 + hh]);
-            v = softplus ? softplus_f(z) : z;
-        }
-        tile[i][hh] = v;
-    }
-    if (seq_idx)
-        for (int i = threadIdx.x; i < Q; i += kThreads) sq[i] = (t0 + i < T) ? seq_idx[t0 + i] : 0;
-    __syncthreads();
-
+    const int c = blockIdx.x, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = blockIdx.y * kCumsumHeads + wave;
+    if (h >= H) return;   // whole wave; no barriers below
+    const int t0 = c * Q;
     const int per = Q >> 6;   // 1, 2 or 4 tokens per lane
-    for (int hh = wave; hh < nh; hh += 4) {
-        const int h = h0 + hh;
-        const double a = (double)A[h];
-        double loc[4];
-        int flg[4];
-        double run = 0.0;
-        int restarted = 0;
-        for (int j = 0; j < per; ++j) {
+    float dv[4];
+    int sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dv[j] = 0.f;
+        sv[j] = 0;
+        const int t = t0 + lane * per + j;
+        if (j < per && t < T) {
+            const float z = to_float(dt[((int64_t)b * T + t) * H + h]);
+            dv[j] = softplus ? softplus_f(z) : z;
+            if (seq_idx) sv[j] = seq_idx[t];
+        }
+    }
+    const int last_sv = per == 4 ? sv[3] : (per == 2 ? sv[1] : sv[0]);
+    const int before = __shfl_up(last_sv, 1);   // id of the token just before this lane's first
+    const double a = (double)A[h];
+    double loc[4];
+    int flg[4];
+    double run = 0.0;
+    int restarted = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < per) {
             const int i = lane * per + j;
-            if (seq_idx && i > 0 && t0 + i < T && sq[i] != sq[i - 1]) {
+            const int prev = j == 0 ? before : sv[j - 1];
+            if (seq_idx && i > 0 && t0 + i < T && sv[j] != prev) {
                 run = 0.0;
                 restarted = 1;
             }
-            run += (double)tile[i][hh] * a;
+            run += (double)dv[j] * a;
             loc[j] = run;
             flg[j] = restarted;
         }
-        // segmented inclusive scan of (restarted, run) over the 64 lanes
-        double v = run;
-        int f = restarted;
-        for (int off = 1; off < 64; off <<= 1) {
-            const double vo = __shfl_up(v, off);
-            const int fo = __shfl_up(f, off);
-            if (lane >= off) {
-                if (!f) v += vo;
-                f |= fo;
-            }
+    }
+    // segmented inclusive scan of (restarted, run) over the 64 lanes
+    double v = run;
+    int f = restarted;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double vo = __shfl_up(v, off);
+        const int fo = __shfl_up(f, off);
+        if (lane >= off) {
+            if (!f) v += vo;
+            f |= fo;
         }
-        double carry = __shfl_up(v, 1);
-        if (lane == 0) carry = 0.0;
-        const int64_t o = (((int64_t)b * H + h) * nc + c) * Q + lane * per;
-        for (int j = 0; j < per; ++j) {
-            delta[o + j] = tile[lane * per + j][hh];
+    }
+    double carry = __shfl_up(v, 1);
+    if (lane == 0) carry = 0.0;
+    const int64_t o = (((int64_t)b * H + h) * nc + c) * Q + lane * per;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < per) {
+            delta[o + j] = dv[j];
             cs[o + j] = (float)(flg[j] ? loc[j] : carry + loc[j]);
         }
     }
 }
+
 
 // ---------------------------------------------------------------------------
 // chunk_cb: cb[b,c,g,t,s] = sum_n C[t,n] B[s,n] for the lower block triangle
@@ -106,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
 // One workgroup per 64x64 (t, s) tile with s-tile <= t-tile; four waves of 32x32.
 // The MFMA computes D[s][t] (A = B rows, B = C rows, K = n, both K-contiguous in
 // memory), so each lane ends with 4 consecutive s of one t: a vector store.
+// Operand fragments are fetched two K steps ahead of their use.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_chunk_cb(
     const E *__restrict__ Bm, const E *__restrict__ Cm, E *__restrict__ cb,
@@ -135,16 +140,28 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(
         brow[i] = Bm + (((int64_t)b * T + t0 + (bv[i] ? s : 0)) * G + g) * N;
         crow[i] = Cm + (((int64_t)b * T + t0 + (cv[i] ? t : 0)) * G + g) * N;
     }
-    floatx4 acc[2][2] = {};
-    for (int k0 = 0; k0 < N; k0 += 32) {
-        const int k = k0 + 8 * lg;
+    const int nks = (N + 31) / 32;
+    F a0[2] = {F{}, F{}}, b0[2] = {F{}, F{}}, a1[2] = {F{}, F{}}, b1[2] = {F{}, F{}};
+    auto fetch = [&](F (&a)[2], F (&bb)[2], int ks) {
+        const int k = ks * 32 + 8 * lg;
         const bool kin = k < N;
-        F a[2], bb[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             a[i] = (bv[i] && kin) ? load_frag(brow[i] + k) : F{};
             bb[i] = (cv[i] && kin) ? load_frag(crow[i] + k) : F{};
         }
+    };
+    fetch(a0, b0, 0);
+    if (nks > 1) fetch(a1, b1, 1);
+    floatx4 acc[2][2] = {};
+    for (int ks = 0; ks < nks; ++ks) {
+        F a[2] = {a0[0], a0[1]}, bb[2] = {b0[0], b0[1]};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            a0[i] = a1[i];
+            b0[i] = b1[i];
+        }
+        if (ks + 2 < nks) fetch(a1, b1, ks + 2);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -161,129 +178,253 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(
         }
 }
 
-// ---------------------------------------------------------------------------
-// Shared pieces of the state kernels
-// ---------------------------------------------------------------------------
 
-// Copy a [Q rows (time) x 64 cols] tile from global memory (row stride `ld`
-// elements; rows >= slen and cols >= ncols read as zero) into LDS transposed,
-// dst[col][row] with a pitch of Q + 16 bytes, optionally scaling row s by w[s]
-// where m[s] != 0 and zeroing it where m[s] == 0 (a select, so a non-finite input
-// in a masked row cannot leak).  Each thread moves V x V blocks (V = 16 B / elem).
-template <typename E, int Q, bool SCALE>
-__device__ __forceinline__ void stage_transposed(E *__restrict__ dst, const E *__restrict__ src, int64_t ld,
-                                                 int slen, int ncols, const float *w, const int *m)
+// ---------------------------------------------------------------------------
+// K tiles: LDS tiles whose MFMA K index (time) is the slow axis in memory
+// ---------------------------------------------------------------------------
+// KTile<E, KR, COLS> holds rows 0..KR-1 (time) and columns 0..COLS-1 of a
+// row-major global array (row stride `ld` elements).  load() issues the
+// global loads into registers, store() writes LDS (optionally scaling row r by
+// w[r], and with SEL zeroing rows whose m[r] == 0 by a select, so a masked
+// non-finite input cannot leak), and frag(tile, k0, col0) returns the MFMA
+// fragment for K rows k0..k0+31 and columns col0..col0+15.
+//
+// bf16: the tile stays row-major in LDS (plain 16-byte copies) and fragments are
+// read with ds_read_b64_tr_b16.  Within each 16-lane group, lane j points at
+// row k0 + 8*(lane/16) + j/4, column col0 + 4*(j%4); the instruction hands lane
+// j column col0 + j of those four rows, i.e. four consecutive K values of one
+// column.  Two reads (rows +0..3 and +4..7) make the 8-wide fragment.  Rows are
+// padded by 32 bytes so a group's four rows fall on disjoint banks.
+// fp32: there is no 32-bit transpose read, so the tile is transposed in registers
+// on its way into LDS ([col][row], rows padded by 16 bytes) and fragments are
+// plain 32-byte reads.
+template <typename E, int KR, int COLS> struct KTile;
+
+template <int KR, int COLS>
+struct KTile<bf16, KR, COLS> {
+    static constexpr int PITCH = COLS + 16;
+    static constexpr int SIZE = KR * PITCH;
+    static constexpr int VPR = COLS / 8;   // 16-byte vectors per row
+    static constexpr int NV = KR * VPR;
+    static constexpr int PER = (NV + kThreads - 1) / kThreads;
+    uint4 raw[PER];
+
+    __device__ __forceinline__ void load(const bf16 *src, int64_t ld, int slen, int ncols)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * kThreads;
+            const int r = v / VPR, c = v % VPR;
+            uint4 x = {0u, 0u, 0u, 0u};
+            if (v < NV && r < slen && c * 8 < ncols)
+                x = *reinterpret_cast<const uint4 *>(src + (int64_t)r * ld + c * 8);
+            raw[i] = x;
+        }
+    }
+
+    template <bool SCALE, bool SEL>
+    __device__ __forceinline__ void store(bf16 *dst, const float *w, const int *m) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * kThreads;
+            if (NV % kThreads != 0 && v >= NV) continue;
+            const int r = v / VPR, c = v % VPR;
+            uint4 o = raw[i];
+            if constexpr (SCALE) {
+                const float ws = w[r];
+                const bool keep = !SEL || m[r] != 0;
+                uint32_t q[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(q[e] << 16) * ws;
+                    const float hi = __uint_as_float(q[e] & 0xffff0000u) * ws;
+                    q[e] = keep ? pack_bf16x2(lo, hi) : 0u;
+                }
+                o = uint4{q[0], q[1], q[2], q[3]};
+            }
+            *reinterpret_cast<uint4 *>(dst + r * PITCH + c * 8) = o;
+        }
+    }
+
+    __device__ __forceinline__ static bf16x8 frag(const bf16 *tile, int k0, int col0)
+    {
+        typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+        const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+        bf16 *p = const_cast<bf16 *>(tile) + (k0 + 8 * g + (j >> 2)) * PITCH + col0 + 4 * (j & 3);
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 4 * PITCH));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+};
+
+template <int KR, int COLS>
+struct KTile<float, KR, COLS> {
+    static constexpr int PITCH = KR + 4;
+    static constexpr int SIZE = COLS * PITCH;
+    static constexpr int CBK = COLS / 4;
+    static constexpr int NB = (KR / 4) * CBK;   // 4x4 blocks
+    static constexpr int PER = (NB + kThreads - 1) / kThreads;
+    uint4 raw[PER][4];
+
+    __device__ __forceinline__ void load(const float *src, int64_t ld, int slen, int ncols)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int blk = threadIdx.x + i * kThreads;
+            const int cbk = blk % CBK, sb = blk / CBK;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = sb * 4 + r;
+                uint4 v = {0u, 0u, 0u, 0u};
+                if (blk < NB && s < slen && cbk * 4 < ncols)
+                    v = *reinterpret_cast<const uint4 *>(src + (int64_t)s * ld + cbk * 4);
+                raw[i][r] = v;
+            }
+        }
+    }
+
+    template <bool SCALE, bool SEL>
+    __device__ __forceinline__ void store(float *dst, const float *w, const int *m) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int blk = threadIdx.x + i * kThreads;
+            if (NB % kThreads != 0 && blk >= NB) continue;
+            const int cbk = blk % CBK, sb = blk / CBK;
+            float f[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t q[4] = {raw[i][r].x, raw[i][r].y, raw[i][r].z, raw[i][r].w};
+                float ws = 1.f;
+                bool keep = true;
+                if constexpr (SCALE) ws = w[sb * 4 + r];
+                if constexpr (SEL) keep = m[sb * 4 + r] != 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = __uint_as_float(q[e]);
+                    f[r][e] = keep ? (SCALE ? v * ws : v) : 0.f;
+                }
+            }
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                *reinterpret_cast<floatx4 *>(dst + (cbk * 4 + cc) * PITCH + sb * 4) =
+                    floatx4{f[0][cc], f[1][cc], f[2][cc], f[3][cc]};
+        }
+    }
+
+    __device__ __forceinline__ static floatx8 frag(const float *tile, int k0, int col0)
+    {
+        const int lane = threadIdx.x & 63;
+        return load_frag(tile + (col0 + (lane & 15)) * PITCH + k0 + 8 * (lane >> 4));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// chunk_state / seq_final: the staged state product
+// ---------------------------------------------------------------------------
+// One workgroup covers 64 p x NT n (NT = N rounded up to 64, so all of N) of one
+// (chunk, head), streamed over time in 64-step K chunks; the next chunk's global
+// loads are issued before the current chunk's MFMAs.  The product is
+// D[n][p] = sum_s B^T[n][s] (w_s x_s)[p]; wave w owns n rows w*NT/4 .. +NT/4:
+//   acc[i][j][r]  <->  n = w*NT/4 + i*16 + 4*(lane/16) + r,  p = j*16 + lane%16.
+// w and m (per-token weights and keep flags, length Q) must be in LDS and
+// visible before the call.
+template <typename E, int NT>
+struct StateSmem {
+    using XT = KTile<E, 64, 64>;
+    using BT = KTile<E, 64, NT>;
+    E x[XT::SIZE];
+    E b[BT::SIZE];
+};
+
+template <typename E, int NT, bool SEL>
+__device__ __forceinline__ void state_product(StateSmem<E, NT> &sm, const E *xsrc, int64_t ldx, const E *bsrc,
+                                              int64_t ldb, int slen, int pcols, int ncols, const float *w,
+                                              const int *m, typename StateSmem<E, NT>::XT &xs,
+                                              typename StateSmem<E, NT>::BT &bs, floatx4 (&acc)[NT / 64][4])
 {
-    constexpr int V = kVec16<E>;
-    constexpr int PITCH = Q + V;
-    constexpr int CB = 64 / V;
-    constexpr int NB = (Q / V) * CB;
-    for (int blk = threadIdx.x; blk < NB; blk += kThreads) {
-        const int cbk = blk % CB, sb = blk / CB;
-        const int col0 = cbk * V;
-        float v[V][V];
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const int s = sb * V + i;
-            if (s < slen && col0 < ncols) {
-                load16_f32(src + (int64_t)s * ld + col0, v[i]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < V; ++j) v[i][j] = 0.f;
-            }
-            if (SCALE) {
-                const float ws = w[s];
-                const bool keep = m[s] != 0;
-#pragma unroll
-                for (int j = 0; j < V; ++j) v[i][j] = keep ? v[i][j] * ws : 0.f;
-            }
+    using XT = typename StateSmem<E, NT>::XT;
+    using BT = typename StateSmem<E, NT>::BT;
+    constexpr int NI = NT / 64;
+    const int wave = threadIdx.x >> 6;
+    for (int kb = 0; kb < slen; kb += 64) {
+        xs.template store<true, SEL>(sm.x, w + kb, m + kb);
+        bs.template store<false, false>(sm.b, nullptr, nullptr);
+        __syncthreads();
+        if (kb + 64 < slen) {
+            xs.load(xsrc + (int64_t)(kb + 64) * ldx, ldx, slen - kb - 64, pcols);
+            bs.load(bsrc + (int64_t)(kb + 64) * ldb, ldb, slen - kb - 64, ncols);
         }
+        const int kend = min(64, ((slen - kb) + 31) & ~31);
+        for (int ks = 0; ks < kend; ks += 32) {
+            frag_t<E> a[NI], bb[4];
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-            float col[V];
+            for (int i = 0; i < NI; ++i) a[i] = BT::frag(sm.b, ks, wave * (NT / 4) + i * 16);
 #pragma unroll
-            for (int i = 0; i < V; ++i) col[i] = v[i][j];
-            store16_f32(dst + (col0 + j) * PITCH + sb * V, col);
+            for (int j = 0; j < 4; ++j) bb[j] = XT::frag(sm.x, ks, j * 16);
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mma(acc[i][j], a[i], bb[j]);
         }
+        __syncthreads();
     }
 }
 
-// acc[i][j][r] += sum_s bt[n][s] * xt[p][s] for the wave's 32x32 (n, p) quadrant,
-// n = wn*32 + i*16 + 4*(lane/16) + r, p = wp*32 + j*16 + lane%16.
-template <typename E, int Q>
-__device__ __forceinline__ void state_mma(const E *bt, const E *xt, floatx4 (&acc)[2][2], int kend)
-{
-    constexpr int PITCH = Q + kVec16<E>;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    const int wn = wave >> 1, wp = wave & 1;
-    const E *a0p = bt + (wn * 32 + li) * PITCH + 8 * lg;
-    const E *a1p = a0p + 16 * PITCH;
-    const E *b0p = xt + (wp * 32 + li) * PITCH + 8 * lg;
-    const E *b1p = b0p + 16 * PITCH;
-    for (int ks = 0; ks < kend; ks += 32) {
-        const auto a0 = load_frag(a0p + ks), a1 = load_frag(a1p + ks);
-        const auto b0 = load_frag(b0p + ks), b1 = load_frag(b1p + ks);
-        mma(acc[0][0], a0, b0);
-        mma(acc[0][1], a0, b1);
-        mma(acc[1][0], a1, b0);
-        mma(acc[1][1], a1, b1);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// chunk_state: states[b,c,h,p,n] = sum_s w_s x_s[p] B_s[n]
-// ---------------------------------------------------------------------------
-// w_s = exp(cs_last - cs_s) * delta_s for s in the segment of the chunk's last
-// token (0 elsewhere).  One workgroup per (c, h, 64-p tile, 64-n tile); the
-// product runs as D[n][p] = sum_s B^T[n][s] X'^T[p][s] so each lane stores 4
-// consecutive n of one p.
-template <typename E, int Q>
-__global__ __launch_bounds__(kThreads) void k_chunk_state(
+// chunk_state: states[b,c,h,p,n] = sum_s w_s x_s[p] B_s[n], w_s = exp(cs_last -
+// cs_s) delta_s for s in the segment of the chunk's last token (0 elsewhere).
+// One workgroup per (b, c, h, 64-p tile).
+template <typename E, int Q, int NT, bool PACKED>
+__global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
     const E *__restrict__ x, const E *__restrict__ Bm, const float *__restrict__ delta,
     const float *__restrict__ cs, const int32_t *__restrict__ seq_idx, E *__restrict__ states,
-    int T, int H, int G, int P, int N, int nc, int ntp, int ntn)
+    int T, int H, int G, int P, int N, int nc, int ntp)
 {
-    constexpr int PITCH = Q + kVec16<E>;
-    __shared__ __align__(16) E xt[64 * PITCH];
-    __shared__ __align__(16) E bt[64 * PITCH];
+    constexpr int NI = NT / 64;
+    __shared__ __align__(16) StateSmem<E, NT> sm;
     __shared__ float w[Q];
     __shared__ int m[Q];
-    const int units = nc * H * ntp * ntn;
+    const int units = nc * H * ntp;
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
-    int r = u;
-    const int tn = r % ntn; r /= ntn;
-    const int tp = r % ntp; r /= ntp;
-    const int h = r % H;
-    const int c = r / H;
+    const int tp = u % ntp;
+    const int h = (u / ntp) % H;
+    const int c = u / (ntp * H);
     const int g = h / (H / G);
     const int t0 = c * Q, len = min(Q, T - t0);
+    const int p0 = tp * 64;
+    const E *xsrc = x + (((int64_t)b * T + t0) * H + h) * P + p0;
+    const E *bsrc = Bm + (((int64_t)b * T + t0) * G + g) * N;
+    const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
+    typename StateSmem<E, NT>::XT xs;
+    typename StateSmem<E, NT>::BT bs;
+    xs.load(xsrc, ldx, len, P - p0);
+    bs.load(bsrc, ldb, len, N);
+
     const int64_t cso = (((int64_t)b * H + h) * nc + c) * Q;
     const float lam = cs[cso + len - 1];
-    const int seq_last = seq_idx ? seq_idx[t0 + len - 1] : 0;
+    const int seq_last = PACKED ? seq_idx[t0 + len - 1] : 0;
     for (int s = threadIdx.x; s < Q; s += kThreads) {
-        const bool keep = s < len && (!seq_idx || seq_idx[t0 + s] == seq_last);
+        const bool keep = s < len && (!PACKED || seq_idx[t0 + s] == seq_last);
         m[s] = keep;
         w[s] = keep ? exp_neg(lam - cs[cso + s]) * delta[cso + s] : 0.f;
     }
     __syncthreads();
-    const int p0 = tp * 64, n0 = tn * 64;
-    stage_transposed<E, Q, true>(xt, x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len,
-                                 P - p0, w, m);
-    stage_transposed<E, Q, false>(bt, Bm + (((int64_t)b * T + t0) * G + g) * N + n0, (int64_t)G * N, len,
-                                  N - n0, nullptr, nullptr);
-    __syncthreads();
-    floatx4 acc[2][2] = {};
-    state_mma<E, Q>(bt, xt, acc, (len + 31) & ~31);
+    floatx4 acc[NI][4];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    state_product<E, NT, PACKED>(sm, xsrc, ldx, bsrc, ldb, len, P - p0, N, w, m, xs, bs, acc);
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    const int wn = wave >> 1, wp = wave & 1;
     E *out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 32 + i * 16 + 4 * lg, p = p0 + wp * 32 + j * 16 + li;
+        for (int j = 0; j < 4; ++j) {
+            const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = p0 + j * 16 + li;
             if (p < P && n < N) {
                 float o[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
                 store4_f32(out + (int64_t)p * N + n, o);
@@ -294,11 +435,27 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
 // ---------------------------------------------------------------------------
 // state_passing: in place S_c -> h_{c-1}; h_c = exp(cs_last(c)) h_{c-1} + S_c
 // ---------------------------------------------------------------------------
-// Every (b, h, p, n) element is an independent length-nc scan, so each thread
-// owns one 16-byte vector of elements and walks the chunks, loading kPrefetch
-// chunk states ahead of the arithmetic to keep many loads in flight.  The
-// carry is replaced by zero (a select) when the chunk holds a segment boundary.
-constexpr int kPrefetch = 8;
+// Every (b, h, p, n) element is an independent length-nc scan.  Each thread owns
+// 4 consecutive elements and walks the chunks with a ring of kPrefetch loads in
+// flight: the slot a chunk's state is read from is refilled with the state
+// kPrefetch chunks ahead before the arithmetic.  The carry is replaced by zero
+// (a select) when the chunk holds a segment boundary.
+constexpr int kPrefetch = 16;
+
+template <typename E> struct Raw4;
+template <> struct Raw4<bf16> { using type = uint2; };
+template <> struct Raw4<float> { using type = uint4; };
+
+__device__ __forceinline__ void unpack4(const uint2 &v, float *o)
+{
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack4(const uint4 &v, float *o)
+{
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_state_passing(
@@ -306,50 +463,58 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
     float *__restrict__ final_states, const int32_t *__restrict__ seq_idx,
     int T, int H, int64_t PN, int nc, int Q, int64_t total_vecs)
 {
-    constexpr int V = kVec16<E>;
+    using R = typename Raw4<E>::type;
+    constexpr int D = kPrefetch;
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= total_vecs) return;
-    const int64_t vecs_per_head = PN / V;
-    const int64_t e0 = (gid % vecs_per_head) * V;
-    const int64_t bh = gid / vecs_per_head;
+    const int64_t vph = PN / 4;
+    const int64_t e0 = (gid % vph) * 4;
+    const int64_t bh = gid / vph;
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
-    float hs[V];
-    if (init) {
-#pragma unroll
-        for (int v = 0; v < V; v += 4) load16_f32(init + bh * PN + e0 + v, hs + v);
-    } else {
-#pragma unroll
-        for (int v = 0; v < V; ++v) hs[v] = 0.f;
-    }
-    const float *lam_ptr = cs + bh * (int64_t)nc * Q + (Q - 1);
+    float hs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (init) load4_f32(init + bh * PN + e0, hs);
+    const float *lamp = cs + bh * (int64_t)nc * Q + (Q - 1);
     const int64_t cstride = (int64_t)H * PN;
     E *base = states + (b * nc * H + h) * PN + e0;
-    for (int c0 = 0; c0 < nc; c0 += kPrefetch) {
-        float sv[kPrefetch][V];
+    R buf[D];
+    float lam[D];
+    int sl[D];
 #pragma unroll
-        for (int k = 0; k < kPrefetch; ++k)
-            if (c0 + k < nc) load16_f32(base + (int64_t)(c0 + k) * cstride, sv[k]);
+    for (int k = 0; k < D; ++k) {
+        sl[k] = 0;
+        lam[k] = 0.f;
+        if (k < nc) {
+            buf[k] = *reinterpret_cast<const R *>(base + (int64_t)k * cstride);
+            lam[k] = lamp[(int64_t)k * Q];
+            if (seq_idx) sl[k] = seq_idx[min(k * Q + Q, T) - 1];
+        }
+    }
+    int sprev = seq_idx ? seq_idx[0] : 0;
+    for (int c0 = 0; c0 < nc; c0 += D) {
 #pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) {
+        for (int k = 0; k < D; ++k) {
             const int c = c0 + k;
             if (c < nc) {
-                store16_f32(base + (int64_t)c * cstride, hs);
-                const float d = exp_neg(lam_ptr[(int64_t)c * Q]);
-                bool keep = true;
-                if (seq_idx) {
-                    const int last = min(c * Q + Q, T) - 1;
-                    keep = seq_idx[last] == seq_idx[c > 0 ? c * Q - 1 : 0];
+                float sv[4];
+                unpack4(buf[k], sv);
+                const float lm = lam[k];
+                const int sc = sl[k];
+                if (c + D < nc) {
+                    buf[k] = *reinterpret_cast<const R *>(base + (int64_t)(c + D) * cstride);
+                    lam[k] = lamp[(int64_t)(c + D) * Q];
+                    if (seq_idx) sl[k] = seq_idx[min((c + D) * Q + Q, T) - 1];
                 }
+                store4_f32(base + (int64_t)c * cstride, hs);
+                const bool keep = !seq_idx || sc == sprev;
+                sprev = sc;
+                const float d = exp_neg(lm);
 #pragma unroll
-                for (int v = 0; v < V; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[k][v];
+                for (int v = 0; v < 4; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
             }
         }
     }
-    if (final_states) {
-#pragma unroll
-        for (int v = 0; v < V; v += 4) store16_f32(final_states + bh * PN + e0 + v, hs + v);
-    }
+    if (final_states) store4_f32(final_states + bh * PN + e0, hs);
 }
 
 // ---------------------------------------------------------------------------
@@ -373,45 +538,48 @@ __global__ void k_seg_end(const int32_t *__restrict__ seq_idx, int32_t *__restri
 // final_states[sg,h,p,n] = state right after segment sg's last token t_e:
 //   sum_{s in t_e's chunk, s <= t_e, seq_s = sg} exp(cs_te - cs_s) delta_s x_s[p] B_s[n]
 //   + [the segment was already open when the chunk started] exp(cs_te) Hin_c[p][n].
-// An id that never occurs gets zeros.
-template <typename E, int Q>
-__global__ __launch_bounds__(kThreads) void k_seq_final(
+// An id that never occurs gets zeros.  Batch is 1 with packed streams.
+template <typename E, int Q, int NT>
+__global__ __launch_bounds__(kThreads, 2) void k_seq_final(
     const E *__restrict__ x, const E *__restrict__ Bm, const float *__restrict__ delta,
     const float *__restrict__ cs, const int32_t *__restrict__ seq_idx, const E *__restrict__ hin,
     const int32_t *__restrict__ seg_end, float *__restrict__ final_states,
-    int T, int H, int G, int P, int N, int nc, int nseq, int ntp, int ntn)
+    int T, int H, int G, int P, int N, int nc, int nseq, int ntp)
 {
-    constexpr int PITCH = Q + kVec16<E>;
-    __shared__ __align__(16) E xt[64 * PITCH];
-    __shared__ __align__(16) E bt[64 * PITCH];
+    constexpr int NI = NT / 64;
+    __shared__ __align__(16) StateSmem<E, NT> sm;
     __shared__ float w[Q];
     __shared__ int m[Q];
-    const int units = nseq * H * ntp * ntn;
+    const int units = nseq * H * ntp;
     const int u = xcd_remap(blockIdx.x, units);
-    int r = u;
-    const int tn = r % ntn; r /= ntn;
-    const int tp = r % ntp; r /= ntp;
-    const int h = r % H;
-    const int sg = r / H;
+    const int tp = u % ntp;
+    const int h = (u / ntp) % H;
+    const int sg = u / (ntp * H);
     const int g = h / (H / G);
-    const int p0 = tp * 64, n0 = tn * 64;
+    const int p0 = tp * 64;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    const int wn = wave >> 1, wp = wave & 1;
     float *out = final_states + ((int64_t)sg * H + h) * (int64_t)P * N;
     const int te = seg_end[sg];
     if (te < 0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int n = n0 + wn * 32 + i * 16 + 4 * lg, p = p0 + wp * 32 + j * 16 + li;
+            for (int j = 0; j < 4; ++j) {
+                const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = p0 + j * 16 + li;
                 float z[4] = {0.f, 0.f, 0.f, 0.f};
                 if (p < P && n < N) store4_f32(out + (int64_t)p * N + n, z);
             }
         return;
     }
     const int c = te / Q, t0 = c * Q, ie = te - t0;
-    const int64_t cso = ((int64_t)h * nc + c) * Q;   // batch is 1 with seq_idx
+    const E *xsrc = x + ((int64_t)t0 * H + h) * P + p0;
+    const E *bsrc = Bm + ((int64_t)t0 * G + g) * N;
+    const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
+    typename StateSmem<E, NT>::XT xs;
+    typename StateSmem<E, NT>::BT bs;
+    xs.load(xsrc, ldx, ie + 1, P - p0);
+    bs.load(bsrc, ldb, ie + 1, N);
+    const int64_t cso = ((int64_t)h * nc + c) * Q;
     const float cse = cs[cso + ie];
     for (int s = threadIdx.x; s < Q; s += kThreads) {
         const bool keep = s <= ie && seq_idx[t0 + s] == sg;
@@ -419,21 +587,21 @@ __global__ __launch_bounds__(kThreads) void k_seq_final(
         w[s] = keep ? exp_neg(cse - cs[cso + s]) * delta[cso + s] : 0.f;
     }
     __syncthreads();
-    stage_transposed<E, Q, true>(xt, x + ((int64_t)t0 * H + h) * P + p0, (int64_t)H * P, ie + 1, P - p0, w, m);
-    stage_transposed<E, Q, false>(bt, Bm + ((int64_t)t0 * G + g) * N + n0, (int64_t)G * N, ie + 1, N - n0,
-                                  nullptr, nullptr);
-    __syncthreads();
-    floatx4 acc[2][2] = {};
-    state_mma<E, Q>(bt, xt, acc, (ie + 1 + 31) & ~31);
+    floatx4 acc[NI][4];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    state_product<E, NT, true>(sm, xsrc, ldx, bsrc, ldb, ie + 1, P - p0, N, w, m, xs, bs, acc);
 
     const bool carry = seq_idx[c > 0 ? t0 - 1 : 0] == sg;
     const float dcar = exp_neg(cse);
     const E *hc = hin + ((int64_t)c * H + h) * (int64_t)P * N;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 32 + i * 16 + 4 * lg, p = p0 + wp * 32 + j * 16 + li;
+        for (int j = 0; j < 4; ++j) {
+            const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = p0 + j * 16 + li;
             if (p < P && n < N) {
                 float hv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (carry) load4_f32(hc + (int64_t)p * N + n, hv);
@@ -450,33 +618,59 @@ __global__ __launch_bounds__(kThreads) void k_seq_final(
 // ---------------------------------------------------------------------------
 // One workgroup per (b, c, h, 64-p tile).  The chunk's Q output rows are split
 // into 16-row sub-blocks j (t0 = 16 j); wave w owns j = w, w+4, ... so the
-// causal work is balanced.  Everything is computed transposed, D[p][t], so the
-// per-head decay enters as a per-column (per-lane) scale:
+// causal work is balanced.  Everything is computed transposed, D[p][t], so a
+// per-token decay is a per-lane scale:
 //   y_t = u_t [ e_{t0} (C_t . Hin) + sum_{s < S_j} CB[t][s] V_j[s] x_s ]
-//         + sum_{S_j <= s <= t} CB[t][s] exp(cs_t - cs_s) delta_s x_s  + D x_t
+//         + sum_{S_j <= s <= t} (CB[t][s] exp(cs_t - cs_s) delta_s + [s = t] D) x_s
 // with e_{t0} = exp(cs_{t0}), u_t = exp(cs_t - cs_{t0}), V_j[s] = exp(cs_{t0} -
 // cs_s) delta_s, and S_j = 32 floor(j/2) the start of the 32-wide K step that
-// holds t0.  Every factor is a decay <= 1, so nothing overflows, and the
-// per-element exponentials are needed only on the diagonal step.  Segment
-// masks (packed streams) are selects on the same factors.
+// holds t0.  Every factor is a decay <= 1, so nothing overflows, and
+// per-element exponentials are needed only on the diagonal step, where the D
+// skip term rides on the diagonal.  Segment masks (packed streams) are selects
+// on the same factors.
+// Memory: the entering-state tile (step 4) and then the x tile (step 1) occupy
+// one LDS region in turn; all their global loads are issued up front.  The C and
+// CB fragments (one row per lane, 16/32 bytes) are buffer loads fetched two K
+// steps ahead; rows past the sequence end fall outside the buffer range and read
+// as zero.
+
+// V_j rows are stored packed: row j holds 32 * floor(j/2) entries.
+__host__ __device__ constexpr int vt_offset(int j)
+{
+    return 32 * ((j & 1) ? (j >> 1) * (j >> 1) : (j >> 1) * ((j >> 1) - 1));
+}
+
+// LDS bytes of the region shared by the entering-state tile and the x tile.
 template <typename E, int Q>
-__global__ __launch_bounds__(kThreads) void k_chunk_scan(
+__host__ __device__ constexpr size_t scan_region_bytes(int N)
+{
+    const size_t hs = (size_t)64 * (N + kVec16<E>) * sizeof(E);
+    const size_t xt = (size_t)KTile<E, Q, 64>::SIZE * sizeof(E);
+    return hs > xt ? hs : xt;
+}
+
+template <typename E, int Q, bool PACKED>
+__global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     const E *__restrict__ x, const E *__restrict__ Cm, const float *__restrict__ delta,
     const float *__restrict__ cs, const E *__restrict__ cb, const E *__restrict__ hin,
     const float *__restrict__ D, const int32_t *__restrict__ seq_idx, E *__restrict__ y,
     int T, int H, int G, int P, int N, int nc, int ntp)
 {
     using F = frag_t<E>;
+    using XT = KTile<E, Q, 64>;
     constexpr int V = kVec16<E>;
-    constexpr int XP = Q + V;     // pitch of the x^T tile
-    constexpr int NJ = Q / 16;    // 16-row sub-blocks per chunk
-    constexpr int NSB = Q / 64;   // sub-blocks per wave
-    __shared__ __align__(16) E xt[64 * XP];
-    __shared__ __align__(16) float vt[NJ * Q];
-    __shared__ float csb[Q], db[Q];
-    __shared__ int sq[Q];
+    constexpr int ES = (int)sizeof(E);
+    constexpr int NJ = Q / 16;     // 16-row sub-blocks per chunk
+    constexpr int NSB = Q / 64;    // sub-blocks per wave
+    constexpr int KSB = (NJ - 1) / 2;   // K steps strictly below some sub-block's diagonal
+    constexpr int HMAX = 64 * kMaxStateDim / V / kThreads;   // Hin vectors per thread
+    __shared__ __align__(16) float vt[vt_offset(NJ)];
+    __shared__ __align__(16) float csb[Q];
+    __shared__ __align__(16) float db[Q];
+    __shared__ __align__(16) int sq[PACKED ? Q : 4];
     extern __shared__ __align__(16) char dyn_smem[];
-    E *hs = reinterpret_cast<E *>(dyn_smem);   // entering state tile [64 p][N], pitch N + V
+    E *hs = reinterpret_cast<E *>(dyn_smem);   // entering-state tile [64 p][N], pitch N + V
+    E *xt = reinterpret_cast<E *>(dyn_smem);   // later: the x tile
     const int HP = N + V;
 
     const int units = nc * H * ntp;
@@ -489,71 +683,123 @@ __global__ __launch_bounds__(kThreads) void k_chunk_scan(
     const int t0 = c * Q, len = min(Q, T - t0);
     const int p0 = tp * 64;
     const int64_t cso = (((int64_t)b * H + h) * nc + c) * Q;
-
-    for (int i = threadIdx.x; i < Q; i += kThreads) {
-        csb[i] = cs[cso + i];
-        db[i] = delta[cso + i];
-        sq[i] = seq_idx ? seq_idx[t0 + min(i, len - 1)] : 0;
-    }
-    const int seq_prev = seq_idx ? seq_idx[c > 0 ? t0 - 1 : 0] : 0;
-    {
-        const E *src = hin + ((((int64_t)b * nc + c) * H + h) * P + p0) * (int64_t)N;
-        const int vpr = N / V;
-        for (int idx = threadIdx.x; idx < 64 * vpr; idx += kThreads) {
-            const int pr = idx / vpr, nv = idx % vpr;
-            uint4 v = {0u, 0u, 0u, 0u};
-            if (p0 + pr < P) v = *reinterpret_cast<const uint4 *>(src + (int64_t)pr * N + nv * V);
-            *reinterpret_cast<uint4 *>(hs + pr * HP + nv * V) = v;
-        }
-    }
-    stage_transposed<E, Q, false>(xt, x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len,
-                                  P - p0, nullptr, nullptr);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < NJ * Q; idx += kThreads) {
-        const int j = idx / Q, s = idx % Q;
-        if (s < 32 * (j >> 1)) {
-            const int tj = 16 * j;
-            const bool keep = sq[s] == sq[tj];
-            vt[idx] = keep ? exp_neg(csb[tj] - csb[s]) * db[s] : 0.f;
-        }
-    }
-    __syncthreads();
-
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    floatx4 acc[NSB][4];
-    const E *crow[NSB];
-    const E *cbrow[NSB];
-    bool tval[NSB];
-    const E *cbase = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+
+    // ---- issue the global loads ----
+    const int vpr = N / V;   // 16-byte vectors per Hin row
+    const E *hsrc = hin + ((((int64_t)b * nc + c) * H + h) * P + p0) * (int64_t)N;
+    uint4 hraw[HMAX];
+#pragma unroll
+    for (int i = 0; i < HMAX; ++i) {
+        const int idx = threadIdx.x + i * kThreads;
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (idx < 64 * vpr) {
+            const int pr = idx / vpr, nv = idx % vpr;
+            if (p0 + pr < P) v = *reinterpret_cast<const uint4 *>(hsrc + (int64_t)pr * N + nv * V);
+        }
+        hraw[i] = v;
+    }
+    XT xs;
+    xs.load(x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len, P - p0);
+    float c_i = 0.f, d_i = 0.f;
+    int s_i = 0;
+    if (threadIdx.x < Q) {
+        c_i = cs[cso + threadIdx.x];
+        d_i = delta[cso + threadIdx.x];
+        if (PACKED) s_i = seq_idx[t0 + min((int)threadIdx.x, len - 1)];
+    }
+    const int seq_prev = PACKED ? seq_idx[c > 0 ? t0 - 1 : 0] : 0;
+
+    const auto crs = make_rsrc(Cm + (((int64_t)b * T + t0) * G + g) * N, ((int64_t)(len - 1) * G * N + N) * ES);
+    const auto cbrs = make_rsrc(cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q, (int64_t)Q * Q * ES);
+    const uint32_t crow_bytes = (uint32_t)(G * N * ES);
+    bool live[NSB];
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) live[k] = 16 * (wave + 4 * k) < len;   // wave-uniform
+    auto c_off = [&](int k, int ks) -> uint32_t {
+        const int kk = ks * 32 + 8 * lg;
+        const int t = 16 * (wave + 4 * k) + li;
+        return kk < N ? (uint32_t)t * crow_bytes + (uint32_t)(kk * ES) : kOffNone;
+    };
+    auto cb_off = [&](int k, int ks) -> uint32_t {
+        const int t = 16 * (wave + 4 * k) + li;
+        return (uint32_t)((t * Q + ks * 32 + 8 * lg) * ES);
+    };
+    const int nks = (N + 31) / 32;
+    F cA[NSB], cB[NSB];
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-        const int t = 16 * (wave + 4 * k) + li;
-        tval[k] = t < len;
-        crow[k] = Cm + (((int64_t)b * T + t0 + (tval[k] ? t : 0)) * G + g) * N;
-        cbrow[k] = cbase + (int64_t)t * Q;
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) acc[k][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        bload_frag(crs, c_off(k, 0), cA[k]);
+        if (nks > 1) bload_frag(crs, c_off(k, 1), cB[k]);
+        else cB[k] = F{};
     }
 
-    // step 4 part: Hin C^T over n
-    for (int k0 = 0; k0 < N; k0 += 32) {
-        const int kk = k0 + 8 * lg;
+    // ---- entering-state tile and per-token values into LDS ----
+#pragma unroll
+    for (int i = 0; i < HMAX; ++i) {
+        const int idx = threadIdx.x + i * kThreads;
+        if (idx < 64 * vpr) {
+            const int pr = idx / vpr, nv = idx % vpr;
+            *reinterpret_cast<uint4 *>(hs + pr * HP + nv * V) = hraw[i];
+        }
+    }
+    if (threadIdx.x < Q) {
+        csb[threadIdx.x] = c_i;
+        db[threadIdx.x] = d_i;
+        if (PACKED) sq[threadIdx.x] = s_i;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 2; j < NJ; ++j) {
+        const int tj = 16 * j;
+        for (int s = threadIdx.x; s < 32 * (j >> 1); s += kThreads)
+            vt[vt_offset(j) + s] = (!PACKED || sq[s] == sq[tj]) ? exp_neg(csb[tj] - csb[s]) * db[s] : 0.f;
+    }
+
+    floatx4 acc[NSB][4];
+#pragma unroll
+    for (int k = 0; k < NSB; ++k)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) acc[k][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- step 4 part: Hin C^T over n (fragments of C two K steps ahead) ----
+    auto step4 = [&](int ks, F (&cf)[NSB]) {
+        const int kk = ks * 32 + 8 * lg;
         const bool kin = kk < N;
         F a[4];
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) a[pb] = kin ? load_frag(hs + (pb * 16 + li) * HP + kk) : F{};
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
-            if (16 * (wave + 4 * k) >= len) continue;
-            const F bf = (tval[k] && kin) ? load_frag(crow[k] + kk) : F{};
+            if (!live[k]) continue;
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], bf);
+            for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], cf[k]);
         }
+        if (ks + 2 < nks) {
+#pragma unroll
+            for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + 2), cf[k]);
+        }
+    };
+    for (int ks = 0; ks < nks; ks += 2) {
+        step4(ks, cA);
+        if (ks + 1 < nks) step4(ks + 1, cB);
+    }
+
+    // CB fragments of the diagonal step of every sub-block and of the first two
+    // strictly-below steps
+    F dcb[NSB], bA[NSB], bB[NSB];
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) {
+        bload_frag(cbrs, cb_off(k, (wave + 4 * k) >> 1), dcb[k]);
+        if (KSB > 0) bload_frag(cbrs, cb_off(k, 0), bA[k]);
+        else bA[k] = F{};
+        if (KSB > 1) bload_frag(cbrs, cb_off(k, 1), bB[k]);
+        else bB[k] = F{};
     }
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
         const int tj = 16 * (wave + 4 * k);
-        const bool mo = !seq_idx || sq[tj] == seq_prev;
+        const bool mo = !PACKED || sq[tj] == seq_prev;
         const float e0 = exp_neg(csb[tj]);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb)
@@ -561,32 +807,45 @@ __global__ __launch_bounds__(kThreads) void k_chunk_scan(
             for (int q = 0; q < 4; ++q) acc[k][pb][q] = mo ? acc[k][pb][q] * e0 : 0.f;
     }
 
-    // step 1, K steps strictly below each sub-block's diagonal step
-    for (int ks = 0; ks < (NJ - 1) / 2; ++ks) {
+    __syncthreads();   // every wave is done with the entering-state tile
+    xs.template store<false, false>(xt, nullptr, nullptr);
+    __syncthreads();
+
+    // ---- step 1, the K steps strictly below each sub-block's diagonal step ----
+    auto step1 = [&](int ks, F (&bf)[NSB]) {
         F a[4];
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) a[pb] = load_frag(xt + (pb * 16 + li) * XP + ks * 32 + 8 * lg);
+        for (int pb = 0; pb < 4; ++pb) a[pb] = XT::frag(xt, ks * 32, pb * 16);
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
             const int j = wave + 4 * k;
-            if (ks >= (j >> 1) || 16 * j >= len) continue;
-            const floatx8 cf = to_f32(load_frag(cbrow[k] + ks * 32 + 8 * lg));
-            const float *vrow = vt + j * Q + ks * 32 + 8 * lg;
+            if (ks >= (j >> 1) || !live[k]) continue;
+            const float *vrow = vt + vt_offset(j) + ks * 32 + 8 * lg;
             const floatx4 v0 = *reinterpret_cast<const floatx4 *>(vrow);
             const floatx4 v1 = *reinterpret_cast<const floatx4 *>(vrow + 4);
             const floatx8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            const F wfr = from_f32<F>(cf * vv);
+            const F wfr = from_f32<F>(to_f32(bf[k]) * vv);
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], wfr);
         }
+        if (ks + 2 < KSB) {
+#pragma unroll
+            for (int k = 0; k < NSB; ++k) bload_frag(cbrs, cb_off(k, ks + 2), bf[k]);
+        }
+    };
+    for (int ks = 0; ks < KSB; ks += 2) {
+        step1(ks, bA);
+        if (ks + 1 < KSB) step1(ks + 1, bB);
     }
-    // u_t scale, then the diagonal K step with per-element decays
+
+    // ---- u_t scale, then the diagonal K step with per-element decays and D ----
+    const float Dh = D ? D[h] : 0.f;
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
         const int j = wave + 4 * k;
-        if (16 * j >= len) continue;
+        if (!live[k]) continue;
         const int tj = 16 * j, t = tj + li;
-        const bool keep = sq[t] == sq[tj];
+        const bool keep = !PACKED || sq[t] == sq[tj];
         const float ut = exp_neg(csb[t] - csb[tj]);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb)
@@ -594,26 +853,29 @@ __global__ __launch_bounds__(kThreads) void k_chunk_scan(
             for (int q = 0; q < 4; ++q) acc[k][pb][q] = keep ? acc[k][pb][q] * ut : 0.f;
 
         const int ks = j >> 1;
-        const floatx8 cf = to_f32(load_frag(cbrow[k] + ks * 32 + 8 * lg));
-        floatx8 wf;
+        const int sb = ks * 32 + 8 * lg;
+        const floatx8 cf = to_f32(dcb[k]);
+        const floatx4 cs0 = *reinterpret_cast<const floatx4 *>(csb + sb);
+        const floatx4 cs1 = *reinterpret_cast<const floatx4 *>(csb + sb + 4);
+        const floatx4 d0 = *reinterpret_cast<const floatx4 *>(db + sb);
+        const floatx4 d1 = *reinterpret_cast<const floatx4 *>(db + sb + 4);
+        const floatx8 csv = __builtin_shufflevector(cs0, cs1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const floatx8 dv = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
         const float cst = csb[t];
-        const int sqt = sq[t];
+        floatx8 wf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int s = ks * 32 + 8 * lg + e;
-            const bool ok = s <= t && sq[s] == sqt;
-            wf[e] = ok ? cf[e] * exp_neg(cst - csb[s]) * db[s] : 0.f;
+            const int s = sb + e;
+            bool ok = s <= t;
+            if (PACKED) ok = ok && sq[s] == sq[t];
+            wf[e] = (ok ? cf[e] * exp_neg(cst - csv[e]) * dv[e] : 0.f) + (s == t ? Dh : 0.f);
         }
         const F wfr = from_f32<F>(wf);
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const F a = load_frag(xt + (pb * 16 + li) * XP + ks * 32 + 8 * lg);
-            mma(acc[k][pb], a, wfr);
-        }
+        for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], XT::frag(xt, ks * 32, pb * 16), wfr);
     }
 
-    // epilogue: + D x, store y (4 consecutive p of one t per lane)
-    const float Dh = D ? D[h] : 0.f;
+    // ---- epilogue: store y (4 consecutive p of one t per lane) ----
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
         const int t = 16 * (wave + 4 * k) + li;
@@ -622,12 +884,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_scan(
         for (int pb = 0; pb < 4; ++pb) {
             const int p = p0 + pb * 16 + 4 * lg;
             if (p >= P) continue;
-            const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * P + p;
-            float xv[4], o[4];
-            load4_f32(x + off, xv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = acc[k][pb][q] + Dh * xv[q];
-            store4_f32(y + off, o);
+            float o[4] = {acc[k][pb][0], acc[k][pb][1], acc[k][pb][2], acc[k][pb][3]};
+            store4_f32(y + (((int64_t)b * T + t0 + t) * H + h) * P + p, o);
         }
     }
 }
