@@ -249,35 +249,25 @@ ssd_status run_seq_final(const Shape &s, const ssd_fwd_args *a, const float *del
     });
 }
 
-template <typename E, int Q, bool PACKED>
-ssd_status run_scan_qp(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
-                       const E *hin, hipStream_t st)
-{
-    const int ntp = (int)((s.P + 63) / 64);
-    static bool attr_set = false;   // raising the dynamic-LDS cap is idempotent
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)k_chunk_scan<E, Q, PACKED>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)scan_region_bytes<E, Q>(kMaxStateDim)) != hipSuccess)
-            return SSD_ERR_HIP;
-        attr_set = true;
-    }
-    dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
-    const size_t dyn = scan_region_bytes<E, Q>((int)s.N);
-    hipLaunchKernelGGL((k_chunk_scan<E, Q, PACKED>), grid, dim3(kThreads), dyn, st,
-                       (const E *)a->x, (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y,
-                       (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
-    return launched();
-}
-
 template <typename E>
 ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
                     const E *hin, hipStream_t st)
 {
+    const int ntp = (int)((s.P + 63) / 64);
+    dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
     return with_q(s.Q, [&](auto q) {
-        constexpr int Q = decltype(q)::value;
-        return s.packed ? run_scan_qp<E, Q, true>(s, a, delta, cs, cb, hin, st)
-                        : run_scan_qp<E, Q, false>(s, a, delta, cs, cb, hin, st);
+        return with_nt(s.N, [&](auto nt) {
+            constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+            if (s.packed)
+                hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->x,
+                                   (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
+                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
+            else
+                hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(kThreads), 0, st, (const E *)a->x,
+                                   (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
+                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
+            return launched();
+        });
     });
 }
 

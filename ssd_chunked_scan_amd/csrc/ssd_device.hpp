@@ -34,6 +34,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // e^x through the hardware base-2 exponential (v_exp_f32).  Used only for
 // arguments <= 0 (decays) where the result is in [0, 1].
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// 2^x for arguments already scaled by log2(e) (v_exp_f32 alone).
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename E> struct Frag;
 template <> struct Frag<bf16> { using type = bf16x8; };
@@ -138,6 +140,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// The same with a wave-uniform extra offset in the scalar offset field (only for
+// accesses known to be in range: the scalar part is not range-checked).
+__device__ __forceinline__ uint4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ uint2 bload8s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
+__device__ __forceinline__ void bstore8s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff, uint2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) unsigned int, v),
+                                          r, off, soff, 0);
+}
+__device__ __forceinline__ void bstore16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff, uint4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(__attribute__((__vector_size__(16))) unsigned int, v), r, off, soff, 0);
 }
 // Fragment (16 or 32 bytes) from a buffer at a byte offset.
 __device__ __forceinline__ void bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 &f)

@@ -140,8 +140,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(
         brow[i] = Bm + (((int64_t)b * T + t0 + (bv[i] ? s : 0)) * G + g) * N;
         crow[i] = Cm + (((int64_t)b * T + t0 + (cv[i] ? t : 0)) * G + g) * N;
     }
+    // all K steps' fragments in flight at once (bf16: N <= 256 is at most 8 steps);
+    // fp32 fragments are twice as large, so fp32 keeps a ring of 2
+    constexpr int RD = sizeof(E) == 2 ? 8 : 2;
     const int nks = (N + 31) / 32;
-    F a0[2] = {F{}, F{}}, b0[2] = {F{}, F{}}, a1[2] = {F{}, F{}}, b1[2] = {F{}, F{}};
+    F fa[RD][2], fb[RD][2];
     auto fetch = [&](F (&a)[2], F (&bb)[2], int ks) {
         const int k = ks * 32 + 8 * lg;
         const bool kin = k < N;
@@ -151,21 +154,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(
             bb[i] = (cv[i] && kin) ? load_frag(crow[i] + k) : F{};
         }
     };
-    fetch(a0, b0, 0);
-    if (nks > 1) fetch(a1, b1, 1);
+#pragma unroll
+    for (int r = 0; r < RD; ++r) {
+        if (r < nks) fetch(fa[r], fb[r], r);
+    }
     floatx4 acc[2][2] = {};
-    for (int ks = 0; ks < nks; ++ks) {
-        F a[2] = {a0[0], a0[1]}, bb[2] = {b0[0], b0[1]};
+    for (int k0 = 0; k0 < nks; k0 += RD) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            a0[i] = a1[i];
-            b0[i] = b1[i];
+        for (int r = 0; r < RD; ++r) {
+            const int ks = k0 + r;
+            if (ks < nks) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) mma(acc[i][j], fa[r][i], fb[r][j]);
+                if (ks + RD < nks) fetch(fa[r], fb[r], ks + RD);
+            }
         }
-        if (ks + 2 < nks) fetch(a1, b1, ks + 2);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc[i][j], a[i], bb[j]);
     }
     E *out = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
 #pragma unroll
@@ -183,43 +188,70 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(
 // K tiles: LDS tiles whose MFMA K index (time) is the slow axis in memory
 // ---------------------------------------------------------------------------
 // KTile<E, KR, COLS> holds rows 0..KR-1 (time) and columns 0..COLS-1 of a
-// row-major global array (row stride `ld` elements).  load() issues the
-// global loads into registers, store() writes LDS (optionally scaling row r by
-// w[r], and with SEL zeroing rows whose m[r] == 0 by a select, so a masked
-// non-finite input cannot leak), and frag(tile, k0, col0) returns the MFMA
-// fragment for K rows k0..k0+31 and columns col0..col0+15.
+// row-major global array.  init() fixes each thread's byte offsets (row r,
+// 16-byte column vector c) once; load(rsrc) issues the buffer loads into
+// registers, where rsrc (see rsrc()) starts at the tile's first element and ends
+// after its last valid row, so rows past it read as zero with no per-load
+// arithmetic; columns >= ncols are masked in init().  store() writes LDS
+// (optionally scaling row r by w[r], and with SEL zeroing rows whose m[r] == 0
+// by a select, so a masked non-finite input cannot leak), and
+// frag(tile, k0, col0) returns the MFMA fragment for K rows k0..k0+31 and
+// columns col0..col0+15.
 //
 // bf16: the tile stays row-major in LDS (plain 16-byte copies) and fragments are
 // read with ds_read_b64_tr_b16.  Within each 16-lane group, lane j points at
 // row k0 + 8*(lane/16) + j/4, column col0 + 4*(j%4); the instruction hands lane
 // j column col0 + j of those four rows, i.e. four consecutive K values of one
-// column.  Two reads (rows +0..3 and +4..7) make the 8-wide fragment.  Rows are
-// padded by 32 bytes so a group's four rows fall on disjoint banks.
+// column.  Two reads (rows +0..3 and +4..7) make the 8-wide fragment.  To keep
+// both these reads (32 lanes x 8 bytes per LDS cycle) and the 16-byte row writes
+// free of bank conflicts on 64 banks, the 8-byte column chunks of row r are
+// stored XOR-swizzled by swz(r) (an even value, so a 16-byte vector stays
+// contiguous): for 64-column tiles swz = 6*((r>>1)&7) mod 16 with no row padding,
+// for wider tiles rows are padded by 32 bytes and swz = 16*((r>>3)&1).
 // fp32: there is no 32-bit transpose read, so the tile is transposed in registers
 // on its way into LDS ([col][row], rows padded by 16 bytes) and fragments are
 // plain 32-byte reads.
 template <typename E, int KR, int COLS> struct KTile;
 
+template <typename E, int COLS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ktile_rsrc(const E *src, int64_t ld, int rows)
+{
+    return make_rsrc(src, rows > 0 ? ((int64_t)(rows - 1) * ld + COLS) * (int64_t)sizeof(E) : 0);
+}
+
 template <int KR, int COLS>
 struct KTile<bf16, KR, COLS> {
-    static constexpr int PITCH = COLS + 16;
+    static constexpr int PITCH = COLS == 64 ? 64 : COLS + 16;
+    static __device__ __forceinline__ int swz(int r)
+    {
+        return COLS == 64 ? ((6 * ((r >> 1) & 7)) & 14) : (((r >> 3) & 1) << 4);
+    }
     static constexpr int SIZE = KR * PITCH;
     static constexpr int VPR = COLS / 8;   // 16-byte vectors per row
     static constexpr int NV = KR * VPR;
     static constexpr int PER = (NV + kThreads - 1) / kThreads;
     uint4 raw[PER];
+    uint32_t voff[PER];
 
-    __device__ __forceinline__ void load(const bf16 *src, int64_t ld, int slen, int ncols)
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const bf16 *src, int64_t ld, int rows)
+    {
+        return ktile_rsrc<bf16, COLS>(src, ld, rows);
+    }
+
+    __device__ __forceinline__ void init(int64_t ld, int ncols)
     {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int v = threadIdx.x + i * kThreads;
             const int r = v / VPR, c = v % VPR;
-            uint4 x = {0u, 0u, 0u, 0u};
-            if (v < NV && r < slen && c * 8 < ncols)
-                x = *reinterpret_cast<const uint4 *>(src + (int64_t)r * ld + c * 8);
-            raw[i] = x;
+            voff[i] = (v < NV && c * 8 < ncols) ? (uint32_t)(r * ld * 2 + c * 16) : kOffNone;
         }
+    }
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) raw[i] = bload16(rs, voff[i]);
     }
 
     template <bool SCALE, bool SEL>
@@ -243,18 +275,34 @@ struct KTile<bf16, KR, COLS> {
                 }
                 o = uint4{q[0], q[1], q[2], q[3]};
             }
-            *reinterpret_cast<uint4 *>(dst + r * PITCH + c * 8) = o;
+            *reinterpret_cast<uint4 *>(dst + r * PITCH + 4 * ((2 * c) ^ swz(r))) = o;
         }
     }
 
-    __device__ __forceinline__ static bf16x8 frag(const bf16 *tile, int k0, int col0)
+    // Per-lane element offsets of the fragment for columns col0..col0+15 at K row 0.
+    // The swizzle has a period of 16 rows, so the fragment at K row k0 (a multiple
+    // of 32) is at the same offsets plus k0 * PITCH: hoisting these out of the K
+    // loops leaves one LDS immediate offset per read.
+    struct Off {
+        int lo, hi;
+    };
+    __device__ __forceinline__ static Off frag_off(int col0)
+    {
+        const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+        const int r0 = 8 * g + (j >> 2), r1 = r0 + 4, c8 = (col0 >> 2) + (j & 3);
+        return Off{r0 * PITCH + 4 * (c8 ^ swz(r0)), r1 * PITCH + 4 * (c8 ^ swz(r1))};
+    }
+    __device__ __forceinline__ static bf16x8 frag_at(const bf16 *tile, Off o, int k0)
     {
         typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-        const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-        bf16 *p = const_cast<bf16 *>(tile) + (k0 + 8 * g + (j >> 2)) * PITCH + col0 + 4 * (j & 3);
-        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p);
-        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 4 * PITCH));
+        bf16 *t = const_cast<bf16 *>(tile) + k0 * PITCH;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(t + o.lo));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(t + o.hi));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    __device__ __forceinline__ static bf16x8 frag(const bf16 *tile, int k0, int col0)
+    {
+        return frag_at(tile, frag_off(col0), k0);
     }
 };
 
@@ -266,22 +314,32 @@ struct KTile<float, KR, COLS> {
     static constexpr int NB = (KR / 4) * CBK;   // 4x4 blocks
     static constexpr int PER = (NB + kThreads - 1) / kThreads;
     uint4 raw[PER][4];
+    uint32_t voff[PER];   // offset of the block's first row
 
-    __device__ __forceinline__ void load(const float *src, int64_t ld, int slen, int ncols)
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float *src, int64_t ld, int rows)
     {
+        return ktile_rsrc<float, COLS>(src, ld, rows);
+    }
+
+    int64_t ldb;
+    __device__ __forceinline__ void init(int64_t ld, int ncols)
+    {
+        ldb = ld * 4;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int blk = threadIdx.x + i * kThreads;
             const int cbk = blk % CBK, sb = blk / CBK;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = sb * 4 + r;
-                uint4 v = {0u, 0u, 0u, 0u};
-                if (blk < NB && s < slen && cbk * 4 < ncols)
-                    v = *reinterpret_cast<const uint4 *>(src + (int64_t)s * ld + cbk * 4);
-                raw[i][r] = v;
-            }
+            voff[i] = (blk < NB && cbk * 4 < ncols) ? (uint32_t)(sb * 4 * ldb + cbk * 16) : kOffNone;
         }
+    }
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                raw[i][r] = bload16(rs, voff[i] == kOffNone ? kOffNone : voff[i] + (uint32_t)(r * ldb));
     }
 
     template <bool SCALE, bool SEL>
@@ -313,10 +371,21 @@ struct KTile<float, KR, COLS> {
         }
     }
 
-    __device__ __forceinline__ static floatx8 frag(const float *tile, int k0, int col0)
+    struct Off {
+        int lo, hi;
+    };
+    __device__ __forceinline__ static Off frag_off(int col0)
     {
         const int lane = threadIdx.x & 63;
-        return load_frag(tile + (col0 + (lane & 15)) * PITCH + k0 + 8 * (lane >> 4));
+        return Off{(col0 + (lane & 15)) * PITCH + 8 * (lane >> 4), 0};
+    }
+    __device__ __forceinline__ static floatx8 frag_at(const float *tile, Off o, int k0)
+    {
+        return load_frag(tile + o.lo + k0);
+    }
+    __device__ __forceinline__ static floatx8 frag(const float *tile, int k0, int col0)
+    {
+        return frag_at(tile, frag_off(col0), k0);
     }
 };
 
@@ -338,31 +407,40 @@ struct StateSmem {
     E b[BT::SIZE];
 };
 
+// The caller has run xs.init/bs.init and issued the loads of the first K chunk.
 template <typename E, int NT, bool SEL>
 __device__ __forceinline__ void state_product(StateSmem<E, NT> &sm, const E *xsrc, int64_t ldx, const E *bsrc,
-                                              int64_t ldb, int slen, int pcols, int ncols, const float *w,
-                                              const int *m, typename StateSmem<E, NT>::XT &xs,
+                                              int64_t ldb, int slen, const float *w, const int *m,
+                                              typename StateSmem<E, NT>::XT &xs,
                                               typename StateSmem<E, NT>::BT &bs, floatx4 (&acc)[NT / 64][4])
 {
     using XT = typename StateSmem<E, NT>::XT;
     using BT = typename StateSmem<E, NT>::BT;
     constexpr int NI = NT / 64;
     const int wave = threadIdx.x >> 6;
+    typename BT::Off aoff[NI];
+    typename XT::Off xoff[4];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) aoff[i] = BT::frag_off(wave * (NT / 4) + i * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xoff[j] = XT::frag_off(j * 16);
     for (int kb = 0; kb < slen; kb += 64) {
         xs.template store<true, SEL>(sm.x, w + kb, m + kb);
         bs.template store<false, false>(sm.b, nullptr, nullptr);
         __syncthreads();
         if (kb + 64 < slen) {
-            xs.load(xsrc + (int64_t)(kb + 64) * ldx, ldx, slen - kb - 64, pcols);
-            bs.load(bsrc + (int64_t)(kb + 64) * ldb, ldb, slen - kb - 64, ncols);
+            xs.load(XT::rsrc(xsrc + (int64_t)(kb + 64) * ldx, ldx, slen - kb - 64));
+            bs.load(BT::rsrc(bsrc + (int64_t)(kb + 64) * ldb, ldb, slen - kb - 64));
         }
         const int kend = min(64, ((slen - kb) + 31) & ~31);
-        for (int ks = 0; ks < kend; ks += 32) {
+#pragma unroll
+        for (int ks = 0; ks < 64; ks += 32) {
+            if (ks >= kend) break;
             frag_t<E> a[NI], bb[4];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) a[i] = BT::frag(sm.b, ks, wave * (NT / 4) + i * 16);
+            for (int i = 0; i < NI; ++i) a[i] = BT::frag_at(sm.b, aoff[i], ks);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bb[j] = XT::frag(sm.x, ks, j * 16);
+            for (int j = 0; j < 4; ++j) bb[j] = XT::frag_at(sm.x, xoff[j], ks);
 #pragma unroll
             for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -397,10 +475,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
     const E *xsrc = x + (((int64_t)b * T + t0) * H + h) * P + p0;
     const E *bsrc = Bm + (((int64_t)b * T + t0) * G + g) * N;
     const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
-    typename StateSmem<E, NT>::XT xs;
-    typename StateSmem<E, NT>::BT bs;
-    xs.load(xsrc, ldx, len, P - p0);
-    bs.load(bsrc, ldb, len, N);
+    using XT = typename StateSmem<E, NT>::XT;
+    using BT = typename StateSmem<E, NT>::BT;
+    XT xs;
+    BT bs;
+    xs.init(ldx, P - p0);
+    bs.init(ldb, N);
+    xs.load(XT::rsrc(xsrc, ldx, len));
+    bs.load(BT::rsrc(bsrc, ldb, len));
 
     const int64_t cso = (((int64_t)b * H + h) * nc + c) * Q;
     const float lam = cs[cso + len - 1];
@@ -416,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
     for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    state_product<E, NT, PACKED>(sm, xsrc, ldx, bsrc, ldb, len, P - p0, N, w, m, xs, bs, acc);
+    state_product<E, NT, PACKED>(sm, xsrc, ldx, bsrc, ldb, len, w, m, xs, bs, acc);
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     E *out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
@@ -464,57 +546,51 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
     int T, int H, int64_t PN, int nc, int Q, int64_t total_vecs)
 {
     using R = typename Raw4<E>::type;
-    constexpr int D = kPrefetch;
+    constexpr int D = kPrefetch;   // divides 64
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= total_vecs) return;
-    const int64_t vph = PN / 4;
-    const int64_t e0 = (gid % vph) * 4;
-    const int64_t bh = gid / vph;
-    const int h = (int)(bh % H);
-    const int64_t b = bh / H;
+    const int lane = threadIdx.x & 63;
+    const int64_t vph = PN / 4;   // a multiple of 64: every wave lies inside one (b, h)
+    const int bh = __builtin_amdgcn_readfirstlane((int)(gid / vph));
+    const int64_t e0 = (gid - (int64_t)bh * vph) * 4;
+    const int h = bh % H;
+    const int b = bh / H;
     float hs[4] = {0.f, 0.f, 0.f, 0.f};
-    if (init) load4_f32(init + bh * PN + e0, hs);
-    const float *lamp = cs + bh * (int64_t)nc * Q + (Q - 1);
+    if (init) load4_f32(init + (int64_t)bh * PN + e0, hs);
+    const float *lamp = cs + (int64_t)bh * nc * Q + (Q - 1);   // cs at each chunk's last position
     const int64_t cstride = (int64_t)H * PN;
-    E *base = states + (b * nc * H + h) * PN + e0;
+    E *lane_base = states + ((int64_t)b * nc * H + h) * PN + e0;
     R buf[D];
-    float lam[D];
-    int sl[D];
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-        sl[k] = 0;
-        lam[k] = 0.f;
-        if (k < nc) {
-            buf[k] = *reinterpret_cast<const R *>(base + (int64_t)k * cstride);
-            lam[k] = lamp[(int64_t)k * Q];
-            if (seq_idx) sl[k] = seq_idx[min(k * Q + Q, T) - 1];
-        }
-    }
+    for (int k = 0; k < D; ++k)
+        if (k < nc) buf[k] = *reinterpret_cast<const R *>(lane_base + (int64_t)k * cstride);
     int sprev = seq_idx ? seq_idx[0] : 0;
-    for (int c0 = 0; c0 < nc; c0 += D) {
+    for (int cb = 0; cb < nc; cb += 64) {
+        // the per-chunk scalars of 64 chunks: lane i holds chunk cb + i
+        const int cl = cb + lane;
+        const float lamv = cl < nc ? lamp[(int64_t)cl * Q] : 0.f;
+        const int slv = (seq_idx && cl < nc) ? seq_idx[min(cl * Q + Q, T) - 1] : 0;
+        for (int k0 = 0; k0 < 64 && cb + k0 < nc; k0 += D) {
 #pragma unroll
-        for (int k = 0; k < D; ++k) {
-            const int c = c0 + k;
-            if (c < nc) {
-                float sv[4];
-                unpack4(buf[k], sv);
-                const float lm = lam[k];
-                const int sc = sl[k];
-                if (c + D < nc) {
-                    buf[k] = *reinterpret_cast<const R *>(base + (int64_t)(c + D) * cstride);
-                    lam[k] = lamp[(int64_t)(c + D) * Q];
-                    if (seq_idx) sl[k] = seq_idx[min((c + D) * Q + Q, T) - 1];
+            for (int j = 0; j < D; ++j) {
+                const int c = cb + k0 + j;
+                if (c < nc) {
+                    float sv[4];
+                    unpack4(buf[j], sv);
+                    if (c + D < nc) buf[j] = *reinterpret_cast<const R *>(lane_base + (int64_t)(c + D) * cstride);
+                    store4_f32(lane_base + (int64_t)c * cstride, hs);
+                    const float lm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lamv), k0 + j));
+                    const int sc = __builtin_amdgcn_readlane(slv, k0 + j);
+                    const bool keep = !seq_idx || sc == sprev;
+                    sprev = sc;
+                    const float d = exp_neg(lm);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
                 }
-                store4_f32(base + (int64_t)c * cstride, hs);
-                const bool keep = !seq_idx || sc == sprev;
-                sprev = sc;
-                const float d = exp_neg(lm);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
             }
         }
     }
-    if (final_states) store4_f32(final_states + bh * PN + e0, hs);
+    if (final_states) store4_f32(final_states + (int64_t)bh * PN + e0, hs);
 }
 
 // ---------------------------------------------------------------------------
@@ -575,10 +651,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
     const E *xsrc = x + ((int64_t)t0 * H + h) * P + p0;
     const E *bsrc = Bm + ((int64_t)t0 * G + g) * N;
     const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
-    typename StateSmem<E, NT>::XT xs;
-    typename StateSmem<E, NT>::BT bs;
-    xs.load(xsrc, ldx, ie + 1, P - p0);
-    bs.load(bsrc, ldb, ie + 1, N);
+    using XT = typename StateSmem<E, NT>::XT;
+    using BT = typename StateSmem<E, NT>::BT;
+    XT xs;
+    BT bs;
+    xs.init(ldx, P - p0);
+    bs.init(ldb, N);
+    xs.load(XT::rsrc(xsrc, ldx, ie + 1));
+    bs.load(BT::rsrc(bsrc, ldb, ie + 1));
     const int64_t cso = ((int64_t)h * nc + c) * Q;
     const float cse = cs[cso + ie];
     for (int s = threadIdx.x; s < Q; s += kThreads) {
@@ -592,7 +672,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
     for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    state_product<E, NT, true>(sm, xsrc, ldx, bsrc, ldb, ie + 1, P - p0, N, w, m, xs, bs, acc);
+    state_product<E, NT, true>(sm, xsrc, ldx, bsrc, ldb, ie + 1, w, m, xs, bs, acc);
 
     const bool carry = seq_idx[c > 0 ? t0 - 1 : 0] == sg;
     const float dcar = exp_neg(cse);
@@ -641,15 +721,17 @@ __host__ __device__ constexpr int vt_offset(int j)
 }
 
 // LDS bytes of the region shared by the entering-state tile and the x tile.
-template <typename E, int Q>
-__host__ __device__ constexpr size_t scan_region_bytes(int N)
+template <typename E, int Q, int NT>
+__host__ __device__ constexpr int scan_region_bytes()
 {
-    const size_t hs = (size_t)64 * (N + kVec16<E>) * sizeof(E);
-    const size_t xt = (size_t)KTile<E, Q, 64>::SIZE * sizeof(E);
+    constexpr int hs = 64 * (NT + kVec16<E>) * (int)sizeof(E);
+    constexpr int xt = KTile<E, Q, 64>::SIZE * (int)sizeof(E);
     return hs > xt ? hs : xt;
 }
 
-template <typename E, int Q, bool PACKED>
+// NT = N rounded up to 64 (compile time, so every K loop unrolls and every LDS
+// fragment offset is an immediate); columns N..NT-1 are masked.
+template <typename E, int Q, int NT, bool PACKED>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     const E *__restrict__ x, const E *__restrict__ Cm, const float *__restrict__ delta,
     const float *__restrict__ cs, const E *__restrict__ cb, const E *__restrict__ hin,
@@ -660,18 +742,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     using XT = KTile<E, Q, 64>;
     constexpr int V = kVec16<E>;
     constexpr int ES = (int)sizeof(E);
-    constexpr int NJ = Q / 16;     // 16-row sub-blocks per chunk
-    constexpr int NSB = Q / 64;    // sub-blocks per wave
+    constexpr int NJ = Q / 16;          // 16-row sub-blocks per chunk
+    constexpr int NSB = Q / 64;         // sub-blocks per wave
     constexpr int KSB = (NJ - 1) / 2;   // K steps strictly below some sub-block's diagonal
-    constexpr int HMAX = 64 * kMaxStateDim / V / kThreads;   // Hin vectors per thread
+    constexpr int NKS = NT / 32;        // K steps of the step-4 product
+    constexpr int HP = NT + V;          // pitch of the entering-state tile
+    constexpr int RING = 3;             // C / CB fragments fetched RING K steps ahead
+    __shared__ __align__(16) char region[scan_region_bytes<E, Q, NT>()];
     __shared__ __align__(16) float vt[vt_offset(NJ)];
-    __shared__ __align__(16) float csb[Q];
+    __shared__ __align__(16) float csb[Q];   // cs * log2(e)
     __shared__ __align__(16) float db[Q];
     __shared__ __align__(16) int sq[PACKED ? Q : 4];
-    extern __shared__ __align__(16) char dyn_smem[];
-    E *hs = reinterpret_cast<E *>(dyn_smem);   // entering-state tile [64 p][N], pitch N + V
-    E *xt = reinterpret_cast<E *>(dyn_smem);   // later: the x tile
-    const int HP = N + V;
+    E *hs = reinterpret_cast<E *>(region);   // entering-state tile [64 p][NT], then ...
+    E *xt = reinterpret_cast<E *>(region);   // ... the x tile
 
     const int units = nc * H * ntp;
     const int u = xcd_remap(blockIdx.x, units);
@@ -686,62 +769,61 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
 
     // ---- issue the global loads ----
-    const int vpr = N / V;   // 16-byte vectors per Hin row
-    const E *hsrc = hin + ((((int64_t)b * nc + c) * H + h) * P + p0) * (int64_t)N;
-    uint4 hraw[HMAX];
+    // entering-state tile: VL lanes per row (one 16-byte vector each), RPP rows per pass
+    constexpr int VL = NT / V, RPP = kThreads / VL, HPASS = 64 / RPP;
+    const int vpr = N / V;
+    const int hv = threadIdx.x % VL, hr = threadIdx.x / VL;
+    const auto hrs = make_rsrc(hin + ((((int64_t)b * nc + c) * H + h) * P + p0) * (int64_t)N,
+                               (int64_t)min(64, P - p0) * N * ES);
+    const uint32_t hvoff = hv < vpr ? (uint32_t)(hr * N * ES + hv * 16) : kOffNone;
+    uint4 hraw[HPASS];
 #pragma unroll
-    for (int i = 0; i < HMAX; ++i) {
-        const int idx = threadIdx.x + i * kThreads;
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (idx < 64 * vpr) {
-            const int pr = idx / vpr, nv = idx % vpr;
-            if (p0 + pr < P) v = *reinterpret_cast<const uint4 *>(hsrc + (int64_t)pr * N + nv * V);
-        }
-        hraw[i] = v;
-    }
+    for (int i = 0; i < HPASS; ++i)
+        hraw[i] = bload16(hrs, hvoff == kOffNone ? kOffNone : hvoff + (uint32_t)(i * RPP * N * ES));
     XT xs;
-    xs.load(x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len, P - p0);
+    xs.init((int64_t)H * P, P - p0);
+    xs.load(XT::rsrc(x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len));
     float c_i = 0.f, d_i = 0.f;
     int s_i = 0;
     if (threadIdx.x < Q) {
-        c_i = cs[cso + threadIdx.x];
+        c_i = cs[cso + threadIdx.x] * kLog2e;   // decays below are exp2 of differences
         d_i = delta[cso + threadIdx.x];
         if (PACKED) s_i = seq_idx[t0 + min((int)threadIdx.x, len - 1)];
     }
     const int seq_prev = PACKED ? seq_idx[c > 0 ? t0 - 1 : 0] : 0;
 
+    // C rows (t, group g) of this chunk and the chunk's CB tile; C rows past the
+    // sequence end fall outside the resource and read as zero
     const auto crs = make_rsrc(Cm + (((int64_t)b * T + t0) * G + g) * N, ((int64_t)(len - 1) * G * N + N) * ES);
     const auto cbrs = make_rsrc(cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q, (int64_t)Q * Q * ES);
-    const uint32_t crow_bytes = (uint32_t)(G * N * ES);
     bool live[NSB];
-#pragma unroll
-    for (int k = 0; k < NSB; ++k) live[k] = 16 * (wave + 4 * k) < len;   // wave-uniform
-    auto c_off = [&](int k, int ks) -> uint32_t {
-        const int kk = ks * 32 + 8 * lg;
-        const int t = 16 * (wave + 4 * k) + li;
-        return kk < N ? (uint32_t)t * crow_bytes + (uint32_t)(kk * ES) : kOffNone;
-    };
-    auto cb_off = [&](int k, int ks) -> uint32_t {
-        const int t = 16 * (wave + 4 * k) + li;
-        return (uint32_t)((t * Q + ks * 32 + 8 * lg) * ES);
-    };
-    const int nks = (N + 31) / 32;
-    F cA[NSB], cB[NSB];
+    uint32_t cbase[NSB], cbbase[NSB];
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-        bload_frag(crs, c_off(k, 0), cA[k]);
-        if (nks > 1) bload_frag(crs, c_off(k, 1), cB[k]);
-        else cB[k] = F{};
+        const int t = 16 * (wave + 4 * k) + li;
+        live[k] = 16 * (wave + 4 * k) < len;   // wave-uniform
+        cbase[k] = (uint32_t)(t * G * N * ES + 8 * lg * ES);
+        cbbase[k] = (uint32_t)((t * Q + 8 * lg) * ES);
     }
+    auto c_off = [&](int k, int ks) -> uint32_t {   // ks is a compile-time constant at every call
+        return (ks * 32 + 8 * lg < N) ? cbase[k] + (uint32_t)(ks * 32 * ES) : kOffNone;
+    };
+    auto cb_off = [&](int k, int ks) -> uint32_t { return cbbase[k] + (uint32_t)(ks * 32 * ES); };
+
+    F cr[RING][NSB];
+#pragma unroll
+    for (int r = 0; r < RING; ++r)
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+            if (r < NKS) bload_frag(crs, c_off(k, r), cr[r][k]);
+            else cr[r][k] = F{};
+        }
 
     // ---- entering-state tile and per-token values into LDS ----
+    if (hv < vpr) {
 #pragma unroll
-    for (int i = 0; i < HMAX; ++i) {
-        const int idx = threadIdx.x + i * kThreads;
-        if (idx < 64 * vpr) {
-            const int pr = idx / vpr, nv = idx % vpr;
-            *reinterpret_cast<uint4 *>(hs + pr * HP + nv * V) = hraw[i];
-        }
+        for (int i = 0; i < HPASS; ++i)
+            *reinterpret_cast<uint4 *>(hs + (hr + i * RPP) * HP + hv * V) = hraw[i];
     }
     if (threadIdx.x < Q) {
         csb[threadIdx.x] = c_i;
@@ -749,11 +831,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
         if (PACKED) sq[threadIdx.x] = s_i;
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 2; j < NJ; ++j) {
-        const int tj = 16 * j;
-        for (int s = threadIdx.x; s < 32 * (j >> 1); s += kThreads)
-            vt[vt_offset(j) + s] = (!PACKED || sq[s] == sq[tj]) ? exp_neg(csb[tj] - csb[s]) * db[s] : 0.f;
+    // V_j[s] for s < 32 floor(j/2): thread s fills its column for every row j that has it
+    if (threadIdx.x < 32 * KSB) {
+        const int s = threadIdx.x;
+        const float css = csb[s], dss = db[s];
+        const int sqs = PACKED ? sq[s] : 0;
+        for (int j = 2 * (s / 32 + 1); j < NJ; ++j) {
+            const int tj = 16 * j;
+            vt[vt_offset(j) + s] = (!PACKED || sqs == sq[tj]) ? exp2_(csb[tj] - css) * dss : 0.f;
+        }
     }
 
     floatx4 acc[NSB][4];
@@ -762,8 +848,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[k][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- step 4 part: Hin C^T over n (fragments of C two K steps ahead) ----
-    auto step4 = [&](int ks, F (&cf)[NSB]) {
+    // ---- step 4 part: Hin C^T over n ----
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
         const int kk = ks * 32 + 8 * lg;
         const bool kin = kk < N;
         F a[4];
@@ -773,34 +860,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
         for (int k = 0; k < NSB; ++k) {
             if (!live[k]) continue;
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], cf[k]);
+            for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], cr[ks % RING][k]);
         }
-        if (ks + 2 < nks) {
+        if (ks + RING < NKS) {
 #pragma unroll
-            for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + 2), cf[k]);
+            for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + RING), cr[ks % RING][k]);
         }
-    };
-    for (int ks = 0; ks < nks; ks += 2) {
-        step4(ks, cA);
-        if (ks + 1 < nks) step4(ks + 1, cB);
     }
 
-    // CB fragments of the diagonal step of every sub-block and of the first two
-    // strictly-below steps
-    F dcb[NSB], bA[NSB], bB[NSB];
+    // CB fragments: the diagonal step of every sub-block, and the first RING
+    // strictly-below steps (every row of cb is in bounds)
+    F dcb[NSB];
 #pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-        bload_frag(cbrs, cb_off(k, (wave + 4 * k) >> 1), dcb[k]);
-        if (KSB > 0) bload_frag(cbrs, cb_off(k, 0), bA[k]);
-        else bA[k] = F{};
-        if (KSB > 1) bload_frag(cbrs, cb_off(k, 1), bB[k]);
-        else bB[k] = F{};
-    }
+    for (int k = 0; k < NSB; ++k) bload_frag(cbrs, cb_off(k, (wave + 4 * k) >> 1), dcb[k]);
+#pragma unroll
+    for (int r = 0; r < RING; ++r)
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+            if (r < KSB) bload_frag(cbrs, cb_off(k, r), cr[r][k]);
+            else cr[r][k] = F{};
+        }
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
         const int tj = 16 * (wave + 4 * k);
         const bool mo = !PACKED || sq[tj] == seq_prev;
-        const float e0 = exp_neg(csb[tj]);
+        const float e0 = exp2_(csb[tj]);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
@@ -811,11 +895,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     xs.template store<false, false>(xt, nullptr, nullptr);
     __syncthreads();
 
+    typename XT::Off xoff[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) xoff[pb] = XT::frag_off(pb * 16);
+
     // ---- step 1, the K steps strictly below each sub-block's diagonal step ----
-    auto step1 = [&](int ks, F (&bf)[NSB]) {
+#pragma unroll
+    for (int ks = 0; ks < KSB; ++ks) {
         F a[4];
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) a[pb] = XT::frag(xt, ks * 32, pb * 16);
+        for (int pb = 0; pb < 4; ++pb) a[pb] = XT::frag_at(xt, xoff[pb], ks * 32);
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
             const int j = wave + 4 * k;
@@ -824,18 +913,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
             const floatx4 v0 = *reinterpret_cast<const floatx4 *>(vrow);
             const floatx4 v1 = *reinterpret_cast<const floatx4 *>(vrow + 4);
             const floatx8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            const F wfr = from_f32<F>(to_f32(bf[k]) * vv);
+            const F wfr = from_f32<F>(to_f32(cr[ks % RING][k]) * vv);
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], wfr);
         }
-        if (ks + 2 < KSB) {
+        if (ks + RING < KSB) {
 #pragma unroll
-            for (int k = 0; k < NSB; ++k) bload_frag(cbrs, cb_off(k, ks + 2), bf[k]);
+            for (int k = 0; k < NSB; ++k) bload_frag(cbrs, cb_off(k, ks + RING), cr[ks % RING][k]);
         }
-    };
-    for (int ks = 0; ks < KSB; ks += 2) {
-        step1(ks, bA);
-        if (ks + 1 < KSB) step1(ks + 1, bB);
     }
 
     // ---- u_t scale, then the diagonal K step with per-element decays and D ----
@@ -846,7 +931,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
         if (!live[k]) continue;
         const int tj = 16 * j, t = tj + li;
         const bool keep = !PACKED || sq[t] == sq[tj];
-        const float ut = exp_neg(csb[t] - csb[tj]);
+        const float ut = exp2_(csb[t] - csb[tj]);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
@@ -862,17 +947,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
         const floatx8 csv = __builtin_shufflevector(cs0, cs1, 0, 1, 2, 3, 4, 5, 6, 7);
         const floatx8 dv = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
         const float cst = csb[t];
+        const int rel = t - sb;   // position of t in this lane's 8 K slots (valid if 0..7)
         floatx8 wf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int s = sb + e;
-            bool ok = s <= t;
-            if (PACKED) ok = ok && sq[s] == sq[t];
-            wf[e] = (ok ? cf[e] * exp_neg(cst - csv[e]) * dv[e] : 0.f) + (s == t ? Dh : 0.f);
+            bool ok = e <= rel;
+            if (PACKED) ok = ok && sq[sb + e] == sq[t];
+            wf[e] = (ok ? cf[e] * exp2_(cst - csv[e]) * dv[e] : 0.f) + (e == rel ? Dh : 0.f);
         }
         const F wfr = from_f32<F>(wf);
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], XT::frag(xt, ks * 32, pb * 16), wfr);
+        for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], XT::frag_at(xt, xoff[pb], ks * 32), wfr);
     }
 
     // ---- epilogue: store y (4 consecutive p of one t per lane) ----
