@@ -28,6 +28,38 @@ sys.path.insert(0, ROOT)
 METRIC = "SSD fwd tokens/sec on 1 MI355X + % of bf16 MFMA / HBM roofline per kernel"
 PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
 DEFAULT_WORKLOAD = 3   # 16K tokens, N = 256: the configuration the roofline targets are quoted on
+CSRC = os.path.join(ROOT, "ssd_chunked_scan_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources (sorted by name): identifies the kernels a
+    counter record was taken from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    FETCH_SIZE / WRITE_SIZE counter records (already scaled by the plain-copy
+    calibration), or None when no record exists or the kernels changed since."""
+    import glob
+    src = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*hbm_traffic*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic-record: "):
+                    continue
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec["kernel"] == kernel and rec["workload"] == workload and rec["source_sha256"] == src:
+                    return int(rec["fetch_bytes"] + rec["write_bytes"])
+    return None
 
 
 def algorithmic_work(shape, esz, packed):
@@ -200,7 +232,9 @@ def main():
     dom = max(names, key=lambda n: kms[n])
     kd = kernels[dom]
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
-                "unit": kd["unit"], "frac": kd["frac"], "traffic": None}
+                "unit": kd["unit"], "frac": kd["frac"],
+                "traffic": measured_traffic(dom, cfg["name"]), "traffic_unit": "HBM bytes per launch",
+                "algorithmic_bytes": int(work[dom]["bytes"])}
     total_flops = sum(w.get("flops", 0.0) for w in work.values())
 
     cpu = None
