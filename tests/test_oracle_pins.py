@@ -451,3 +451,32 @@ def test_golden_regression_fixture():
     out = _run(inp)
     assert np.allclose(out.y.reshape(-1), y_ref, rtol=1e-14, atol=1e-15)
     assert np.allclose(out.final_states.reshape(-1), fs_ref, rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("G,H", [(1, 2), (2, 4)])
+def test_chunk_cb_rebuilds_chunk_outputs(G, H):
+    """Within one chunk and with a zero incoming state, the dual form gives
+    y_t = sum_{s<=t} exp(cs_t - cs_s) CB[t][s] Delta_s x_s + D x_t ([tomabc] section
+    3.2, formula 1, with Q = C and K = B).  Rebuilt from the oracle's chunk_cb and
+    chunk_cumsum, it must equal the recurrence's y of a zero-start run over each chunk
+    alone.  CB is not symmetric, so a transposed or mis-indexed product fails here."""
+    Q, T, P, N = 8, 21, 3, 5
+    inp = _small(seed=131, T=T, H=H, P=P, N=N, G=G, chunk=Q)
+    x, dt, A, D = _np(inp.x), _np(inp.dt), _np(inp.A), _np(inp.D)
+    cb = oracle.chunk_cb(_np(inp.B), _np(inp.C), Q)
+    delta, cs = oracle.chunk_cumsum(dt, A, Q)
+    nc = (T + Q - 1) // Q
+    assert cb.shape == (1, nc, G, Q, Q)
+    for c in range(nc):
+        s0, e = c * Q, min((c + 1) * Q, T)
+        one = _run(wl.Inputs(inp.x[:, s0:e], inp.dt[:, s0:e], inp.A, inp.B[:, s0:e], inp.C[:, s0:e],
+                             inp.D, None, None, 0, Q))
+        for h in range(H):
+            g = h // (H // G)
+            n = e - s0
+            W = np.zeros((n, n))
+            for t in range(n):
+                for s in range(t + 1):
+                    W[t, s] = math.exp(cs[0, h, c, t] - cs[0, h, c, s]) * cb[0, c, g, t, s] * delta[0, h, c, s]
+            y = W @ x[0, s0:e, h, :] + D[h] * x[0, s0:e, h, :]
+            assert rel(y, one.y[0, :, h, :]) < 1e-13
