@@ -259,11 +259,11 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
         return with_nt(s.N, [&](auto nt) {
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
             if (s.packed)
-                hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->x,
+                hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, true>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
             else
-                hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(kThreads), 0, st, (const E *)a->x,
+                hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
             return launched();

@@ -15,6 +15,8 @@
 // delta, cs [b,H,nc,Q] fp32; cb [b,nc,G,Q,Q]; states [b,nc,H,P,N].
 #pragma once
 
+#include <type_traits>
+
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(
 // fp32: there is no 32-bit transpose read, so the tile is transposed in registers
 // on its way into LDS ([col][row], rows padded by 16 bytes) and fragments are
 // plain 32-byte reads.
-template <typename E, int KR, int COLS> struct KTile;
+template <typename E, int KR, int COLS, int TH = kThreads> struct KTile;
 
 template <typename E, int COLS>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ktile_rsrc(const E *src, int64_t ld, int rows)
@@ -219,8 +221,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ktile_rsrc(const E *src, int64
     return make_rsrc(src, rows > 0 ? ((int64_t)(rows - 1) * ld + COLS) * (int64_t)sizeof(E) : 0);
 }
 
-template <int KR, int COLS>
-struct KTile<bf16, KR, COLS> {
+template <int KR, int COLS, int TH>
+struct KTile<bf16, KR, COLS, TH> {
     static constexpr int PITCH = COLS == 64 ? 64 : COLS + 16;
     static __device__ __forceinline__ int swz(int r)
     {
@@ -229,7 +231,7 @@ struct KTile<bf16, KR, COLS> {
     static constexpr int SIZE = KR * PITCH;
     static constexpr int VPR = COLS / 8;   // 16-byte vectors per row
     static constexpr int NV = KR * VPR;
-    static constexpr int PER = (NV + kThreads - 1) / kThreads;
+    static constexpr int PER = (NV + TH - 1) / TH;
     uint4 raw[PER];
     uint32_t voff[PER];
 
@@ -242,7 +244,7 @@ struct KTile<bf16, KR, COLS> {
     {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int v = threadIdx.x + i * kThreads;
+            const int v = threadIdx.x + i * TH;
             const int r = v / VPR, c = v % VPR;
             voff[i] = (v < NV && c * 8 < ncols) ? (uint32_t)(r * ld * 2 + c * 16) : kOffNone;
         }
@@ -259,8 +261,8 @@ struct KTile<bf16, KR, COLS> {
     {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int v = threadIdx.x + i * kThreads;
-            if (NV % kThreads != 0 && v >= NV) continue;
+            const int v = threadIdx.x + i * TH;
+            if (NV % TH != 0 && v >= NV) continue;
             const int r = v / VPR, c = v % VPR;
             uint4 o = raw[i];
             if constexpr (SCALE) {
@@ -306,13 +308,13 @@ struct KTile<bf16, KR, COLS> {
     }
 };
 
-template <int KR, int COLS>
-struct KTile<float, KR, COLS> {
+template <int KR, int COLS, int TH>
+struct KTile<float, KR, COLS, TH> {
     static constexpr int PITCH = KR + 4;
     static constexpr int SIZE = COLS * PITCH;
     static constexpr int CBK = COLS / 4;
     static constexpr int NB = (KR / 4) * CBK;   // 4x4 blocks
-    static constexpr int PER = (NB + kThreads - 1) / kThreads;
+    static constexpr int PER = (NB + TH - 1) / TH;
     uint4 raw[PER][4];
     uint32_t voff[PER];   // offset of the block's first row
 
@@ -327,7 +329,7 @@ struct KTile<float, KR, COLS> {
         ldb = ld * 4;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int blk = threadIdx.x + i * kThreads;
+            const int blk = threadIdx.x + i * TH;
             const int cbk = blk % CBK, sb = blk / CBK;
             voff[i] = (blk < NB && cbk * 4 < ncols) ? (uint32_t)(sb * 4 * ldb + cbk * 16) : kOffNone;
         }
@@ -347,8 +349,8 @@ struct KTile<float, KR, COLS> {
     {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int blk = threadIdx.x + i * kThreads;
-            if (NB % kThreads != 0 && blk >= NB) continue;
+            const int blk = threadIdx.x + i * TH;
+            if (NB % TH != 0 && blk >= NB) continue;
             const int cbk = blk % CBK, sb = blk / CBK;
             float f[4][4];
 #pragma unroll
@@ -696,10 +698,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
 // ---------------------------------------------------------------------------
 // chunk_scan: y = intra-chunk quadratic form + decayed entering state + D x
 // ---------------------------------------------------------------------------
-// One workgroup per (b, c, h, 64-p tile).  The chunk's Q output rows are split
-// into 16-row sub-blocks j (t0 = 16 j); wave w owns j = w, w+4, ... so the
-// causal work is balanced.  Everything is computed transposed, D[p][t], so a
-// per-token decay is a per-lane scale:
+// One workgroup of Q/32 waves per (b, c, h, 64-p tile).  The chunk's Q output
+// rows are split into NJ = Q/16 sub-blocks j of 16 rows (t0 = 16 j); wave w owns
+// j = w and j = NJ-1-w, which balances the causal triangle exactly (every wave
+// has NJ/2 - 1 K steps strictly below its two diagonal steps).  Everything is
+// computed transposed, D[p][t], so a per-token decay is a per-lane scale:
 //   y_t = u_t [ e_{t0} (C_t . Hin) + sum_{s < S_j} CB[t][s] V_j[s] x_s ]
 //         + sum_{S_j <= s <= t} (CB[t][s] exp(cs_t - cs_s) delta_s + [s = t] D) x_s
 // with e_{t0} = exp(cs_{t0}), u_t = exp(cs_t - cs_{t0}), V_j[s] = exp(cs_{t0} -
@@ -708,11 +711,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
 // per-element exponentials are needed only on the diagonal step, where the D
 // skip term rides on the diagonal.  Segment masks (packed streams) are selects
 // on the same factors.
-// Memory: the entering-state tile (step 4) and then the x tile (step 1) occupy
-// one LDS region in turn; all their global loads are issued up front.  The C and
-// CB fragments (one row per lane, 16/32 bytes) are buffer loads fetched two K
-// steps ahead; rows past the sequence end fall outside the buffer range and read
-// as zero.
+// Memory: the entering-state tile and the x tile have LDS regions of their own
+// and are stored as soon as their loads land, so one barrier publishes both.
+// The C and CB fragments (one row per lane, 16/32 bytes) are buffer loads
+// fetched RING K steps ahead; rows past the sequence end fall outside the
+// buffer range and read as zero.
 
 // V_j rows are stored packed: row j holds 32 * floor(j/2) entries.
 __host__ __device__ constexpr int vt_offset(int j)
@@ -720,41 +723,39 @@ __host__ __device__ constexpr int vt_offset(int j)
     return 32 * ((j & 1) ? (j >> 1) * (j >> 1) : (j >> 1) * ((j >> 1) - 1));
 }
 
-// LDS bytes of the region shared by the entering-state tile and the x tile.
-template <typename E, int Q, int NT>
-__host__ __device__ constexpr int scan_region_bytes()
-{
-    constexpr int hs = 64 * (NT + kVec16<E>) * (int)sizeof(E);
-    constexpr int xt = KTile<E, Q, 64>::SIZE * (int)sizeof(E);
-    return hs > xt ? hs : xt;
-}
+template <int Q> constexpr int scan_threads() { return Q * 2; }
 
 // NT = N rounded up to 64 (compile time, so every K loop unrolls and every LDS
 // fragment offset is an immediate); columns N..NT-1 are masked.
 template <typename E, int Q, int NT, bool PACKED>
-__global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
+__global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const E *__restrict__ x, const E *__restrict__ Cm, const float *__restrict__ delta,
     const float *__restrict__ cs, const E *__restrict__ cb, const E *__restrict__ hin,
     const float *__restrict__ D, const int32_t *__restrict__ seq_idx, E *__restrict__ y,
     int T, int H, int G, int P, int N, int nc, int ntp)
 {
     using F = frag_t<E>;
-    using XT = KTile<E, Q, 64>;
+    constexpr int TH = scan_threads<Q>();
+    using XT = KTile<E, Q, 64, TH>;
     constexpr int V = kVec16<E>;
     constexpr int ES = (int)sizeof(E);
     constexpr int NJ = Q / 16;          // 16-row sub-blocks per chunk
-    constexpr int NSB = Q / 64;         // sub-blocks per wave
-    constexpr int KSB = (NJ - 1) / 2;   // K steps strictly below some sub-block's diagonal
-    constexpr int NKS = NT / 32;        // K steps of the step-4 product
-    constexpr int HP = NT + V;          // pitch of the entering-state tile
+    constexpr int NSB = 2;              // sub-blocks per wave
+    constexpr int KSB = (NJ - 1) / 2;   // K steps strictly below some sub-block's diagonal step
+    constexpr int NKS = NT / 32;        // K steps of the entering-state product
+    // Pitch of the entering-state tile: rows 32 bytes apart modulo 256 keep its
+    // 16-byte fragment reads free of bank conflicts (a 128-bit LDS read serves
+    // lanes 0-7 with 16-23, 8-15 with 24-31, and so on, in one pass).
+    constexpr int HP = NT + 2 * V;
     constexpr int RING = 3;             // C / CB fragments fetched RING K steps ahead
-    __shared__ __align__(16) char region[scan_region_bytes<E, Q, NT>()];
+    // the entering-state tile; after step 4 the same memory stages y (bf16)
+    constexpr int HSZ = 64 * HP > Q * 64 ? 64 * HP : Q * 64;
+    __shared__ __align__(16) E hs[HSZ];
+    __shared__ __align__(16) E xt[XT::SIZE];
     __shared__ __align__(16) float vt[vt_offset(NJ)];
     __shared__ __align__(16) float csb[Q];   // cs * log2(e)
     __shared__ __align__(16) float db[Q];
     __shared__ __align__(16) int sq[PACKED ? Q : 4];
-    E *hs = reinterpret_cast<E *>(region);   // entering-state tile [64 p][NT], then ...
-    E *xt = reinterpret_cast<E *>(region);   // ... the x tile
 
     const int units = nc * H * ntp;
     const int u = xcd_remap(blockIdx.x, units);
@@ -766,20 +767,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     const int t0 = c * Q, len = min(Q, T - t0);
     const int p0 = tp * 64;
     const int64_t cso = (((int64_t)b * H + h) * nc + c) * Q;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    int jb[NSB];
+    jb[0] = wave;
+    jb[1] = NJ - 1 - wave;
 
     // ---- issue the global loads ----
-    // entering-state tile: VL lanes per row (one 16-byte vector each), RPP rows per pass
-    constexpr int VL = NT / V, RPP = kThreads / VL, HPASS = 64 / RPP;
+    // entering-state tile: VL lanes per row (one 16-byte vector each), RPP rows
+    // per pass; at most HG passes are held in registers at once
+    constexpr int VL = NT / V, RPP = TH / VL, HPASS = 64 / RPP, HG = HPASS < 8 ? HPASS : 8;
     const int vpr = N / V;
     const int hv = threadIdx.x % VL, hr = threadIdx.x / VL;
     const auto hrs = make_rsrc(hin + ((((int64_t)b * nc + c) * H + h) * P + p0) * (int64_t)N,
                                (int64_t)min(64, P - p0) * N * ES);
     const uint32_t hvoff = hv < vpr ? (uint32_t)(hr * N * ES + hv * 16) : kOffNone;
-    uint4 hraw[HPASS];
+    auto hoff = [&](int i) -> uint32_t {
+        return hvoff == kOffNone ? kOffNone : hvoff + (uint32_t)(i * RPP * N * ES);
+    };
+    uint4 hraw[HG];
 #pragma unroll
-    for (int i = 0; i < HPASS; ++i)
-        hraw[i] = bload16(hrs, hvoff == kOffNone ? kOffNone : hvoff + (uint32_t)(i * RPP * N * ES));
+    for (int i = 0; i < HG; ++i) hraw[i] = bload16(hrs, hoff(i));
     XT xs;
     xs.init((int64_t)H * P, P - p0);
     xs.load(XT::rsrc(x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len));
@@ -800,31 +808,46 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     uint32_t cbase[NSB], cbbase[NSB];
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-        const int t = 16 * (wave + 4 * k) + li;
-        live[k] = 16 * (wave + 4 * k) < len;   // wave-uniform
-        cbase[k] = (uint32_t)(t * G * N * ES + 8 * lg * ES);
+        const int t = 16 * jb[k] + li;
+        live[k] = 16 * jb[k] < len;   // wave-uniform
+        cbase[k] = live[k] ? (uint32_t)(t * G * N * ES + 8 * lg * ES) : kOffNone;
         cbbase[k] = (uint32_t)((t * Q + 8 * lg) * ES);
     }
-    auto c_off = [&](int k, int ks) -> uint32_t {   // ks is a compile-time constant at every call
-        return (ks * 32 + 8 * lg < N) ? cbase[k] + (uint32_t)(ks * 32 * ES) : kOffNone;
+    // C fragment offset of K step ks (a compile-time constant at every call).  A
+    // dead sub-block's base is kOffNone, and kOffNone plus a step offset is still
+    // outside the buffer, so it reads zero.  Columns >= N (only when N < NT) are
+    // masked explicitly; with N == NT the step offset is a plain immediate.
+    auto c_off = [&](int k, int ks, auto full) -> uint32_t {
+        if constexpr (decltype(full)::value) return cbase[k] + (uint32_t)(ks * 32 * ES);
+        else return (ks * 32 + 8 * lg < N) ? cbase[k] + (uint32_t)(ks * 32 * ES) : kOffNone;
     };
-    auto cb_off = [&](int k, int ks) -> uint32_t { return cbbase[k] + (uint32_t)(ks * 32 * ES); };
+    const std::false_type masked{};
+    auto cb_off = [&](int k, int ks) -> uint32_t {
+        return (live[k] && ks < (jb[k] >> 1)) ? cbbase[k] + (uint32_t)(ks * 32 * ES) : kOffNone;
+    };
 
     F cr[RING][NSB];
 #pragma unroll
     for (int r = 0; r < RING; ++r)
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
-            if (r < NKS) bload_frag(crs, c_off(k, r), cr[r][k]);
+            if (r < NKS) bload_frag(crs, c_off(k, r, masked), cr[r][k]);
             else cr[r][k] = F{};
         }
 
-    // ---- entering-state tile and per-token values into LDS ----
-    if (hv < vpr) {
+    // ---- entering-state tile, x tile and per-token values into LDS ----
 #pragma unroll
-        for (int i = 0; i < HPASS; ++i)
-            *reinterpret_cast<uint4 *>(hs + (hr + i * RPP) * HP + hv * V) = hraw[i];
+    for (int i0 = 0; i0 < HPASS; i0 += HG) {
+        if (i0 > 0) {
+#pragma unroll
+            for (int i = 0; i < HG; ++i) hraw[i] = bload16(hrs, hoff(i0 + i));
+        }
+        // lanes past column N loaded zeros: storing them zero-fills columns N..NT-1
+#pragma unroll
+        for (int i = 0; i < HG; ++i)
+            *reinterpret_cast<uint4 *>(hs + (hr + (i0 + i) * RPP) * HP + hv * V) = hraw[i];
     }
+    xs.template store<false, false>(xt, nullptr, nullptr);
     if (threadIdx.x < Q) {
         csb[threadIdx.x] = c_i;
         db[threadIdx.x] = d_i;
@@ -848,31 +871,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[k][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- step 4 part: Hin C^T over n ----
+    // ---- step 4 part: Hin C^T over n (Hin columns N..NT-1 are zero in LDS) ----
+    auto step4 = [&](auto full) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        const int kk = ks * 32 + 8 * lg;
-        const bool kin = kk < N;
-        F a[4];
+        for (int ks = 0; ks < NKS; ++ks) {
+            F a[4];
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) a[pb] = kin ? load_frag(hs + (pb * 16 + li) * HP + kk) : F{};
+            for (int pb = 0; pb < 4; ++pb) a[pb] = load_frag(hs + (pb * 16 + li) * HP + ks * 32 + 8 * lg);
 #pragma unroll
-        for (int k = 0; k < NSB; ++k) {
-            if (!live[k]) continue;
+            for (int k = 0; k < NSB; ++k) {
+                if (!live[k]) continue;
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], cr[ks % RING][k]);
+                for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], cr[ks % RING][k]);
+            }
+            if (ks + RING < NKS) {
+#pragma unroll
+                for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + RING, full), cr[ks % RING][k]);
+            }
         }
-        if (ks + RING < NKS) {
-#pragma unroll
-            for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + RING), cr[ks % RING][k]);
-        }
-    }
+    };
+    if (N == NT) step4(std::true_type{});
+    else step4(masked);
 
-    // CB fragments: the diagonal step of every sub-block, and the first RING
+    // CB fragments: the diagonal step of both sub-blocks, and the first RING
     // strictly-below steps (every row of cb is in bounds)
     F dcb[NSB];
 #pragma unroll
-    for (int k = 0; k < NSB; ++k) bload_frag(cbrs, cb_off(k, (wave + 4 * k) >> 1), dcb[k]);
+    for (int k = 0; k < NSB; ++k)
+        bload_frag(cbrs, live[k] ? cbbase[k] + (uint32_t)((jb[k] >> 1) * 32 * ES) : kOffNone, dcb[k]);
 #pragma unroll
     for (int r = 0; r < RING; ++r)
 #pragma unroll
@@ -882,7 +908,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
         }
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-        const int tj = 16 * (wave + 4 * k);
+        const int tj = 16 * jb[k];
         const bool mo = !PACKED || sq[tj] == seq_prev;
         const float e0 = exp2_(csb[tj]);
 #pragma unroll
@@ -891,10 +917,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
             for (int q = 0; q < 4; ++q) acc[k][pb][q] = mo ? acc[k][pb][q] * e0 : 0.f;
     }
 
-    __syncthreads();   // every wave is done with the entering-state tile
-    xs.template store<false, false>(xt, nullptr, nullptr);
-    __syncthreads();
-
+    __syncthreads();   // the V table is complete
     typename XT::Off xoff[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) xoff[pb] = XT::frag_off(pb * 16);
@@ -907,7 +930,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
         for (int pb = 0; pb < 4; ++pb) a[pb] = XT::frag_at(xt, xoff[pb], ks * 32);
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
-            const int j = wave + 4 * k;
+            const int j = jb[k];
             if (ks >= (j >> 1) || !live[k]) continue;
             const float *vrow = vt + vt_offset(j) + ks * 32 + 8 * lg;
             const floatx4 v0 = *reinterpret_cast<const floatx4 *>(vrow);
@@ -927,7 +950,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
     const float Dh = D ? D[h] : 0.f;
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-        const int j = wave + 4 * k;
+        const int j = jb[k];
         if (!live[k]) continue;
         const int tj = 16 * j, t = tj + li;
         const bool keep = !PACKED || sq[t] == sq[tj];
@@ -960,17 +983,53 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_scan(
         for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], XT::frag_at(xt, xoff[pb], ks * 32), wfr);
     }
 
-    // ---- epilogue: store y (4 consecutive p of one t per lane) ----
+    // ---- epilogue: store y ----
+    if constexpr (sizeof(E) == 2) {
+        // Each wave turns its own 32 rows around in the entering-state region (free
+        // since the barrier after step 4) so that y leaves as whole 128-byte rows.
+        // Rows have 8 chunks of 16 bytes stored at chunk ^ ((t >> 1) & 7): the 8-byte
+        // writes of 16 rows spread over all banks.  The 16-byte reads take 8 rows
+        // per instruction, ordered so that the two lane octets sharing an LDS pass
+        // (0-7 with 16-23, ...) read rows of opposite parity, i.e. opposite bank halves.
+        auto yoff = [](int t, int chunk) { return t * 64 + 8 * (chunk ^ ((t >> 1) & 7)); };
 #pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-        const int t = 16 * (wave + 4 * k) + li;
-        if (t >= len) continue;
+        for (int k = 0; k < NSB; ++k) {
+            const int t = 16 * jb[k] + li;
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const int p = p0 + pb * 16 + 4 * lg;
-            if (p >= P) continue;
-            float o[4] = {acc[k][pb][0], acc[k][pb][1], acc[k][pb][2], acc[k][pb][3]};
-            store4_f32(y + (((int64_t)b * T + t0 + t) * H + h) * P + p, o);
+            for (int pb = 0; pb < 4; ++pb) {
+                const uint2 v{pack_bf16x2(acc[k][pb][0], acc[k][pb][1]), pack_bf16x2(acc[k][pb][2], acc[k][pb][3])};
+                *reinterpret_cast<uint2 *>(hs + yoff(t, 2 * pb + (lg >> 1)) + 4 * (lg & 1)) = v;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int oct = lane >> 3, chunk = lane & 7;
+        const int rsel = (oct & 4) + ((oct & 1) << 1) + ((oct >> 1) & 1);   // 0,2,1,3,4,6,5,7
+        const bool pin = p0 + 8 * chunk < P;
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int t = 16 * jb[k] + 8 * half + rsel;
+                const uint4 v = *reinterpret_cast<const uint4 *>(hs + yoff(t, chunk));
+                if (t < len && pin)
+                    *reinterpret_cast<uint4 *>(y + (((int64_t)b * T + t0 + t) * H + h) * P + p0 + 8 * chunk) = v;
+            }
+        }
+    } else {
+        // fp32: each lane writes 16 bytes (4 consecutive p of one t) directly
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+            const int t = 16 * jb[k] + li;
+            if (t >= len) continue;
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int p = p0 + pb * 16 + 4 * lg;
+                if (p >= P) continue;
+                float o[4] = {acc[k][pb][0], acc[k][pb][1], acc[k][pb][2], acc[k][pb][3]};
+                store4_f32(y + (((int64_t)b * T + t0 + t) * H + h) * P + p, o);
+            }
         }
     }
 }
