@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
     float *__restrict__ delta, float *__restrict__ cs, int T, int H, int Q, int nc, int softplus)
 {
     const int c = blockIdx.x, b = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int h = blockIdx.y * kCumsumHeads + wave;
     if (h >= H) return;   // whole wave; no barriers below
     const int t0 = c * Q;
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(
     int ti = 0;
     while (tile > ti) { tile -= ti + 1; ++ti; }
     const int si = tile;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const int s_base = si * 64 + (wave & 1) * 32;
     const int t_base = ti * 64 + (wave >> 1) * 32;
     const int t0 = c * Q, len = min(Q, T - t0);
@@ -419,7 +420,7 @@ __device__ __forceinline__ void state_product(StateSmem<E, NT> &sm, const E *xsr
     using XT = typename StateSmem<E, NT>::XT;
     using BT = typename StateSmem<E, NT>::BT;
     constexpr int NI = NT / 64;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     typename BT::Off aoff[NI];
     typename XT::Off xoff[4];
 #pragma unroll
@@ -449,6 +450,56 @@ __device__ __forceinline__ void state_product(StateSmem<E, NT> &sm, const E *xsr
                 for (int j = 0; j < 4; ++j) mma(acc[i][j], a[i], bb[j]);
         }
         __syncthreads();
+    }
+}
+
+// Writes the 64 x NT state tile held in MFMA layout (acc[i][j][r] <-> n = w*NT/4 +
+// i*16 + 4*(lane/16) + r, p = j*16 + lane%16) to out[p][n] (row pitch N), rows
+// p < prows and columns n < N only.  bf16 goes through LDS (`stage`, at least
+// 64 * NT elements, free on entry; the caller's last barrier covers earlier
+// readers) so that whole rows leave as 16-byte vectors: the 8-byte writes put
+// 16-byte chunk c of row p at c ^ (p mod min(NT/8, 16)), which spreads 16 rows
+// over all banks, and each read instruction covers 64 consecutive chunks in a
+// lane order (bits 3 and 4 of the lane swapped) that gives every LDS pass 256
+// contiguous bytes.  fp32 lanes already hold 16 bytes and store directly.
+template <typename E, int NT>
+__device__ __forceinline__ void store_state_tile(E *stage, const floatx4 (&acc)[NT / 64][4], E *out, int prows,
+                                                 int N)
+{
+    constexpr int NI = NT / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    if constexpr (sizeof(E) == 2) {
+        constexpr int CPR = NT / 8;                       // 16-byte chunks per row
+        constexpr int GM = (CPR < 16 ? CPR : 16) - 1;     // chunk swizzle mask
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = j * 16 + li;
+                const uint2 v{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+                *reinterpret_cast<uint2 *>(stage + p * NT + 8 * ((n >> 3) ^ (p & GM)) + (n & 7)) = v;
+            }
+        __syncthreads();
+        const int f = (lane & 7) | ((lane & 16) >> 1) | ((lane & 8) << 1) | (lane & 32);
+#pragma unroll
+        for (int m = 0; m < NT / 32; ++m) {
+            const int F = (wave + 4 * m) * 64 + f;
+            const int p = F / CPR, ch = F % CPR;
+            const uint4 v = *reinterpret_cast<const uint4 *>(stage + p * NT + 8 * (ch ^ (p & GM)));
+            if (p < prows && 8 * ch < N) *reinterpret_cast<uint4 *>(out + (int64_t)p * N + 8 * ch) = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = j * 16 + li;
+                if (p < prows && n < N) {
+                    float o[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                    store4_f32(out + (int64_t)p * N + n, o);
+                }
+            }
     }
 }
 
@@ -502,18 +553,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     state_product<E, NT, PACKED>(sm, xsrc, ldx, bsrc, ldb, len, w, m, xs, bs, acc);
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     E *out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = p0 + j * 16 + li;
-            if (p < P && n < N) {
-                float o[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-                store4_f32(out + (int64_t)p * N + n, o);
-            }
-        }
+    store_state_tile<E, NT>(sm.b, acc, out + (int64_t)p0 * N, P - p0, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -635,7 +676,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
     const int sg = u / (ntp * H);
     const int g = h / (H / G);
     const int p0 = tp * 64;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     float *out = final_states + ((int64_t)sg * H + h) * (int64_t)P * N;
     const int te = seg_end[sg];
     if (te < 0) {
