@@ -191,7 +191,7 @@ def main():
     names.append("chunk_scan")
     delta = torch.empty((p.b, p.H, p.nc, p.Q), dtype=torch.float32, device=dev)
     cs = torch.empty_like(delta)
-    cb = torch.empty((p.b, p.nc, p.G, p.Q, p.Q), dtype=g.x.dtype, device=dev)
+    cb = torch.empty(p.cb_shape(), dtype=g.x.dtype, device=dev)
     states = torch.empty((p.b, p.nc, p.H, p.P, p.N), dtype=g.x.dtype, device=dev)
     seg_end = torch.empty((max(p.nseq, 1),), dtype=torch.int32, device=dev)
     ybuf = torch.empty_like(g.x)

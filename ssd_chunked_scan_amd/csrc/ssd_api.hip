@@ -136,11 +136,14 @@ struct Workspace {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// N rounded up to 64: the state width the kernels are compiled for.
+int64_t nt_of(int64_t N) { return N <= 64 ? 64 : N <= 128 ? 128 : 256; }
+
 Workspace workspace_layout(const Shape &s)
 {
     Workspace w;
     const size_t dcs = (size_t)(s.b * s.H * s.nc * s.Q) * 4;
-    const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * s.Q) * s.esz;
+    const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * (s.Q + nt_of(s.N))) * s.esz;
     const size_t sts = (size_t)(s.b * s.nc * s.H * s.P * s.N) * s.esz;
     w.delta = 0;
     w.cs = align256(w.delta + dcs);
@@ -166,16 +169,6 @@ ssd_status run_cumsum(const Shape &s, const ssd_fwd_args *a, float *delta, float
     return launched();
 }
 
-template <typename E>
-ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
-{
-    const int nt = (int)(s.Q / 64), ntri = nt * (nt + 1) / 2;
-    dim3 grid((unsigned)(ntri * s.nc * s.G), (unsigned)s.b);
-    hipLaunchKernelGGL(k_chunk_cb<E>, grid, dim3(kThreads), 0, st, (const E *)a->B, (const E *)a->C, cb,
-                       (int)s.T, (int)s.G, (int)s.N, (int)s.Q, (int)s.nc, ntri);
-    return launched();
-}
-
 // The state kernels cover all of N in one workgroup: NT = N rounded up to 64.
 template <typename F>
 ssd_status with_nt(int64_t N, F &&f)
@@ -192,6 +185,22 @@ ssd_status with_q(int64_t Q, F &&f)
     if (Q == 128) return f(std::integral_constant<int, 128>{});
     return f(std::integral_constant<int, 256>{});
 }
+
+template <typename E>
+ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
+{
+    const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
+    dim3 grid((unsigned)(ntri * s.nc * s.G), (unsigned)s.b);
+    return with_q(s.Q, [&](auto q) {
+        return with_nt(s.N, [&](auto nt) {
+            constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+            hipLaunchKernelGGL((k_chunk_cb<E, Q, NT>), grid, dim3(kThreads), 0, st, (const E *)a->B,
+                               (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc);
+            return launched();
+        });
+    });
+}
+
 
 template <typename E>
 ssd_status run_state(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, E *states,
@@ -260,11 +269,11 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
             if (s.packed)
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, true>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
-                                   (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
+                                   delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
             else
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
-                                   (const E *)a->C, delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
+                                   delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
             return launched();
         });

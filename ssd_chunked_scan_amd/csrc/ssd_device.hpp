@@ -65,6 +65,14 @@ __device__ __forceinline__ floatx8 load_frag(const float *p)
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Fragment stores to a 16-byte aligned address.
+__device__ __forceinline__ void store_frag(bf16 *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
+__device__ __forceinline__ void store_frag(float *p, const floatx8 &v)
+{
+    *reinterpret_cast<floatx4 *>(p) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+    *reinterpret_cast<floatx4 *>(p + 4) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ floatx8 to_f32(const bf16x8 &v) { return __builtin_convertvector(v, floatx8); }
 __device__ __forceinline__ floatx8 to_f32(const floatx8 &v) { return v; }
 

@@ -107,83 +107,125 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
 
 
 // ---------------------------------------------------------------------------
-// chunk_cb: cb[b,c,g,t,s] = sum_n C[t,n] B[s,n] for the lower block triangle
+// chunk_cb: C B^T and a copy of C per (b, c, g), in fragment-major order
 // ---------------------------------------------------------------------------
-// One workgroup per 64x64 (t, s) tile with s-tile <= t-tile; four waves of 32x32.
-// The MFMA computes D[s][t] (A = B rows, B = C rows, K = n, both K-contiguous in
-// memory), so each lane ends with 4 consecutive s of one t: a vector store.
-// Operand fragments are fetched two K steps ahead of their use.
-template <typename E>
-__global__ __launch_bounds__(kThreads) void k_chunk_cb(
-    const E *__restrict__ Bm, const E *__restrict__ Cm, E *__restrict__ cb,
-    int T, int G, int N, int Q, int nc, int ntri)
+// Fragment-major order stores a row-major matrix as 16-row x 32-column blocks
+// (one MFMA K step), block (rb, kb) at (rb * NCOL/32 + kb) * 512 elements, each
+// block as the 64 lanes' fragments: lane l = r % 16 + 16 ((col % 32) / 8) holds
+// the 8 consecutive columns 8 ((col % 32) / 8) .. +7 of row r.  chunk_scan then
+// fetches a fragment as one contiguous 1 KB (bf16) per wave instead of 16 rows x
+// 64 bytes.  Per (b, c, g) the chunk_cb buffer holds the Q x Q matrix CB[t][s] =
+// sum_n C[t][n] B[s][n] (only the 64 x 64 tiles with s-tile <= t-tile are
+// written) followed by the chunk's C rows as a Q x NT matrix (rows past the
+// sequence end and columns past N are zero).
+template <int Q, int NT> constexpr int64_t cb_group_elems() { return (int64_t)Q * Q + (int64_t)Q * NT; }
+
+// One workgroup per 64x64 (t, s) tile with s-tile <= t-tile.  The B rows of the
+// s-tile and the C rows of the t-tile are loaded with row-contiguous 16-byte
+// loads into LDS (row pitch 32 bytes past a multiple of 256, which keeps the
+// 16-byte fragment reads conflict-free); each wave computes 32x32 as D[s][t]
+// (A = B rows, B = C rows, K = n).  The result goes through LDS to leave in
+// fragment-major order; the tiles of the first s-tile also copy their C rows.
+template <typename E, int Q, int NT>
+__global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm, const E *__restrict__ Cm,
+                                                       E *__restrict__ cbuf, int T, int G, int N, int nc)
 {
     using F = frag_t<E>;
-    const int units = ntri * nc * G;
+    constexpr int V = kVec16<E>, ES = (int)sizeof(E);
+    constexpr int QT = Q / 64, NTRI = QT * (QT + 1) / 2;
+    constexpr int PITCH = NT + 2 * V;
+    constexpr int NKS = NT / 32;
+    __shared__ __align__(16) E bs[64 * PITCH];
+    __shared__ __align__(16) E csm[64 * PITCH];
+    const int units = NTRI * nc * G;
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
-    int tile = u % ntri;
-    const int cg = u / ntri, g = cg % G, c = cg / G;
+    int tile = u % NTRI;
+    const int cg = u / NTRI, g = cg % G, c = cg / G;
     int ti = 0;
-    while (tile > ti) { tile -= ti + 1; ++ti; }
+    while (tile > ti) {
+        tile -= ti + 1;
+        ++ti;
+    }
     const int si = tile;
+    const int t0 = c * Q, len = min(Q, T - t0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    const int s_base = si * 64 + (wave & 1) * 32;
-    const int t_base = ti * 64 + (wave >> 1) * 32;
-    const int t0 = c * Q, len = min(Q, T - t0);
 
-    const E *brow[2], *crow[2];
-    bool bv[2], cv[2];
+    // ---- B rows si*64.. and C rows ti*64.. into LDS (zero past len and past N) ----
+    constexpr int VL = NT / V, RPP = kThreads / VL, NPASS = 64 / RPP, PG = NPASS < 8 ? NPASS : 8;
+    const int hv = threadIdx.x % VL, hr = threadIdx.x / VL;
+    const uint32_t voff = hv * V < N ? (uint32_t)(hr * G * N * ES + hv * 16) : kOffNone;
+    auto rows_rsrc = [&](const E *m, int r0) {
+        const int rows = min(64, len - r0);
+        return make_rsrc(m + (((int64_t)b * T + t0 + r0) * G + g) * N,
+                         rows > 0 ? ((int64_t)(rows - 1) * G * N + N) * ES : 0);
+    };
+    const auto brs = rows_rsrc(Bm, si * 64), crs = rows_rsrc(Cm, ti * 64);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int s = s_base + i * 16 + li, t = t_base + i * 16 + li;
-        bv[i] = s < len;
-        cv[i] = t < len;
-        brow[i] = Bm + (((int64_t)b * T + t0 + (bv[i] ? s : 0)) * G + g) * N;
-        crow[i] = Cm + (((int64_t)b * T + t0 + (cv[i] ? t : 0)) * G + g) * N;
+    for (int i0 = 0; i0 < NPASS; i0 += PG) {
+        uint4 rb[PG], rc[PG];
+#pragma unroll
+        for (int i = 0; i < PG; ++i) {
+            const uint32_t o = voff == kOffNone ? kOffNone : voff + (uint32_t)((i0 + i) * RPP * G * N * ES);
+            rb[i] = bload16(brs, o);
+            rc[i] = bload16(crs, o);
+        }
+#pragma unroll
+        for (int i = 0; i < PG; ++i) {
+            *reinterpret_cast<uint4 *>(bs + (hr + (i0 + i) * RPP) * PITCH + hv * V) = rb[i];
+            *reinterpret_cast<uint4 *>(csm + (hr + (i0 + i) * RPP) * PITCH + hv * V) = rc[i];
+        }
     }
-    // all K steps' fragments in flight at once (bf16: N <= 256 is at most 8 steps);
-    // fp32 fragments are twice as large, so fp32 keeps a ring of 2
-    constexpr int RD = sizeof(E) == 2 ? 8 : 2;
-    const int nks = (N + 31) / 32;
-    F fa[RD][2], fb[RD][2];
-    auto fetch = [&](F (&a)[2], F (&bb)[2], int ks) {
-        const int k = ks * 32 + 8 * lg;
-        const bool kin = k < N;
+    __syncthreads();
+
+    E *group = cbuf + (((int64_t)b * nc + c) * G + g) * cb_group_elems<Q, NT>();
+    if (si == 0) {
+        // the C rows of this t-tile, fragment-major: 4 row blocks x NKS K steps
+        E *cf = group + (int64_t)Q * Q;
+#pragma unroll
+        for (int blk = wave; blk < 4 * NKS; blk += 4) {
+            const int rb = blk / NKS, kb = blk % NKS;
+            const F v = load_frag(csm + (16 * rb + li) * PITCH + kb * 32 + 8 * lg);
+            store_frag(cf + ((int64_t)((4 * ti + rb) * NKS + kb) * 64 + lane) * 8, v);
+        }
+    }
+
+    // ---- D[s][t] over K = n ----
+    const int s_w = (wave & 1) * 32, t_w = (wave >> 1) * 32;
+    floatx4 acc[2][2] = {};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        F fa[2], fb[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            a[i] = (bv[i] && kin) ? load_frag(brow[i] + k) : F{};
-            bb[i] = (cv[i] && kin) ? load_frag(crow[i] + k) : F{};
+            fa[i] = load_frag(bs + (s_w + 16 * i + li) * PITCH + ks * 32 + 8 * lg);
+            fb[i] = load_frag(csm + (t_w + 16 * i + li) * PITCH + ks * 32 + 8 * lg);
         }
-    };
 #pragma unroll
-    for (int r = 0; r < RD; ++r) {
-        if (r < nks) fetch(fa[r], fb[r], r);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mma(acc[i][j], fa[i], fb[j]);
     }
-    floatx4 acc[2][2] = {};
-    for (int k0 = 0; k0 < nks; k0 += RD) {
-#pragma unroll
-        for (int r = 0; r < RD; ++r) {
-            const int ks = k0 + r;
-            if (ks < nks) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) mma(acc[i][j], fa[r][i], fb[r][j]);
-                if (ks + RD < nks) fetch(fa[r], fb[r], ks + RD);
-            }
-        }
-    }
-    E *out = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+
+    // ---- through LDS (bs reused as st[t][s]) to fragment-major CB ----
+    constexpr int SP = 64 + 2 * V;
+    __syncthreads();   // every wave is done reading bs
+    E *st = bs;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int s = s_base + i * 16 + 4 * lg, t = t_base + j * 16 + li;
-            float o[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            store4_f32(out + (int64_t)t * Q + s, o);
+            const float o[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            store4_f32(st + (t_w + 16 * j + li) * SP + s_w + 16 * i + 4 * lg, o);
         }
+    __syncthreads();
+#pragma unroll
+    for (int blk = wave; blk < 8; blk += 4) {
+        const int rb = blk >> 1, kb = blk & 1;
+        const F v = load_frag(st + (16 * rb + li) * SP + 32 * kb + 8 * lg);
+        store_frag(group + ((int64_t)((4 * ti + rb) * (Q / 32) + 2 * si + kb) * 64 + lane) * 8, v);
+    }
 }
 
 
@@ -755,9 +797,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
 // on the same factors.
 // Memory: the entering-state tile and the x tile have LDS regions of their own
 // and are stored as soon as their loads land, so one barrier publishes both.
-// The C and CB fragments (one row per lane, 16/32 bytes) are buffer loads
-// fetched RING K steps ahead; rows past the sequence end fall outside the
-// buffer range and read as zero.
+// The C and CB fragments come from the chunk_cb buffer, fragment-major (one
+// contiguous block per wave and K step), fetched RING K steps ahead.
 
 // V_j rows are stored packed: row j holds 32 * floor(j/2) entries.
 __host__ __device__ constexpr int vt_offset(int j)
@@ -771,8 +812,8 @@ template <int Q> constexpr int scan_threads() { return Q * 2; }
 // fragment offset is an immediate); columns N..NT-1 are masked.
 template <typename E, int Q, int NT, bool PACKED>
 __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
-    const E *__restrict__ x, const E *__restrict__ Cm, const float *__restrict__ delta,
-    const float *__restrict__ cs, const E *__restrict__ cb, const E *__restrict__ hin,
+    const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
+    const E *__restrict__ cbuf, const E *__restrict__ hin,
     const float *__restrict__ D, const int32_t *__restrict__ seq_idx, E *__restrict__ y,
     int T, int H, int G, int P, int N, int nc, int ntp)
 {
@@ -842,30 +883,26 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     }
     const int seq_prev = PACKED ? seq_idx[c > 0 ? t0 - 1 : 0] : 0;
 
-    // C rows (t, group g) of this chunk and the chunk's CB tile; C rows past the
-    // sequence end fall outside the resource and read as zero
-    const auto crs = make_rsrc(Cm + (((int64_t)b * T + t0) * G + g) * N, ((int64_t)(len - 1) * G * N + N) * ES);
-    const auto cbrs = make_rsrc(cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q, (int64_t)Q * Q * ES);
+    // The chunk_cb buffer of this (b, c, g): CB then C, both fragment-major, so
+    // the fragment of row block j and K step ks is the contiguous 64 x 8 block
+    // (j * steps-per-row + ks); lane l takes elements 8 l .. 8 l + 7 of it.  A
+    // dead sub-block (rows past the sequence end) reads nothing: its offset is
+    // kOffNone, which stays outside the buffer after adding a block offset.
+    const E *group = cbuf + (((int64_t)b * nc + c) * G + g) * cb_group_elems<Q, NT>();
+    const auto cbrs = make_rsrc(group, (int64_t)Q * Q * ES);
+    const auto crs = make_rsrc(group + (int64_t)Q * Q, (int64_t)Q * NT * ES);
+    constexpr uint32_t BLK = 512 * ES;   // bytes per fragment block
     bool live[NSB];
     uint32_t cbase[NSB], cbbase[NSB];
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-        const int t = 16 * jb[k] + li;
         live[k] = 16 * jb[k] < len;   // wave-uniform
-        cbase[k] = live[k] ? (uint32_t)(t * G * N * ES + 8 * lg * ES) : kOffNone;
-        cbbase[k] = (uint32_t)((t * Q + 8 * lg) * ES);
+        cbase[k] = live[k] ? (uint32_t)(jb[k] * NKS) * BLK + lane * 8 * ES : kOffNone;
+        cbbase[k] = (uint32_t)(jb[k] * (Q / 32)) * BLK + lane * 8 * ES;
     }
-    // C fragment offset of K step ks (a compile-time constant at every call).  A
-    // dead sub-block's base is kOffNone, and kOffNone plus a step offset is still
-    // outside the buffer, so it reads zero.  Columns >= N (only when N < NT) are
-    // masked explicitly; with N == NT the step offset is a plain immediate.
-    auto c_off = [&](int k, int ks, auto full) -> uint32_t {
-        if constexpr (decltype(full)::value) return cbase[k] + (uint32_t)(ks * 32 * ES);
-        else return (ks * 32 + 8 * lg < N) ? cbase[k] + (uint32_t)(ks * 32 * ES) : kOffNone;
-    };
-    const std::false_type masked{};
+    auto c_off = [&](int k, int ks) -> uint32_t { return cbase[k] + (uint32_t)ks * BLK; };
     auto cb_off = [&](int k, int ks) -> uint32_t {
-        return (live[k] && ks < (jb[k] >> 1)) ? cbbase[k] + (uint32_t)(ks * 32 * ES) : kOffNone;
+        return (live[k] && ks < (jb[k] >> 1)) ? cbbase[k] + (uint32_t)ks * BLK : kOffNone;
     };
 
     F cr[RING][NSB];
@@ -873,7 +910,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     for (int r = 0; r < RING; ++r)
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
-            if (r < NKS) bload_frag(crs, c_off(k, r, masked), cr[r][k]);
+            if (r < NKS) bload_frag(crs, c_off(k, r), cr[r][k]);
             else cr[r][k] = F{};
         }
 
@@ -913,34 +950,30 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[k][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- step 4 part: Hin C^T over n (Hin columns N..NT-1 are zero in LDS) ----
-    auto step4 = [&](auto full) {
+    // ---- step 4 part: Hin C^T over n (columns N..NT-1 are zero in both) ----
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            F a[4];
+    for (int ks = 0; ks < NKS; ++ks) {
+        F a[4];
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) a[pb] = load_frag(hs + (pb * 16 + li) * HP + ks * 32 + 8 * lg);
+        for (int pb = 0; pb < 4; ++pb) a[pb] = load_frag(hs + (pb * 16 + li) * HP + ks * 32 + 8 * lg);
 #pragma unroll
-            for (int k = 0; k < NSB; ++k) {
-                if (!live[k]) continue;
+        for (int k = 0; k < NSB; ++k) {
+            if (!live[k]) continue;
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], cr[ks % RING][k]);
-            }
-            if (ks + RING < NKS) {
-#pragma unroll
-                for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + RING, full), cr[ks % RING][k]);
-            }
+            for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], a[pb], cr[ks % RING][k]);
         }
-    };
-    if (N == NT) step4(std::true_type{});
-    else step4(masked);
+        if (ks + RING < NKS) {
+#pragma unroll
+            for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + RING), cr[ks % RING][k]);
+        }
+    }
 
     // CB fragments: the diagonal step of both sub-blocks, and the first RING
     // strictly-below steps (every row of cb is in bounds)
     F dcb[NSB];
 #pragma unroll
     for (int k = 0; k < NSB; ++k)
-        bload_frag(cbrs, live[k] ? cbbase[k] + (uint32_t)((jb[k] >> 1) * 32 * ES) : kOffNone, dcb[k]);
+        bload_frag(cbrs, live[k] ? cbbase[k] + (uint32_t)(jb[k] >> 1) * BLK : kOffNone, dcb[k]);
 #pragma unroll
     for (int r = 0; r < RING; ++r)
 #pragma unroll

@@ -136,6 +136,7 @@ class Problem:
         self.D, self.initial_states, self.seq_idx = D, initial_states, seq_idx
         self.b, self.T, self.H, self.P, self.N, self.G, self.Q = b, T, H, P, N, G, int(chunk)
         self.nc = (T + self.Q - 1) // self.Q
+        self.NT = 64 if N <= 64 else 128 if N <= 128 else 256   # state width the kernels use
         self.nseq = int(nseq) if seq_idx is not None else 0
         self.dtype = x.dtype
         self.device = dev
@@ -147,6 +148,10 @@ class Problem:
     # shapes of the outputs and intermediates
     def final_shape(self):
         return (self.nseq if self.seq_idx is not None else self.b, self.H, self.P, self.N)
+
+    def cb_shape(self):
+        # per (b, c, g): the Q x Q CB blocks then the Q x NT C blocks, fragment-major
+        return (self.b, self.nc, self.G, self.Q * (self.Q + self.NT))
 
     def empty(self, shape, dtype=None):
         return torch.empty(shape, dtype=dtype or self.dtype, device=self.device)
@@ -210,7 +215,7 @@ def chunk_cumsum(p: Problem, delta=None, cs=None, stream=None):
 
 
 def chunk_cb(p: Problem, cb=None, stream=None):
-    shape = (p.b, p.nc, p.G, p.Q, p.Q)
+    shape = p.cb_shape()
     cb = p.empty(shape) if cb is None else cb
     _check(cb, "cb", p.dtype, shape, p.device)
     p.call("ssd_chunk_cb", _ptr(cb), stream=stream)
@@ -254,6 +259,7 @@ def seq_final_states(p: Problem, delta, cs, states, final_states=None, seg_end=N
 def chunk_scan(p: Problem, delta, cs, cb, states, y=None, stream=None):
     y = p.empty(p.x.shape) if y is None else y
     _check(y, "y", p.dtype, p.x.shape, p.device)
+    _check(cb, "cb", p.dtype, p.cb_shape(), p.device)
     p.args.y = _ptr(y)
     try:
         p.call("ssd_chunk_scan", _ptr(delta), _ptr(cs), _ptr(cb), _ptr(states), stream=stream)

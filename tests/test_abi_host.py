@@ -90,7 +90,8 @@ def test_workspace_size(lib):
     assert lib.ssd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == OK
     nc = 32
     al = lambda v: (v + 255) // 256 * 256
-    want = al(2 * 24 * nc * 64 * 4) * 2 + al(2 * nc * 1 * 64 * 64 * 2) + al(2 * nc * 24 * 64 * 64 * 2)
+    # delta and cs; CB plus the C copy (Q x (Q + 64) per chunk and group); the chunk states
+    want = al(2 * 24 * nc * 64 * 4) * 2 + al(2 * nc * 1 * 64 * (64 + 64) * 2) + al(2 * nc * 24 * 64 * 64 * 2)
     assert n.value == want
     bad = _args(chunk=48)
     assert lib.ssd_fwd_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == CHUNK

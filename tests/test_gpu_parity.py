@@ -265,6 +265,19 @@ def test_nan_isolation_across_chunk_aligned_sequences():
 # per-step pins against oracle intermediates
 # ---------------------------------------------------------------------------
 
+def unpack_cb(buf, Q, NT):
+    """Dense CB [.., Q, Q] and C copy [.., Q, NT] from the chunk_cb buffer
+    [.., Q*(Q+NT)]: each part is 16 x 32 blocks (row block, K block), each block
+    64 lanes x 8, lane = row % 16 + 16 * (column % 32 // 8)."""
+    def dense(m, ncol):
+        lead = m.shape[:-1]
+        m = m.reshape(*lead, Q // 16, ncol // 32, 4, 16, 8)       # rb, kb, lg, li, e
+        n = len(lead)
+        m = m.transpose(*range(n), n, n + 3, n + 1, n + 2, n + 4)  # rb, li, kb, lg, e
+        return m.reshape(*lead, Q, ncol)
+    return dense(buf[..., :Q * Q], Q), dense(buf[..., Q * Q:], NT)
+
+
 def _problem(g, inp):
     return ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states, g.seq_idx,
                        inp.nseq if inp.seq_idx is not None else None, inp.dt_softplus)
@@ -293,14 +306,21 @@ def test_per_step_pins(dtype, Q, packed):
     assert rel(f64(delta), d_ref) < 1e-6
     assert rel(f64(cs), cs_ref) < 1e-6
 
-    # chunk_cb (lower block triangle of 64x64 tiles)
-    cb = ssd.chunk_cb(p)
+    # chunk_cb: CB (lower block triangle of 64x64 tiles) and the C copy, both
+    # fragment-major inside the buffer (layout documented in include/ssd.h)
+    cb = ssd.chunk_cb(p, torch.zeros(p.cb_shape(), dtype=p.dtype, device=p.device))   # upper tiles stay unwritten
     cb_ref = oracle.chunk_cb(inp.B, inp.C, Q)
     torch.cuda.synchronize()
+    cbm, cm = unpack_cb(f64(cb), Q, p.NT)
     ti = np.arange(Q)[:, None] // 64
     si = np.arange(Q)[None, :] // 64
     lower = np.broadcast_to(si <= ti, cb_ref.shape)
-    assert rel(f64(cb)[lower], cb_ref[lower]) < (1e-5 if dtype == "fp32" else 1e-2)
+    assert rel(cbm[lower], cb_ref[lower]) < (1e-5 if dtype == "fp32" else 1e-2)
+    N = inp.B.shape[3]
+    c_pad = np.zeros((b, nc * Q, inp.C.shape[2], p.NT))
+    c_pad[:, :T, :, :N] = f64(inp.C)
+    want_c = c_pad.reshape(b, nc, Q, -1, p.NT).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(cm, want_c)   # a copy: exact, zero past seqlen and N
 
     # chunk_state: each chunk's end state from its own inputs (oracle chunk-local mode)
     states = ssd.chunk_state(p, delta, cs)
