@@ -198,7 +198,7 @@ def main():
     calls = {
         "chunk_cumsum": lambda: ssd.chunk_cumsum(p, delta, cs),
         "chunk_cb": lambda: ssd.chunk_cb(p, cb),
-        "chunk_state": lambda: ssd.chunk_state(p, delta, cs, states),
+        "chunk_state": lambda: ssd.chunk_state(p, delta, cs, cb, states),
         "state_passing": lambda: ssd.state_passing(p, cs, states, None if inp.seq_idx is not None else fin),
         "seq_final": lambda: ssd.seq_final_states(p, delta, cs, states, fin, seg_end),
         "chunk_scan": lambda: ssd.chunk_scan(p, delta, cs, cb, states, ybuf),

@@ -118,15 +118,15 @@ ssd_status ssd_fwd(const ssd_fwd_args *args, void *stream);
  * its workspace fields are ignored.  Intermediate layouts ("E" = the dtype's
  * element type, fp32 or bf16):
  *   delta, cs : [b,H,nc,Q] fp32
- *   cb        : [b,nc,G,Q*(Q+NT)] E, NT = N rounded up to 64 (64, 128 or 256)
+ *   cb        : [b,nc,G,Q*(Q+2*NT)] E, NT = N rounded up to 64 (64, 128 or 256)
  *   states    : [b,nc,H,P,N] E
- * cb holds, per (b, c, g), the Q x Q matrix CB[t][s] and then the chunk's C rows
- * as a Q x NT matrix (rows past seqlen and columns past N zero), both in
+ * cb holds, per (b, c, g), the Q x Q matrix CB[t][s], then the chunk's C rows as
+ * a Q x NT matrix, then B^T as an NT x Q matrix (row n, column s), all in
  * "fragment-major" order: a matrix with NCOL columns is cut into 16-row x
  * 32-column blocks, block (rb, kb) at element (rb*NCOL/32 + kb)*512, and inside a
  * block row r, column k sits at ((r%16) + 16*((k%32)/8))*8 + k%8 (the order in
- * which one wave's matrix-core fragments are read).  Of CB only the 64 x 64
- * tiles with s/64 <= t/64 are written.
+ * which one wave's matrix-core fragments are read).  Rows past seqlen and columns
+ * past N are zero; of CB only the 64 x 64 tiles with s/64 <= t/64 are written.
  */
 
 /* Step 0 ("chunk_cumsum").  delta[t] = softplus(dt[t]) (or dt[t]);
@@ -138,16 +138,17 @@ ssd_status ssd_chunk_cumsum(const ssd_fwd_args *args, float *delta, float *cs, v
 
 /* C B^T of every chunk and group: CB[t][s] = sum_n C[cQ+t,g,n] B[cQ+s,g,n]
  * (the Q K^T of the dual form, formula 1 of "Mamba 2 -- Transformers are SSMs",
- * shared by the heads of a group), plus the copy of C that ssd_chunk_scan reads;
- * layout above. */
+ * shared by the heads of a group), plus the copies of C and B^T that
+ * ssd_chunk_scan and ssd_chunk_state read; layout above. */
 ssd_status ssd_chunk_cb(const ssd_fwd_args *args, void *cb, void *stream);
 
 /* Step 2 ("chunk_state", step 2 of the four-step algorithm): every chunk's end
  * state from its own inputs with a zero start,
  * states[b,c,h,p,n] = sum_{s in chunk c, same segment as the chunk's last token}
- *                      exp(cs_last - cs_s) * delta_s * x_s[p] * B_s[n]. */
+ *                      exp(cs_last - cs_s) * delta_s * x_s[p] * B_s[n].
+ * Reads B through `cb` as left by ssd_chunk_cb. */
 ssd_status ssd_chunk_state(const ssd_fwd_args *args, const float *delta, const float *cs,
-                           void *states, void *stream);
+                           const void *cb, void *states, void *stream);
 
 /* Step 3 ("state_passing", the short scan over chunk states): in place,
  * states[c] := h_{c-1} (the state entering chunk c; h_{-1} = initial_states) where

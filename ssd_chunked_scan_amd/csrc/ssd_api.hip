@@ -143,7 +143,7 @@ Workspace workspace_layout(const Shape &s)
 {
     Workspace w;
     const size_t dcs = (size_t)(s.b * s.H * s.nc * s.Q) * 4;
-    const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * (s.Q + nt_of(s.N))) * s.esz;
+    const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * (s.Q + 2 * nt_of(s.N))) * s.esz;
     const size_t sts = (size_t)(s.b * s.nc * s.H * s.P * s.N) * s.esz;
     w.delta = 0;
     w.cs = align256(w.delta + dcs);
@@ -203,8 +203,8 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
 
 
 template <typename E>
-ssd_status run_state(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, E *states,
-                     hipStream_t st)
+ssd_status run_state(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
+                     E *states, hipStream_t st)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -213,11 +213,11 @@ ssd_status run_state(const Shape &s, const ssd_fwd_args *a, const float *delta, 
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
             if (s.packed)
                 hipLaunchKernelGGL((k_chunk_state<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->x,
-                                   (const E *)a->B, delta, cs, a->seq_idx, states, (int)s.T, (int)s.H, (int)s.G,
+                                   cb, delta, cs, a->seq_idx, states, (int)s.T, (int)s.H, (int)s.G,
                                    (int)s.P, (int)s.N, (int)s.nc, ntp);
             else
                 hipLaunchKernelGGL((k_chunk_state<E, Q, NT, false>), grid, dim3(kThreads), 0, st,
-                                   (const E *)a->x, (const E *)a->B, delta, cs, a->seq_idx, states, (int)s.T,
+                                   (const E *)a->x, cb, delta, cs, a->seq_idx, states, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
             return launched();
         });
@@ -302,7 +302,7 @@ ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, 
     ssd_status r;
     if ((r = run_cumsum<E>(s, a, delta, cs, st)) != SSD_OK) return r;
     if ((r = run_cb<E>(s, a, cb, st)) != SSD_OK) return r;
-    if ((r = run_state<E>(s, a, delta, cs, states, st)) != SSD_OK) return r;
+    if ((r = run_state<E>(s, a, delta, cs, cb, states, st)) != SSD_OK) return r;
     if ((r = run_passing<E>(s, a, cs, states, s.packed ? nullptr : a->final_states, st)) != SSD_OK) return r;
     if (s.packed && a->final_states)
         if ((r = run_seq_final<E>(s, a, delta, cs, states, seg_end, st)) != SSD_OK) return r;
@@ -395,19 +395,19 @@ ssd_status ssd_chunk_cb(const ssd_fwd_args *args, void *cb, void *stream)
                                      : run_cb<float>(s, args, (float *)cb, st);
 }
 
-ssd_status ssd_chunk_state(const ssd_fwd_args *args, const float *delta, const float *cs, void *states,
-                           void *stream)
+ssd_status ssd_chunk_state(const ssd_fwd_args *args, const float *delta, const float *cs, const void *cb,
+                           void *states, void *stream)
 {
     Shape s;
     ssd_status r = parse_shape(args, &s);
     if (r != SSD_OK) return r;
     if ((r = check_pointers(args, s, kNeedX | kNeedB)) != SSD_OK) return r;
     if (s.T == 0) return SSD_OK;
-    if (!delta || !cs || !states) return SSD_ERR_NULL_POINTER;
-    if (!aligned16(delta) || !aligned16(cs) || !aligned16(states)) return SSD_ERR_MISALIGNED;
+    if (!delta || !cs || !cb || !states) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(delta) || !aligned16(cs) || !aligned16(cb) || !aligned16(states)) return SSD_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return s.dtype == SSD_DTYPE_BF16 ? run_state<bf16>(s, args, delta, cs, (bf16 *)states, st)
-                                     : run_state<float>(s, args, delta, cs, (float *)states, st);
+    return s.dtype == SSD_DTYPE_BF16 ? run_state<bf16>(s, args, delta, cs, (const bf16 *)cb, (bf16 *)states, st)
+                                     : run_state<float>(s, args, delta, cs, (const float *)cb, (float *)states, st);
 }
 
 ssd_status ssd_state_passing(const ssd_fwd_args *args, const float *cs, void *states, void *stream)

@@ -116,16 +116,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
 // fetches a fragment as one contiguous 1 KB (bf16) per wave instead of 16 rows x
 // 64 bytes.  Per (b, c, g) the chunk_cb buffer holds the Q x Q matrix CB[t][s] =
 // sum_n C[t][n] B[s][n] (only the 64 x 64 tiles with s-tile <= t-tile are
-// written) followed by the chunk's C rows as a Q x NT matrix (rows past the
-// sequence end and columns past N are zero).
-template <int Q, int NT> constexpr int64_t cb_group_elems() { return (int64_t)Q * Q + (int64_t)Q * NT; }
+// written), then the chunk's C rows as a Q x NT matrix, then B^T as an NT x Q
+// matrix (rows n, columns s) for chunk_state; rows past the sequence end and
+// columns past N are zero.
+template <int Q, int NT> constexpr int64_t cb_group_elems() { return (int64_t)Q * Q + 2 * (int64_t)Q * NT; }
 
 // One workgroup per 64x64 (t, s) tile with s-tile <= t-tile.  The B rows of the
 // s-tile and the C rows of the t-tile are loaded with row-contiguous 16-byte
 // loads into LDS (row pitch 32 bytes past a multiple of 256, which keeps the
 // 16-byte fragment reads conflict-free); each wave computes 32x32 as D[s][t]
 // (A = B rows, B = C rows, K = n).  The result goes through LDS to leave in
-// fragment-major order; the tiles of the first s-tile also copy their C rows.
+// fragment-major order; the tiles of the first s-tile also copy their C rows,
+// and the diagonal tiles write B^T of their s rows.
 template <typename E, int Q, int NT>
 __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm, const E *__restrict__ Cm,
                                                        E *__restrict__ cbuf, int T, int G, int N, int nc)
@@ -188,6 +190,29 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm,
             const int rb = blk / NKS, kb = blk % NKS;
             const F v = load_frag(csm + (16 * rb + li) * PITCH + kb * 32 + 8 * lg);
             store_frag(cf + ((int64_t)((4 * ti + rb) * NKS + kb) * 64 + lane) * 8, v);
+        }
+    }
+    if (si == ti) {
+        // B^T of this s-tile, fragment-major: NT/16 row blocks (n) x 2 K steps (s);
+        // lane (li, lg) needs column n = 16 nb + li over rows s = 32 kb + 8 lg ..
+        // +7: in bf16 two transposing reads (rows +0..3, +4..7; lane j of each
+        // 16-lane group points at row j/4, columns 4 (j%4) ..), in fp32 8 reads
+        E *bt = group + (int64_t)Q * Q + (int64_t)Q * NT;
+#pragma unroll
+        for (int blk = wave; blk < (NT / 16) * 2; blk += 4) {
+            const int nb = blk >> 1, kb = blk & 1;
+            F v;
+            if constexpr (sizeof(E) == 2) {
+                typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+                E *q = bs + (32 * kb + 8 * lg + (li >> 2)) * PITCH + 16 * nb + 4 * (li & 3);
+                const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)q);
+                const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(q + 4 * PITCH));
+                v = __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = bs[(32 * kb + 8 * lg + e) * PITCH + 16 * nb + li];
+            }
+            store_frag(bt + ((int64_t)(nb * (Q / 32) + 2 * si + kb) * 64 + lane) * 8, v);
         }
     }
 
@@ -547,15 +572,26 @@ __device__ __forceinline__ void store_state_tile(E *stage, const floatx4 (&acc)[
 
 // chunk_state: states[b,c,h,p,n] = sum_s w_s x_s[p] B_s[n], w_s = exp(cs_last -
 // cs_s) delta_s for s in the segment of the chunk's last token (0 elsewhere).
-// One workgroup per (b, c, h, 64-p tile).
+// One workgroup per (b, c, h, 64-p tile).  The weighted x tile of all Q tokens
+// is staged in LDS once (its K index, time, read back transposed); the B^T
+// fragments (rows n, K = s) are streamed fragment-major from the chunk_cb
+// buffer, RING K steps ahead, one contiguous block per wave and step.  Wave w
+// owns n rows w*NT/4 .. +NT/4 of D[n][p] (A = B^T, B = (w x)^T):
+//   acc[i][j][r]  <->  n = w*NT/4 + i*16 + 4*(lane/16) + r,  p = j*16 + lane%16.
 template <typename E, int Q, int NT, bool PACKED>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
-    const E *__restrict__ x, const E *__restrict__ Bm, const float *__restrict__ delta,
+    const E *__restrict__ x, const E *__restrict__ cbuf, const float *__restrict__ delta,
     const float *__restrict__ cs, const int32_t *__restrict__ seq_idx, E *__restrict__ states,
     int T, int H, int G, int P, int N, int nc, int ntp)
 {
+    using F = frag_t<E>;
+    using XT = KTile<E, Q, 64>;
     constexpr int NI = NT / 64;
-    __shared__ __align__(16) StateSmem<E, NT> sm;
+    constexpr int NKS = Q / 32;
+    constexpr int RING = 3;
+    constexpr int ES = (int)sizeof(E);
+    constexpr int XSZ = XT::SIZE > 64 * NT ? XT::SIZE : 64 * NT;   // the x tile, then the result
+    __shared__ __align__(16) E xt[XSZ];
     __shared__ float w[Q];
     __shared__ int m[Q];
     const int units = nc * H * ntp;
@@ -567,17 +603,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
     const int g = h / (H / G);
     const int t0 = c * Q, len = min(Q, T - t0);
     const int p0 = tp * 64;
-    const E *xsrc = x + (((int64_t)b * T + t0) * H + h) * P + p0;
-    const E *bsrc = Bm + (((int64_t)b * T + t0) * G + g) * N;
-    const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
-    using XT = typename StateSmem<E, NT>::XT;
-    using BT = typename StateSmem<E, NT>::BT;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+
+    const int64_t ldx = (int64_t)H * P;
     XT xs;
-    BT bs;
     xs.init(ldx, P - p0);
-    bs.init(ldb, N);
-    xs.load(XT::rsrc(xsrc, ldx, len));
-    bs.load(BT::rsrc(bsrc, ldb, len));
+    xs.load(XT::rsrc(x + (((int64_t)b * T + t0) * H + h) * P + p0, ldx, len));
+
+    // B^T fragments of this chunk and group; K steps past the sequence end are skipped
+    const E *group = cbuf + (((int64_t)b * nc + c) * G + g) * cb_group_elems<Q, NT>();
+    const auto brs = make_rsrc(group + (int64_t)Q * Q + (int64_t)Q * NT, (int64_t)NT * Q * ES);
+    constexpr uint32_t BLK = 512 * ES;   // bytes per fragment block
+    const int kend = (len + 31) / 32;
+    uint32_t bbase[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) bbase[i] = (uint32_t)((wave * NI + i) * NKS) * BLK + lane * 8 * ES;
+    auto b_off = [&](int i, int ks) -> uint32_t { return ks < kend ? bbase[i] + (uint32_t)ks * BLK : kOffNone; };
+    F ra[RING][NI];
+#pragma unroll
+    for (int r = 0; r < RING; ++r)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            if (r < NKS) bload_frag(brs, b_off(i, r), ra[r][i]);
+            else ra[r][i] = F{};
+        }
 
     const int64_t cso = (((int64_t)b * H + h) * nc + c) * Q;
     const float lam = cs[cso + len - 1];
@@ -588,15 +638,37 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
         w[s] = keep ? exp_neg(lam - cs[cso + s]) * delta[cso + s] : 0.f;
     }
     __syncthreads();
+    xs.template store<true, PACKED>(xt, w, m);
+    __syncthreads();
+
     floatx4 acc[NI][4];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    state_product<E, NT, PACKED>(sm, xsrc, ldx, bsrc, ldb, len, w, m, xs, bs, acc);
+    typename XT::Off xoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xoff[j] = XT::frag_off(j * 16);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (ks < kend) {   // wave-uniform
+            F bx[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bx[j] = XT::frag_at(xt, xoff[j], ks * 32);
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mma(acc[i][j], ra[ks % RING][i], bx[j]);
+        }
+        if (ks + RING < NKS) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) bload_frag(brs, b_off(i, ks + RING), ra[ks % RING][i]);
+        }
+    }
 
+    __syncthreads();   // the x tile is no longer read: its memory stages the result
     E *out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-    store_state_tile<E, NT>(sm.b, acc, out + (int64_t)p0 * N, P - p0, N);
+    store_state_tile<E, NT>(xt, acc, out + (int64_t)p0 * N, P - p0, N);
 }
 
 // ---------------------------------------------------------------------------

@@ -70,7 +70,7 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_fwd.argtypes = [P, vp]
     lib.ssd_chunk_cumsum.argtypes = [P, vp, vp, vp]
     lib.ssd_chunk_cb.argtypes = [P, vp, vp]
-    lib.ssd_chunk_state.argtypes = [P, vp, vp, vp, vp]
+    lib.ssd_chunk_state.argtypes = [P, vp, vp, vp, vp, vp]
     lib.ssd_state_passing.argtypes = [P, vp, vp, vp]
     lib.ssd_seq_final_states.argtypes = [P, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp]
@@ -150,8 +150,8 @@ class Problem:
         return (self.nseq if self.seq_idx is not None else self.b, self.H, self.P, self.N)
 
     def cb_shape(self):
-        # per (b, c, g): the Q x Q CB blocks then the Q x NT C blocks, fragment-major
-        return (self.b, self.nc, self.G, self.Q * (self.Q + self.NT))
+        # per (b, c, g): CB (Q x Q), C (Q x NT) and B^T (NT x Q), fragment-major
+        return (self.b, self.nc, self.G, self.Q * (self.Q + 2 * self.NT))
 
     def empty(self, shape, dtype=None):
         return torch.empty(shape, dtype=dtype or self.dtype, device=self.device)
@@ -222,11 +222,12 @@ def chunk_cb(p: Problem, cb=None, stream=None):
     return cb
 
 
-def chunk_state(p: Problem, delta, cs, states=None, stream=None):
+def chunk_state(p: Problem, delta, cs, cb, states=None, stream=None):
     shape = (p.b, p.nc, p.H, p.P, p.N)
     states = p.empty(shape) if states is None else states
+    _check(cb, "cb", p.dtype, p.cb_shape(), p.device)
     _check(states, "states", p.dtype, shape, p.device)
-    p.call("ssd_chunk_state", _ptr(delta), _ptr(cs), _ptr(states), stream=stream)
+    p.call("ssd_chunk_state", _ptr(delta), _ptr(cs), _ptr(cb), _ptr(states), stream=stream)
     return states
 
 

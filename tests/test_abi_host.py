@@ -90,8 +90,8 @@ def test_workspace_size(lib):
     assert lib.ssd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == OK
     nc = 32
     al = lambda v: (v + 255) // 256 * 256
-    # delta and cs; CB plus the C copy (Q x (Q + 64) per chunk and group); the chunk states
-    want = al(2 * 24 * nc * 64 * 4) * 2 + al(2 * nc * 1 * 64 * (64 + 64) * 2) + al(2 * nc * 24 * 64 * 64 * 2)
+    # delta and cs; CB plus the C and B^T copies (Q x (Q + 2 * 64) per chunk and group); the chunk states
+    want = al(2 * 24 * nc * 64 * 4) * 2 + al(2 * nc * 1 * 64 * (64 + 2 * 64) * 2) + al(2 * nc * 24 * 64 * 64 * 2)
     assert n.value == want
     bad = _args(chunk=48)
     assert lib.ssd_fwd_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == CHUNK
@@ -103,7 +103,8 @@ def test_step_entry_points_validate(lib):
     assert lib.ssd_chunk_cumsum(ctypes.byref(a), None, p(0x90000000), None) == NULLP
     assert lib.ssd_chunk_cumsum(ctypes.byref(a), p(0x90000004), p(0x90000000), None) == MISAL
     assert lib.ssd_chunk_cb(ctypes.byref(a), None, None) == NULLP
-    assert lib.ssd_chunk_state(ctypes.byref(a), p(0x90000000), None, p(0xa0000000), None) == NULLP
+    assert lib.ssd_chunk_state(ctypes.byref(a), p(0x90000000), None, p(0xb0000000), p(0xa0000000), None) == NULLP
+    assert lib.ssd_chunk_state(ctypes.byref(a), p(0x90000000), p(0x98000000), None, p(0xa0000000), None) == NULLP
     assert lib.ssd_state_passing(ctypes.byref(a), None, p(0xa0000000), None) == NULLP
     assert lib.ssd_chunk_scan(ctypes.byref(a), p(1 << 33), p(2 << 33), None, p(3 << 33), None) == NULLP
     # seq_final_states only makes sense for a packed stream

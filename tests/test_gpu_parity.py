@@ -266,16 +266,18 @@ def test_nan_isolation_across_chunk_aligned_sequences():
 # ---------------------------------------------------------------------------
 
 def unpack_cb(buf, Q, NT):
-    """Dense CB [.., Q, Q] and C copy [.., Q, NT] from the chunk_cb buffer
-    [.., Q*(Q+NT)]: each part is 16 x 32 blocks (row block, K block), each block
-    64 lanes x 8, lane = row % 16 + 16 * (column % 32 // 8)."""
-    def dense(m, ncol):
+    """Dense CB [.., Q, Q], C copy [.., Q, NT] and B^T copy [.., NT, Q] from the
+    chunk_cb buffer [.., Q*(Q+2*NT)]: each part is 16 x 32 blocks (row block, K
+    block), each block 64 lanes x 8, lane = row % 16 + 16 * (column % 32 // 8)."""
+    def dense(m, nrow, ncol):
         lead = m.shape[:-1]
-        m = m.reshape(*lead, Q // 16, ncol // 32, 4, 16, 8)       # rb, kb, lg, li, e
+        m = m.reshape(*lead, nrow // 16, ncol // 32, 4, 16, 8)    # rb, kb, lg, li, e
         n = len(lead)
         m = m.transpose(*range(n), n, n + 3, n + 1, n + 2, n + 4)  # rb, li, kb, lg, e
-        return m.reshape(*lead, Q, ncol)
-    return dense(buf[..., :Q * Q], Q), dense(buf[..., Q * Q:], NT)
+        return m.reshape(*lead, nrow, ncol)
+    qq, qn = Q * Q, Q * NT
+    return (dense(buf[..., :qq], Q, Q), dense(buf[..., qq:qq + qn], Q, NT),
+            dense(buf[..., qq + qn:], NT, Q))
 
 
 def _problem(g, inp):
@@ -311,7 +313,7 @@ def test_per_step_pins(dtype, Q, packed):
     cb = ssd.chunk_cb(p, torch.zeros(p.cb_shape(), dtype=p.dtype, device=p.device))   # upper tiles stay unwritten
     cb_ref = oracle.chunk_cb(inp.B, inp.C, Q)
     torch.cuda.synchronize()
-    cbm, cm = unpack_cb(f64(cb), Q, p.NT)
+    cbm, cm, btm = unpack_cb(f64(cb), Q, p.NT)
     ti = np.arange(Q)[:, None] // 64
     si = np.arange(Q)[None, :] // 64
     lower = np.broadcast_to(si <= ti, cb_ref.shape)
@@ -321,9 +323,13 @@ def test_per_step_pins(dtype, Q, packed):
     c_pad[:, :T, :, :N] = f64(inp.C)
     want_c = c_pad.reshape(b, nc, Q, -1, p.NT).transpose(0, 1, 3, 2, 4)
     assert np.array_equal(cm, want_c)   # a copy: exact, zero past seqlen and N
+    b_pad = np.zeros_like(c_pad)
+    b_pad[:, :T, :, :N] = f64(inp.B)
+    want_bt = b_pad.reshape(b, nc, Q, -1, p.NT).transpose(0, 1, 3, 4, 2)
+    assert np.array_equal(btm, want_bt)
 
     # chunk_state: each chunk's end state from its own inputs (oracle chunk-local mode)
-    states = ssd.chunk_state(p, delta, cs)
+    states = ssd.chunk_state(p, delta, cs, cb)
     loc = run_oracle(inp, chunk=Q, chunk_local=True, want_chunk_states=True)
     torch.cuda.synchronize()
     sg = f64(states)
