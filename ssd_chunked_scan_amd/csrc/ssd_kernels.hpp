@@ -675,45 +675,76 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
 // state_passing: in place S_c -> h_{c-1}; h_c = exp(cs_last(c)) h_{c-1} + S_c
 // ---------------------------------------------------------------------------
 // Every (b, h, p, n) element is an independent length-nc scan.  Each thread owns
-// 4 consecutive elements and walks the chunks with a ring of kPrefetch loads in
-// flight: the slot a chunk's state is read from is refilled with the state
-// kPrefetch chunks ahead before the arithmetic.  The carry is replaced by zero
-// (a select) when the chunk holds a segment boundary.
-constexpr int kPrefetch = 16;
+// VE consecutive elements (8 or 4 bf16, 4 fp32: 16 or 8 bytes) and walks the
+// chunks with a ring of kPrefetch loads in flight: the slot a chunk's state is
+// read from is refilled with the state kPrefetch chunks ahead before the
+// arithmetic.  The carry is replaced by zero (a select) when the chunk holds a
+// segment boundary.
+constexpr int kPrefetch = 32;
 
-template <typename E> struct Raw4;
-template <> struct Raw4<bf16> { using type = uint2; };
-template <> struct Raw4<float> { using type = uint4; };
+template <typename E, int VE> struct RawVec;
+template <> struct RawVec<bf16, 4> { using type = uint2; };
+template <> struct RawVec<bf16, 8> { using type = uint4; };
+template <> struct RawVec<float, 4> { using type = uint4; };
 
-__device__ __forceinline__ void unpack4(const uint2 &v, float *o)
+__device__ __forceinline__ void unpack_raw(const uint2 &v, float *o)
 {
     o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
     o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
 }
-__device__ __forceinline__ void unpack4(const uint4 &v, float *o)
+template <typename E> __device__ __forceinline__ void unpack_raw(const uint4 &v, float *o);
+template <> __device__ __forceinline__ void unpack_raw<float>(const uint4 &v, float *o)
 {
     o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
     o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
 }
+template <> __device__ __forceinline__ void unpack_raw<bf16>(const uint4 &v, float *o)
+{
+    unpack_raw(uint2{v.x, v.y}, o);
+    unpack_raw(uint2{v.z, v.w}, o + 4);
+}
+template <typename E, int VE> __device__ __forceinline__ void unpack_vec(const typename RawVec<E, VE>::type &v, float *o)
+{
+    if constexpr (sizeof(v) == 8) unpack_raw(v, o);
+    else unpack_raw<E>(v, o);
+}
+template <int VE> __device__ __forceinline__ void store_vec(float *p, const float *v) { store16_f32(p, v); }
+template <int VE> __device__ __forceinline__ void store_vec(bf16 *p, const float *v)
+{
+    if constexpr (VE == 8) store16_f32(p, v);
+    else store4_f32(p, v);
+}
+template <int VE> __device__ __forceinline__ void load_init(const float *p, float *v)
+{
+#pragma unroll
+    for (int i = 0; i < VE; i += 4) load4_f32(p + i, v + i);
+}
+template <int VE> __device__ __forceinline__ void store_final(float *p, const float *v)
+{
+#pragma unroll
+    for (int i = 0; i < VE; i += 4) store4_f32(p + i, v + i);
+}
 
-template <typename E>
+template <typename E, int VE>
 __global__ __launch_bounds__(kThreads) void k_state_passing(
     E *__restrict__ states, const float *__restrict__ cs, const float *__restrict__ init,
     float *__restrict__ final_states, const int32_t *__restrict__ seq_idx,
     int T, int H, int64_t PN, int nc, int Q, int64_t total_vecs)
 {
-    using R = typename Raw4<E>::type;
+    using R = typename RawVec<E, VE>::type;
     constexpr int D = kPrefetch;   // divides 64
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= total_vecs) return;
     const int lane = threadIdx.x & 63;
-    const int64_t vph = PN / 4;   // a multiple of 64: every wave lies inside one (b, h)
+    const int64_t vph = PN / VE;   // a multiple of 64: every wave lies inside one (b, h)
     const int bh = __builtin_amdgcn_readfirstlane((int)(gid / vph));
-    const int64_t e0 = (gid - (int64_t)bh * vph) * 4;
+    const int64_t e0 = (gid - (int64_t)bh * vph) * VE;
     const int h = bh % H;
     const int b = bh / H;
-    float hs[4] = {0.f, 0.f, 0.f, 0.f};
-    if (init) load4_f32(init + (int64_t)bh * PN + e0, hs);
+    float hs[VE];
+#pragma unroll
+    for (int v = 0; v < VE; ++v) hs[v] = 0.f;
+    if (init) load_init<VE>(init + (int64_t)bh * PN + e0, hs);
     const float *lamp = cs + (int64_t)bh * nc * Q + (Q - 1);   // cs at each chunk's last position
     const int64_t cstride = (int64_t)H * PN;
     E *lane_base = states + ((int64_t)b * nc * H + h) * PN + e0;
@@ -732,22 +763,22 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
             for (int j = 0; j < D; ++j) {
                 const int c = cb + k0 + j;
                 if (c < nc) {
-                    float sv[4];
-                    unpack4(buf[j], sv);
+                    float sv[VE];
+                    unpack_vec<E, VE>(buf[j], sv);
                     if (c + D < nc) buf[j] = *reinterpret_cast<const R *>(lane_base + (int64_t)(c + D) * cstride);
-                    store4_f32(lane_base + (int64_t)c * cstride, hs);
+                    store_vec<VE>(lane_base + (int64_t)c * cstride, hs);
                     const float lm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lamv), k0 + j));
                     const int sc = __builtin_amdgcn_readlane(slv, k0 + j);
                     const bool keep = !seq_idx || sc == sprev;
                     sprev = sc;
                     const float d = exp_neg(lm);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
+                    for (int v = 0; v < VE; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
                 }
             }
         }
     }
-    if (final_states) store4_f32(final_states + (int64_t)bh * PN + e0, hs);
+    if (final_states) store_final<VE>(final_states + (int64_t)bh * PN + e0, hs);
 }
 
 // ---------------------------------------------------------------------------
