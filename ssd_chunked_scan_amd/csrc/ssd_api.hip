@@ -160,14 +160,6 @@ unsigned grid1(int64_t n, int threads) { return (unsigned)((n + threads - 1) / t
 
 // ---- per-step launches (typed) ----
 
-template <typename E>
-ssd_status run_cumsum(const Shape &s, const ssd_fwd_args *a, float *delta, float *cs, hipStream_t st)
-{
-    dim3 grid((unsigned)s.nc, (unsigned)((s.H + kCumsumHeads - 1) / kCumsumHeads), (unsigned)s.b);
-    hipLaunchKernelGGL(k_chunk_cumsum<E>, grid, dim3(kThreads), 0, st, (const E *)a->dt, a->A, a->seq_idx,
-                       delta, cs, (int)s.T, (int)s.H, (int)s.Q, (int)s.nc, (int)a->dt_softplus);
-    return launched();
-}
 
 // The state kernels cover all of N in one workgroup: NT = N rounded up to 64.
 template <typename F>
@@ -184,6 +176,15 @@ ssd_status with_q(int64_t Q, F &&f)
     if (Q == 64) return f(std::integral_constant<int, 64>{});
     if (Q == 128) return f(std::integral_constant<int, 128>{});
     return f(std::integral_constant<int, 256>{});
+}
+
+template <typename E>
+ssd_status run_cumsum(const Shape &s, const ssd_fwd_args *a, float *delta, float *cs, hipStream_t st)
+{
+    dim3 grid((unsigned)s.nc, (unsigned)((s.H + kCumsumHeads - 1) / kCumsumHeads), (unsigned)s.b);
+    hipLaunchKernelGGL(k_chunk_cumsum<E>, grid, dim3(kThreads), 0, st, (const E *)a->dt, a->A, a->seq_idx,
+                       delta, cs, (int)s.T, (int)s.H, (int)s.Q, (int)s.nc, (int)a->dt_softplus);
+    return launched();
 }
 
 template <typename E>

@@ -26,10 +26,17 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 constexpr int kCumsumHeads = 4;   // one wave per head
 
+// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(u) with u = e^-|z| in (0, 1],
+// from the hardware base-2 exponential and logarithm.  log1p(u) is taken as
+// log(w) u / (w - 1) with w = fl(1 + u): w - 1 is exact, and the quotient
+// cancels the rounding of 1 + u, so the result keeps a few-ulp relative error
+// however small u is (w == 1 means u is below half an ulp of 1: log1p(u) = u).
 __device__ __forceinline__ float softplus_f(float z)
 {
-    // log(1 + e^z); above 20 the correction e^-z is below 2e-9 relative.
-    return z > 20.f ? z : log1pf(expf(z));
+    const float u = __builtin_amdgcn_exp2f(-fabsf(z) * kLog2e);
+    const float w = 1.f + u;
+    const float l1p = w == 1.f ? u : __builtin_amdgcn_logf(w) * 0.6931471805599453f * (u / (w - 1.f));
+    return fmaxf(z, 0.f) + l1p;
 }
 
 // Grid (nc, ceil(H/4), b): one wave per (chunk, head).  Every lane owns Q/64
