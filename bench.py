@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the chunked SSD forward pass on one MI355X.
 
-One step = one full forward pass (chunk_cumsum, chunk_cb, chunk_state,
-state_passing, [seq_final], chunk_scan) over one batch of seeded synthetic
+One step = one full forward pass (chunk_cb, chunk_state with the cumsum step
+inside, state_passing, [seq_final], chunk_scan) over one batch of seeded synthetic
 input already resident in HBM.  Prints ONE JSON line:
 
   value        whole-job tokens/s over the K timed steps (wall clock, synchronised)
@@ -78,8 +78,9 @@ def algorithmic_work(shape, esz, packed):
         "chunk_cumsum": dict(bound="hbm", bytes=b * T * H * esz + H * 4 + dcs),
         "chunk_cb": dict(bound="mfma", flops=2.0 * b * nc * Q * G * Q * N * causal,
                          bytes=2 * b * T * G * N * esz + cbb),
+        # chunk_state runs the cumsum step too: it reads dt and writes delta and cs
         "chunk_state": dict(bound="mfma", flops=2.0 * b * T * H * P * N,
-                            bytes=b * T * H * P * esz + b * T * G * N * esz + dcs + st),
+                            bytes=b * T * H * P * esz + b * T * G * N * esz + b * T * H * esz + dcs + st),
         "state_passing": dict(bound="hbm", bytes=2 * st + b * H * nc * 4 + 2 * b * H * P * N * 4),
         "chunk_scan": dict(bound="mfma",
                            flops=2.0 * b * T * H * P * Q * causal + 2.0 * b * T * H * N * P,
@@ -129,8 +130,9 @@ def run_cpu_baseline(inp, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # a forward is ~0.1 ms: enough steps that clocks and queues settle (still milliseconds)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
@@ -185,7 +187,7 @@ def main():
     # per-kernel breakdown: the same kernels through the per-step entry points,
     # bracketed by HIP events on the stream they are launched on
     stream = torch.cuda.current_stream(dev)
-    names = ["chunk_cumsum", "chunk_cb", "chunk_state", "state_passing"]
+    names = ["chunk_cb", "chunk_state", "state_passing"]   # the kernels ssd_fwd launches
     if inp.seq_idx is not None:
         names.append("seq_final")
     names.append("chunk_scan")

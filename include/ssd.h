@@ -146,9 +146,11 @@ ssd_status ssd_chunk_cb(const ssd_fwd_args *args, void *cb, void *stream);
  * state from its own inputs with a zero start,
  * states[b,c,h,p,n] = sum_{s in chunk c, same segment as the chunk's last token}
  *                      exp(cs_last - cs_s) * delta_s * x_s[p] * B_s[n].
- * Reads B through `cb` as left by ssd_chunk_cb. */
-ssd_status ssd_chunk_state(const ssd_fwd_args *args, const float *delta, const float *cs,
-                           const void *cb, void *states, void *stream);
+ * It runs step 0 itself: delta and cs are OUTPUTS here, written with the same
+ * values ssd_chunk_cumsum produces (ssd_fwd launches no separate cumsum).  Reads
+ * B through `cb` as left by ssd_chunk_cb. */
+ssd_status ssd_chunk_state(const ssd_fwd_args *args, float *delta, float *cs, const void *cb, void *states,
+                           void *stream);
 
 /* Step 3 ("state_passing", the short scan over chunk states): in place,
  * states[c] := h_{c-1} (the state entering chunk c; h_{-1} = initial_states) where

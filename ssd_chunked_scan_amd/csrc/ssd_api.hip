@@ -204,22 +204,21 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
 
 
 template <typename E>
-ssd_status run_state(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
-                     E *states, hipStream_t st)
+ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float *cs, const E *cb, E *states,
+                     hipStream_t st)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
     return with_q(s.Q, [&](auto q) {
         return with_nt(s.N, [&](auto nt) {
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
-            if (s.packed)
-                hipLaunchKernelGGL((k_chunk_state<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->x,
-                                   cb, delta, cs, a->seq_idx, states, (int)s.T, (int)s.H, (int)s.G,
-                                   (int)s.P, (int)s.N, (int)s.nc, ntp);
-            else
-                hipLaunchKernelGGL((k_chunk_state<E, Q, NT, false>), grid, dim3(kThreads), 0, st,
-                                   (const E *)a->x, cb, delta, cs, a->seq_idx, states, (int)s.T,
-                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
+            auto launch = [&](auto kern) {
+                hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, (const E *)a->x, cb, (const E *)a->dt, a->A,
+                                   a->seq_idx, delta, cs, states, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
+                                   (int)s.nc, ntp, (int)a->dt_softplus);
+            };
+            if (s.packed) launch(k_chunk_state<E, Q, NT, true>);
+            else launch(k_chunk_state<E, Q, NT, false>);
             return launched();
         });
     });
@@ -309,8 +308,7 @@ ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, 
     E *states = reinterpret_cast<E *>(ws + w.states);
     int32_t *seg_end = reinterpret_cast<int32_t *>(ws + w.seg_end);
     ssd_status r;
-    if ((r = run_cumsum<E>(s, a, delta, cs, st)) != SSD_OK) return r;
-    if ((r = run_cb<E>(s, a, cb, st)) != SSD_OK) return r;
+    if ((r = run_cb<E>(s, a, cb, st)) != SSD_OK) return r;   // the cumsum step runs inside chunk_state
     if ((r = run_state<E>(s, a, delta, cs, cb, states, st)) != SSD_OK) return r;
     if ((r = run_passing<E>(s, a, cs, states, s.packed ? nullptr : a->final_states, st)) != SSD_OK) return r;
     if (s.packed && a->final_states)
@@ -404,13 +402,13 @@ ssd_status ssd_chunk_cb(const ssd_fwd_args *args, void *cb, void *stream)
                                      : run_cb<float>(s, args, (float *)cb, st);
 }
 
-ssd_status ssd_chunk_state(const ssd_fwd_args *args, const float *delta, const float *cs, const void *cb,
-                           void *states, void *stream)
+ssd_status ssd_chunk_state(const ssd_fwd_args *args, float *delta, float *cs, const void *cb, void *states,
+                           void *stream)
 {
     Shape s;
     ssd_status r = parse_shape(args, &s);
     if (r != SSD_OK) return r;
-    if ((r = check_pointers(args, s, kNeedX | kNeedB)) != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB)) != SSD_OK) return r;
     if (s.T == 0) return SSD_OK;
     if (!delta || !cs || !cb || !states) return SSD_ERR_NULL_POINTER;
     if (!aligned16(delta) || !aligned16(cs) || !aligned16(cb) || !aligned16(states)) return SSD_ERR_MISALIGNED;

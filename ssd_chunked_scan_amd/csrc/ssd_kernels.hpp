@@ -39,34 +39,66 @@ __device__ __forceinline__ float softplus_f(float z)
     return fmaxf(z, 0.f) + l1p;
 }
 
-// Grid (nc, ceil(H/4), b): one wave per (chunk, head).  Every lane owns Q/64
-// consecutive tokens, sums them sequentially, and a segmented wave scan (a
-// segment restarts at a packed-sequence boundary) combines the lanes.  Sums run
-// in fp64 and are rounded once, so a stored cs carries a single rounding.
-template <typename E>
-__global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
-    const E *__restrict__ dt, const float *__restrict__ A, const int32_t *__restrict__ seq_idx,
-    float *__restrict__ delta, float *__restrict__ cs, int T, int H, int Q, int nc, int softplus)
+// Inclusive segmented scan over the 64 lanes of a wave: lane i ends with the
+// sum of v over lanes j <= i back to (and including) the nearest lane whose
+// flag is set, and f = whether any lane in 0..i has it.  Hillis-Steele steps
+// with DPP moves: shifts by 1, 2, 4, 8 inside each 16-lane row (a lane with no
+// source reads the identity (0, 0)), then row 15's last lane into row 1 and 3,
+// and lane 31 into rows 2 and 3.  A double moves as two 32-bit halves.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dpp_seg_step(double &v, int &f)
 {
-    const int c = blockIdx.x, b = blockIdx.z;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int h = blockIdx.y * kCumsumHeads + wave;
-    if (h >= H) return;   // whole wave; no barriers below
+    const int64_t bits = __builtin_bit_cast(int64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)bits, CTRL, ROWS, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(bits >> 32), CTRL, ROWS, 0xf, true);
+    const int fo = __builtin_amdgcn_update_dpp(0, f, CTRL, ROWS, 0xf, true);
+    const double vo = __builtin_bit_cast(double, ((int64_t)hi << 32) | (uint32_t)lo);
+    v = f ? v : v + vo;
+    f |= fo;
+}
+__device__ __forceinline__ void wave_segmented_scan(double &v, int &f)
+{
+    dpp_seg_step<0x111, 0xf>(v, f);   // row_shr:1
+    dpp_seg_step<0x112, 0xf>(v, f);   // row_shr:2
+    dpp_seg_step<0x114, 0xf>(v, f);   // row_shr:4
+    dpp_seg_step<0x118, 0xf>(v, f);   // row_shr:8
+    dpp_seg_step<0x142, 0xa>(v, f);   // row_bcast:15 into rows 1 and 3
+    dpp_seg_step<0x143, 0xc>(v, f);   // row_bcast:31 into rows 2 and 3
+}
+
+// The loads of chunk_cumsum_wave (issued early by callers that have other
+// loads to overlap): raw dt (softplus not yet applied) and sequence ids.
+template <typename E>
+__device__ __forceinline__ void chunk_cumsum_load(const E *__restrict__ dt, const int32_t *__restrict__ seq_idx,
+                                                  int b, int c, int h, int T, int H, int Q, float (&zv)[4],
+                                                  int (&sv)[4])
+{
+    const int lane = threadIdx.x & 63;
     const int t0 = c * Q;
-    const int per = Q >> 6;   // 1, 2 or 4 tokens per lane
-    float dv[4];
-    int sv[4];
+    const int per = Q >> 6;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        dv[j] = 0.f;
+        zv[j] = 0.f;
         sv[j] = 0;
         const int t = t0 + lane * per + j;
         if (j < per && t < T) {
-            const float z = to_float(dt[((int64_t)b * T + t) * H + h]);
-            dv[j] = softplus ? softplus_f(z) : z;
+            zv[j] = to_float(dt[((int64_t)b * T + t) * H + h]);
             if (seq_idx) sv[j] = seq_idx[t];
         }
     }
+}
+
+// The arithmetic of chunk_cumsum_wave on loaded values; zv becomes Delta.
+__device__ __forceinline__ void chunk_cumsum_compute(const float *__restrict__ A, bool packed, int c, int h,
+                                                     int T, int Q, int softplus, float (&zv)[4], float (&cv)[4],
+                                                     const int (&sv)[4])
+{
+    const int lane = threadIdx.x & 63;
+    const int t0 = c * Q;
+    const int per = Q >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (j < per && t0 + lane * per + j < T && softplus) zv[j] = softplus_f(zv[j]);
     const int last_sv = per == 4 ? sv[3] : (per == 2 ? sv[1] : sv[0]);
     const int before = __shfl_up(last_sv, 1);   // id of the token just before this lane's first
     const double a = (double)A[h];
@@ -76,14 +108,16 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
     int restarted = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        loc[j] = 0.0;
+        flg[j] = 0;
         if (j < per) {
             const int i = lane * per + j;
             const int prev = j == 0 ? before : sv[j - 1];
-            if (seq_idx && i > 0 && t0 + i < T && sv[j] != prev) {
+            if (packed && i > 0 && t0 + i < T && sv[j] != prev) {
                 run = 0.0;
                 restarted = 1;
             }
-            run += (double)dv[j] * a;
+            run += (double)zv[j] * a;
             loc[j] = run;
             flg[j] = restarted;
         }
@@ -91,25 +125,60 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
     // segmented inclusive scan of (restarted, run) over the 64 lanes
     double v = run;
     int f = restarted;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double vo = __shfl_up(v, off);
-        const int fo = __shfl_up(f, off);
-        if (lane >= off) {
-            if (!f) v += vo;
-            f |= fo;
-        }
-    }
+    wave_segmented_scan(v, f);
     double carry = __shfl_up(v, 1);
     if (lane == 0) carry = 0.0;
-    const int64_t o = (((int64_t)b * H + h) * nc + c) * Q + lane * per;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cv[j] = (float)(flg[j] ? loc[j] : carry + loc[j]);
+}
+
+// One wave computes Delta and cs of one (b, chunk, head): every lane owns Q/64
+// consecutive tokens (per = 1, 2 or 4), sums them sequentially, and a segmented
+// wave scan (a segment restarts at a packed-sequence boundary) combines the
+// lanes.  Sums run in fp64 and are rounded once, so a stored cs carries a single
+// rounding.  On return lane l holds, for token l*per + j (j < per), dv[j] = Delta
+// (0 past the sequence end), cv[j] = cs and sv[j] = its sequence id (0 without
+// seq_idx).  Used by the cumsum kernel and by chunk_state, which must agree bit
+// for bit.
+template <typename E>
+__device__ __forceinline__ void chunk_cumsum_wave(const E *__restrict__ dt, const float *__restrict__ A,
+                                                  const int32_t *__restrict__ seq_idx, int b, int c, int h,
+                                                  int T, int H, int Q, int softplus, float (&dv)[4],
+                                                  float (&cv)[4], int (&sv)[4])
+{
+    chunk_cumsum_load<E>(dt, seq_idx, b, c, h, T, H, Q, dv, sv);
+    chunk_cumsum_compute(A, seq_idx != nullptr, c, h, T, Q, softplus, dv, cv, sv);
+}
+
+// Delta and cs rows of one (b, chunk, head) as left by chunk_cumsum_wave.
+__device__ __forceinline__ void store_cumsum_wave(float *__restrict__ delta, float *__restrict__ cs, int64_t row,
+                                                  int Q, const float (&dv)[4], const float (&cv)[4])
+{
+    const int per = Q >> 6;
+    const int64_t o = row * Q + (threadIdx.x & 63) * per;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (j < per) {
             delta[o + j] = dv[j];
-            cs[o + j] = (float)(flg[j] ? loc[j] : carry + loc[j]);
+            cs[o + j] = cv[j];
         }
     }
+}
+
+// Grid (nc, ceil(H/4), b): one wave per (chunk, head).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void k_chunk_cumsum(
+    const E *__restrict__ dt, const float *__restrict__ A, const int32_t *__restrict__ seq_idx,
+    float *__restrict__ delta, float *__restrict__ cs, int T, int H, int Q, int nc, int softplus)
+{
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y * kCumsumHeads + wave;
+    if (h >= H) return;   // whole wave; no barriers below
+    float dv[4], cv[4];
+    int sv[4];
+    chunk_cumsum_wave<E>(dt, A, seq_idx, b, c, h, T, H, Q, softplus, dv, cv, sv);
+    store_cumsum_wave(delta, cs, ((int64_t)b * H + h) * nc + c, Q, dv, cv);
 }
 
 
@@ -579,7 +648,8 @@ __device__ __forceinline__ void store_state_tile(E *stage, const floatx4 (&acc)[
 
 // chunk_state: states[b,c,h,p,n] = sum_s w_s x_s[p] B_s[n], w_s = exp(cs_last -
 // cs_s) delta_s for s in the segment of the chunk's last token (0 elsewhere).
-// One workgroup per (b, c, h, 64-p tile).  The weighted x tile of all Q tokens
+// One workgroup per (b, c, h, 64-p tile).  Wave 0 first runs the cumsum step
+// for (b, c, h) (Delta, cs and the weights).  The weighted x tile of all Q tokens
 // is staged in LDS once (its K index, time, read back transposed); the B^T
 // fragments (rows n, K = s) are streamed fragment-major from the chunk_cb
 // buffer, RING K steps ahead, one contiguous block per wave and step.  Wave w
@@ -587,9 +657,9 @@ __device__ __forceinline__ void store_state_tile(E *stage, const floatx4 (&acc)[
 //   acc[i][j][r]  <->  n = w*NT/4 + i*16 + 4*(lane/16) + r,  p = j*16 + lane%16.
 template <typename E, int Q, int NT, bool PACKED>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
-    const E *__restrict__ x, const E *__restrict__ cbuf, const float *__restrict__ delta,
-    const float *__restrict__ cs, const int32_t *__restrict__ seq_idx, E *__restrict__ states,
-    int T, int H, int G, int P, int N, int nc, int ntp)
+    const E *__restrict__ x, const E *__restrict__ cbuf, const E *__restrict__ dt, const float *__restrict__ A,
+    const int32_t *__restrict__ seq_idx, float *__restrict__ delta, float *__restrict__ cs,
+    E *__restrict__ states, int T, int H, int G, int P, int N, int nc, int ntp, int softplus)
 {
     using F = frag_t<E>;
     using XT = KTile<E, Q, 64>;
@@ -613,6 +683,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
 
+    // wave 0's dt loads go first: vector loads complete in issue order, and the
+    // cumsum step below must not wait for the tiles
+    float dv[4], cv[4];
+    int sv[4];
+    if (wave == 0) chunk_cumsum_load<E>(dt, seq_idx, b, c, h, T, H, Q, dv, sv);
     const int64_t ldx = (int64_t)H * P;
     XT xs;
     xs.init(ldx, P - p0);
@@ -636,13 +711,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
             else ra[r][i] = F{};
         }
 
-    const int64_t cso = (((int64_t)b * H + h) * nc + c) * Q;
-    const float lam = cs[cso + len - 1];
-    const int seq_last = PACKED ? seq_idx[t0 + len - 1] : 0;
-    for (int s = threadIdx.x; s < Q; s += kThreads) {
-        const bool keep = s < len && (!PACKED || seq_idx[t0 + s] == seq_last);
-        m[s] = keep;
-        w[s] = keep ? exp_neg(lam - cs[cso + s]) * delta[cso + s] : 0.f;
+    // Delta and cs of this chunk and head (the cumsum step, bit-identical to
+    // k_chunk_cumsum) by wave 0 while the loads above fly; the first p-tile's
+    // workgroup also stores them for state_passing and chunk_scan
+    if (wave == 0) {
+        chunk_cumsum_compute(A, PACKED, c, h, T, Q, softplus, dv, cv, sv);
+        if (tp == 0) store_cumsum_wave(delta, cs, ((int64_t)b * H + h) * nc + c, Q, dv, cv);
+        constexpr int per = Q / 64;
+        const int il = len - 1, ll = il / per, jl = il % per;   // lane and slot of the last token
+        float cl = cv[0];
+        int sl = sv[0];
+#pragma unroll
+        for (int j = 1; j < per; ++j) {
+            cl = jl == j ? cv[j] : cl;
+            sl = jl == j ? sv[j] : sl;
+        }
+        const float lam = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), ll));
+        const int seq_last = __builtin_amdgcn_readlane(sl, ll);
+#pragma unroll
+        for (int j = 0; j < per; ++j) {
+            const int s = lane * per + j;
+            const bool keep = s < len && (!PACKED || sv[j] == seq_last);
+            m[s] = keep;
+            w[s] = keep ? exp_neg(lam - cv[j]) * dv[j] : 0.f;
+        }
     }
     __syncthreads();
     xs.template store<true, PACKED>(xt, w, m);

@@ -223,7 +223,11 @@ def chunk_cb(p: Problem, cb=None, stream=None):
 
 
 def chunk_state(p: Problem, delta, cs, cb, states=None, stream=None):
+    """Chunk end states; also (re)writes ``delta`` and ``cs`` (the cumsum step)."""
     shape = (p.b, p.nc, p.H, p.P, p.N)
+    cshape = (p.b, p.H, p.nc, p.Q)
+    _check(delta, "delta", torch.float32, cshape, p.device)
+    _check(cs, "cs", torch.float32, cshape, p.device)
     states = p.empty(shape) if states is None else states
     _check(cb, "cb", p.dtype, p.cb_shape(), p.device)
     _check(states, "states", p.dtype, shape, p.device)

@@ -329,7 +329,10 @@ def test_per_step_pins(dtype, Q, packed):
     assert np.array_equal(btm, want_bt)
 
     # chunk_state: each chunk's end state from its own inputs (oracle chunk-local mode)
-    states = ssd.chunk_state(p, delta, cs, cb)
+    delta_c, cs_c = delta.clone(), cs.clone()
+    states = ssd.chunk_state(p, delta, cs, cb)   # runs the cumsum step again, in place
+    torch.cuda.synchronize()
+    assert torch.equal(delta, delta_c) and torch.equal(cs, cs_c)
     loc = run_oracle(inp, chunk=Q, chunk_local=True, want_chunk_states=True)
     torch.cuda.synchronize()
     sg = f64(states)
