@@ -656,7 +656,7 @@ __device__ __forceinline__ void store_state_tile(E *stage, const floatx4 (&acc)[
 // owns n rows w*NT/4 .. +NT/4 of D[n][p] (A = B^T, B = (w x)^T):
 //   acc[i][j][r]  <->  n = w*NT/4 + i*16 + 4*(lane/16) + r,  p = j*16 + lane%16.
 template <typename E, int Q, int NT, bool PACKED>
-__global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
+__global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const E *__restrict__ x, const E *__restrict__ cbuf, const E *__restrict__ dt, const float *__restrict__ A,
     const int32_t *__restrict__ seq_idx, float *__restrict__ delta, float *__restrict__ cs,
     E *__restrict__ states, int T, int H, int G, int P, int N, int nc, int ntp, int softplus)
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state(
     using XT = KTile<E, Q, 64>;
     constexpr int NI = NT / 64;
     constexpr int NKS = Q / 32;
-    constexpr int RING = 3;
+    constexpr int RING = 2;   // deep enough with four waves per SIMD, small enough to allow them
     constexpr int ES = (int)sizeof(E);
     constexpr int XSZ = XT::SIZE > 64 * NT ? XT::SIZE : 64 * NT;   // the x tile, then the result
     __shared__ __align__(16) E xt[XSZ];
