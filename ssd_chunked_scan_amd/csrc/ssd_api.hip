@@ -229,19 +229,12 @@ ssd_status run_passing(const Shape &s, const ssd_fwd_args *a, const float *cs, E
                        hipStream_t st)
 {
     const int64_t PN = s.P * s.N;   // a multiple of 256
-    // 16 bytes per thread when a wave of them still fits in one (b, h), else 4 elements
-    auto launch = [&](auto ve) {
-        constexpr int VE = decltype(ve)::value;
-        const int64_t vecs = s.b * s.H * PN / VE;
-        hipLaunchKernelGGL((k_state_passing<E, VE>), dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, states,
-                           cs, a->initial_states, final_states, a->seq_idx, (int)s.T, (int)s.H, PN, (int)s.nc,
-                           (int)s.Q, vecs);
-        return launched();
-    };
-    if constexpr (sizeof(E) == 2) {
-        if (PN % 512 == 0) return launch(std::integral_constant<int, 8>{});
-    }
-    return launch(std::integral_constant<int, 4>{});
+    constexpr int VE = 4;            // elements per thread
+    const int64_t vecs = s.b * s.H * PN / VE;
+    hipLaunchKernelGGL((k_state_passing<E, VE>), dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, states, cs,
+                       a->initial_states, final_states, a->seq_idx, (int)s.T, (int)s.H, PN, (int)s.nc, (int)s.Q,
+                       vecs);
+    return launched();
 }
 
 template <typename E>

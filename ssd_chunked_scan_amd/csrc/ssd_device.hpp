@@ -93,27 +93,10 @@ __device__ __forceinline__ float to_float(float v) { return v; }
 __device__ __forceinline__ float to_float(bf16 v) { return (float)v; }
 template <typename E> __device__ __forceinline__ E from_float(float v) { return (E)v; }
 
-// 16-byte vector <-> 4 or 8 floats.
-__device__ __forceinline__ void load16_f32(const float *p, float *out)
-{
-    const floatx4 v = *reinterpret_cast<const floatx4 *>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = v[i];
-}
-__device__ __forceinline__ void load16_f32(const bf16 *p, float *out)
-{
-    const floatx8 v = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p), floatx8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = v[i];
-}
+// Four floats to a 16-byte fp32 vector.
 __device__ __forceinline__ void store16_f32(float *p, const float *in)
 {
     *reinterpret_cast<floatx4 *>(p) = floatx4{in[0], in[1], in[2], in[3]};
-}
-__device__ __forceinline__ void store16_f32(bf16 *p, const float *in)
-{
-    const floatx8 v{in[0], in[1], in[2], in[3], in[4], in[5], in[6], in[7]};
-    *reinterpret_cast<bf16x8 *>(p) = __builtin_convertvector(v, bf16x8);
 }
 
 // Four consecutive elements <-> floats (8-byte bf16 or 16-byte fp32 access).

@@ -774,16 +774,16 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
 // state_passing: in place S_c -> h_{c-1}; h_c = exp(cs_last(c)) h_{c-1} + S_c
 // ---------------------------------------------------------------------------
 // Every (b, h, p, n) element is an independent length-nc scan.  Each thread owns
-// VE consecutive elements (8 or 4 bf16, 4 fp32: 16 or 8 bytes) and walks the
-// chunks with a ring of kPrefetch loads in flight: the slot a chunk's state is
-// read from is refilled with the state kPrefetch chunks ahead before the
-// arithmetic.  The carry is replaced by zero (a select) when the chunk holds a
-// segment boundary.
+// VE = 4 consecutive elements (8 bytes of bf16, 16 of fp32) and walks the chunks
+// with a ring of kPrefetch loads in flight: the slot a chunk's state is read from
+// is refilled with the state kPrefetch chunks ahead before the arithmetic.  The
+// carry is replaced by zero (a select) when the chunk holds a segment boundary.
+// (Four bf16 per thread measured best: eight leave the latency-bound small
+// shapes with too few waves, two waste bandwidth on 4-byte accesses.)
 constexpr int kPrefetch = 32;
 
 template <typename E, int VE> struct RawVec;
 template <> struct RawVec<bf16, 4> { using type = uint2; };
-template <> struct RawVec<bf16, 8> { using type = uint4; };
 template <> struct RawVec<float, 4> { using type = uint4; };
 
 __device__ __forceinline__ void unpack_raw(const uint2 &v, float *o)
@@ -791,28 +791,17 @@ __device__ __forceinline__ void unpack_raw(const uint2 &v, float *o)
     o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
     o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
 }
-template <typename E> __device__ __forceinline__ void unpack_raw(const uint4 &v, float *o);
-template <> __device__ __forceinline__ void unpack_raw<float>(const uint4 &v, float *o)
+__device__ __forceinline__ void unpack_raw(const uint4 &v, float *o)
 {
     o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
     o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
 }
-template <> __device__ __forceinline__ void unpack_raw<bf16>(const uint4 &v, float *o)
-{
-    unpack_raw(uint2{v.x, v.y}, o);
-    unpack_raw(uint2{v.z, v.w}, o + 4);
-}
 template <typename E, int VE> __device__ __forceinline__ void unpack_vec(const typename RawVec<E, VE>::type &v, float *o)
 {
-    if constexpr (sizeof(v) == 8) unpack_raw(v, o);
-    else unpack_raw<E>(v, o);
+    unpack_raw(v, o);
 }
 template <int VE> __device__ __forceinline__ void store_vec(float *p, const float *v) { store16_f32(p, v); }
-template <int VE> __device__ __forceinline__ void store_vec(bf16 *p, const float *v)
-{
-    if constexpr (VE == 8) store16_f32(p, v);
-    else store4_f32(p, v);
-}
+template <int VE> __device__ __forceinline__ void store_vec(bf16 *p, const float *v) { store4_f32(p, v); }
 template <int VE> __device__ __forceinline__ void load_init(const float *p, float *v)
 {
 #pragma unroll
