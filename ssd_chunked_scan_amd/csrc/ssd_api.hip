@@ -205,7 +205,7 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
 
 template <typename E>
 ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float *cs, const E *cb, E *states,
-                     hipStream_t st)
+                     int32_t *seg_end, hipStream_t st)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -214,8 +214,8 @@ ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float 
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
             auto launch = [&](auto kern) {
                 hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, (const E *)a->x, cb, (const E *)a->dt, a->A,
-                                   a->seq_idx, delta, cs, states, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
-                                   (int)s.nc, ntp, (int)a->dt_softplus);
+                                   a->seq_idx, delta, cs, states, seg_end, (int)s.nseq, (int)s.T, (int)s.H,
+                                   (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (int)a->dt_softplus);
             };
             if (s.packed) launch(k_chunk_state<E, Q, NT, true>);
             else launch(k_chunk_state<E, Q, NT, false>);
@@ -237,15 +237,17 @@ ssd_status run_passing(const Shape &s, const ssd_fwd_args *a, const float *cs, E
     return launched();
 }
 
+// `marked`: seg_end already holds the segment ends (chunk_state marks them in the
+// forward); otherwise they are marked here first.
 template <typename E>
 ssd_status run_seq_final(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs,
-                         const E *hin, int32_t *seg_end, hipStream_t st)
+                         const E *hin, int32_t *seg_end, bool marked, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_seg_end_init, dim3(grid1(s.nseq, 256)), dim3(256), 0, st, seg_end, (int)s.nseq);
-    if (launched() != SSD_OK) return SSD_ERR_HIP;
-    hipLaunchKernelGGL(k_seg_end, dim3(grid1(s.T, 256)), dim3(256), 0, st, a->seq_idx, seg_end, (int)s.T,
-                       (int)s.nseq);
-    if (launched() != SSD_OK) return SSD_ERR_HIP;
+    if (!marked) {
+        hipLaunchKernelGGL(k_seg_end, dim3(grid1(s.T, 256)), dim3(256), 0, st, a->seq_idx, seg_end, (int)s.T,
+                           (int)s.nseq);
+        if (launched() != SSD_OK) return SSD_ERR_HIP;
+    }
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nseq * s.H * ntp));
     return with_q(s.Q, [&](auto q) {
@@ -302,10 +304,11 @@ ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, 
     int32_t *seg_end = reinterpret_cast<int32_t *>(ws + w.seg_end);
     ssd_status r;
     if ((r = run_cb<E>(s, a, cb, st)) != SSD_OK) return r;   // the cumsum step runs inside chunk_state
-    if ((r = run_state<E>(s, a, delta, cs, cb, states, st)) != SSD_OK) return r;
+    const bool seq_final = s.packed && a->final_states;   // chunk_state then marks the segment ends
+    if ((r = run_state<E>(s, a, delta, cs, cb, states, seq_final ? seg_end : nullptr, st)) != SSD_OK) return r;
     if ((r = run_passing<E>(s, a, cs, states, s.packed ? nullptr : a->final_states, st)) != SSD_OK) return r;
-    if (s.packed && a->final_states)
-        if ((r = run_seq_final<E>(s, a, delta, cs, states, seg_end, st)) != SSD_OK) return r;
+    if (seq_final)
+        if ((r = run_seq_final<E>(s, a, delta, cs, states, seg_end, true, st)) != SSD_OK) return r;
     return run_scan<E>(s, a, delta, cs, cb, states, st);
 }
 
@@ -406,8 +409,9 @@ ssd_status ssd_chunk_state(const ssd_fwd_args *args, float *delta, float *cs, co
     if (!delta || !cs || !cb || !states) return SSD_ERR_NULL_POINTER;
     if (!aligned16(delta) || !aligned16(cs) || !aligned16(cb) || !aligned16(states)) return SSD_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return s.dtype == SSD_DTYPE_BF16 ? run_state<bf16>(s, args, delta, cs, (const bf16 *)cb, (bf16 *)states, st)
-                                     : run_state<float>(s, args, delta, cs, (const float *)cb, (float *)states, st);
+    return s.dtype == SSD_DTYPE_BF16
+               ? run_state<bf16>(s, args, delta, cs, (const bf16 *)cb, (bf16 *)states, nullptr, st)
+               : run_state<float>(s, args, delta, cs, (const float *)cb, (float *)states, nullptr, st);
 }
 
 ssd_status ssd_state_passing(const ssd_fwd_args *args, const float *cs, void *states, void *stream)
@@ -440,8 +444,8 @@ ssd_status ssd_seq_final_states(const ssd_fwd_args *args, const float *delta, co
     if (!aligned16(delta) || !aligned16(cs) || !aligned16(states) || !aligned16(seg_end))
         return SSD_ERR_MISALIGNED;
     return s.dtype == SSD_DTYPE_BF16
-               ? run_seq_final<bf16>(s, args, delta, cs, (const bf16 *)states, seg_end, st)
-               : run_seq_final<float>(s, args, delta, cs, (const float *)states, seg_end, st);
+               ? run_seq_final<bf16>(s, args, delta, cs, (const bf16 *)states, seg_end, false, st)
+               : run_seq_final<float>(s, args, delta, cs, (const float *)states, seg_end, false, st);
 }
 
 ssd_status ssd_chunk_scan(const ssd_fwd_args *args, const float *delta, const float *cs, const void *cb,

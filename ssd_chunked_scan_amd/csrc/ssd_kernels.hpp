@@ -646,10 +646,32 @@ __device__ __forceinline__ void store_state_tile(E *stage, const floatx4 (&acc)[
     }
 }
 
+// seg_end[s] = the last position of segment id s, or -1 for an id that never
+// occurs, from non-decreasing ids in [0, nseq): position t writes the entry of
+// its id if the id changes after t, and -1 for the ids it skips (those between
+// its id and the next position's, those below the first id at t = 0, those past
+// the last id at t = T-1).  Every id is written exactly once, so no pass has to
+// clear the array first.  Ids are clamped to [0, nseq), so no write leaves the
+// array whatever the ids hold.
+__device__ __forceinline__ void seg_end_mark(const int32_t *__restrict__ seq_idx, int32_t *__restrict__ seg_end,
+                                             int t, int T, int nseq)
+{
+    const int sid = seq_idx[t];
+    if (t == 0)
+        for (int id = 0; id < min(sid, nseq); ++id) seg_end[id] = -1;
+    const int nxt = t == T - 1 ? nseq : seq_idx[t + 1];
+    if (nxt != sid) {
+        if (sid >= 0 && sid < nseq) seg_end[sid] = t;
+        for (int id = max(sid + 1, 0); id < min(nxt, nseq); ++id) seg_end[id] = -1;
+    }
+}
+
 // chunk_state: states[b,c,h,p,n] = sum_s w_s x_s[p] B_s[n], w_s = exp(cs_last -
 // cs_s) delta_s for s in the segment of the chunk's last token (0 elsewhere).
 // One workgroup per (b, c, h, 64-p tile).  Wave 0 first runs the cumsum step
-// for (b, c, h) (Delta, cs and the weights).  The weighted x tile of all Q tokens
+// for (b, c, h) (Delta, cs and the weights); with packed streams and seg_end
+// given, wave 1 of the (c, h = 0, first p-tile) workgroup marks the segment ends
+// of the chunk (seg_end_mark).  The weighted x tile of all Q tokens
 // is staged in LDS once (its K index, time, read back transposed); the B^T
 // fragments (rows n, K = s) are streamed fragment-major from the chunk_cb
 // buffer, RING K steps ahead, one contiguous block per wave and step.  Wave w
@@ -659,7 +681,8 @@ template <typename E, int Q, int NT, bool PACKED>
 __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const E *__restrict__ x, const E *__restrict__ cbuf, const E *__restrict__ dt, const float *__restrict__ A,
     const int32_t *__restrict__ seq_idx, float *__restrict__ delta, float *__restrict__ cs,
-    E *__restrict__ states, int T, int H, int G, int P, int N, int nc, int ntp, int softplus)
+    E *__restrict__ states, int32_t *__restrict__ seg_end, int nseq, int T, int H, int G, int P, int N, int nc,
+    int ntp, int softplus)
 {
     using F = frag_t<E>;
     using XT = KTile<E, Q, 64>;
@@ -710,6 +733,12 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
             if (r < NKS) bload_frag(brs, b_off(i, r), ra[r][i]);
             else ra[r][i] = F{};
         }
+
+    // Packed streams: wave 1 of one workgroup per chunk records the segment ends
+    // among the chunk's positions (for the per-segment final states), while wave
+    // 0 runs the cumsum step.
+    if (PACKED && seg_end && h == 0 && tp == 0 && wave == 1)
+        for (int t = t0 + lane; t < t0 + len; t += 64) seg_end_mark(seq_idx, seg_end, t, T, nseq);
 
     // Delta and cs of this chunk and head (the cumsum step, bit-identical to
     // k_chunk_cumsum) by wave 0 while the loads above fly; the first p-tile's
@@ -872,19 +901,11 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
 // ---------------------------------------------------------------------------
 // Packed streams: segment ends and per-segment final states
 // ---------------------------------------------------------------------------
-__global__ void k_seg_end_init(int32_t *seg_end, int nseq)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < nseq) seg_end[i] = -1;
-}
-
-// seg_end[s] = last position of segment id s (ids outside [0, nseq) are ignored).
+// seg_end for every segment, one thread per position (seg_end_mark).
 __global__ void k_seg_end(const int32_t *__restrict__ seq_idx, int32_t *__restrict__ seg_end, int T, int nseq)
 {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= T) return;
-    const int s = seq_idx[t];
-    if ((t == T - 1 || seq_idx[t + 1] != s) && s >= 0 && s < nseq) seg_end[s] = t;
+    if (t < T) seg_end_mark(seq_idx, seg_end, t, T, nseq);
 }
 
 // final_states[sg,h,p,n] = state right after segment sg's last token t_e:

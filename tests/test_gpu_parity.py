@@ -181,6 +181,37 @@ def test_fwd_packed_slow_decay(dtype):
     check(inp, DT[dtype], label="packed slow decay")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fwd_packed_sparse_ids(dtype):
+    """Segment ids with a gap, starting above 0 and ending below nseq - 1: every id
+    that never occurs gets a zero final state, both in the forward (where
+    chunk_state records the segment ends) and through the per-step entry point
+    (which records them with its own kernel); the two agree bit for bit."""
+    Q = 64
+    lengths, sids, nseq = [70, 150, 90], [2, 3, 6], 9
+    T = sum(lengths)
+    ids = np.concatenate([np.full(L, s) for s, L in zip(sids, lengths)]).astype(np.int32)
+    base = small(dtype, T, H=3, P=32, N=32, b=1, seed=31, init_std=0.3)
+    inp = wl.Inputs(base.x, base.dt, base.A, base.B, base.C, base.D, base.initial_states,
+                    torch.from_numpy(ids), nseq, Q, lengths=lengths)
+    _log(f"[parity] sparse segment ids {sids} of nseq={nseq} dtype={dtype}")
+    y, fs = run_gpu(inp)
+    ref = run_oracle(inp)
+    assert max_rel_y(y, ref.y, inp) <= TOL[DT[dtype]]
+    assert max_rel_states(fs, ref.final_states, rows=sids) <= TOL[DT[dtype]]
+    absent = [i for i in range(nseq) if i not in sids]
+    assert torch.count_nonzero(fs[absent]) == 0
+    # the per-step path
+    g = inp.to("cuda:0")
+    p = _problem(g, inp)
+    delta, cs = ssd.chunk_cumsum(p)
+    cb = ssd.chunk_cb(p)
+    states = ssd.chunk_state(p, delta, cs, cb)
+    ssd.state_passing(p, cs, states)
+    fs_step = ssd.seq_final_states(p, delta, cs, states)
+    assert torch.equal(fs_step, fs)
+
+
 @pytest.mark.parametrize("shape", [
     dict(T=1), dict(T=37), dict(T=64), dict(T=65), dict(P=16, N=16, H=2, T=256),
     dict(P=128, N=64, T=150), dict(P=48, N=48, T=200), dict(N=256, T=300, H=2), dict(H=6, G=3, T=129),
