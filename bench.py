@@ -9,8 +9,11 @@ input already resident in HBM.  Prints ONE JSON line:
   roofline     the dominant kernel's achieved algorithmic FLOP/s (or bytes/s) per
                launch, from HIP events recorded on the launch stream, against
                MI355X's published peak
+  step_ms      p10/p50/p90 of single steps between HIP events, warm (back to back)
+               and cold (L2 and MALL evicted by a 1 GiB write before each step)
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same workload
-  kernels      per-kernel breakdown (average ms per launch, achieved rate, fraction)
+  kernels      per-kernel breakdown (average ms per launch, achieved rate, fraction,
+               counter-measured MFMA busy % where a record for these sources exists)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
 """
@@ -60,6 +63,44 @@ def measured_traffic(kernel, workload):
                 if rec["kernel"] == kernel and rec["workload"] == workload and rec["source_sha256"] == src:
                     return int(rec["fetch_bytes"] + rec["write_bytes"])
     return None
+
+
+def measured_mfma(kernel, workload):
+    """Counter-measured MFMA busy percentage of `kernel` on `workload` (the
+    MfmaUtil metric: MFMA busy cycles over active cycles x SIMDs) from the
+    committed counter records, or None when no record exists or the kernels
+    changed since."""
+    import glob
+    src = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*mfma_util*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("mfma-record: "):
+                    continue
+                rec = json.loads(line[len("mfma-record: "):])
+                if rec["kernel"] == kernel and rec["workload"] == workload and rec["source_sha256"] == src:
+                    return rec["mfma_busy_pct"]
+    return None
+
+
+def host_cpu():
+    """(online CPUs, CPU model name) of this host, for the oracle baseline."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def percentiles(ms):
+    v = sorted(ms)
+    pick = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    return {"p10": round(pick(0.1), 5), "p50": round(pick(0.5), 5), "p90": round(pick(0.9), 5)}
 
 
 def algorithmic_work(shape, esz, packed):
@@ -120,8 +161,9 @@ def run_cpu_baseline(inp, budget_s=20.0):
             break
     dt = sorted(times)[len(times) // 2]
     full_time = dt * units / k
+    nproc, model = host_cpu()
     return {"value": inp.real_tokens / full_time, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "nproc": nproc, "cpu_model": model,
             "sample": f"{k} of {units} (batch, head) units, all {T} tokens each; median of "
                       f"{len(times)} runs of {dt:.2f} s, extrapolated x{units / k:.1f}",
             "seconds_measured": round(sum(times), 3)}
@@ -184,9 +226,31 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = inp.real_tokens * args.steps / elapsed
 
+    # per-step latency: HIP events around single steps on the launch stream, warm
+    # (back to back) and cold (a 1 GiB write before each step, outside the events,
+    # evicts L2 and the 256 MB MALL)
+    stream = torch.cuda.current_stream(dev)
+    reps = max(5, min(args.steps, 100))
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    lat = {}
+    for mode in ("warm", "cold"):
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(reps)]
+        for r in range(reps):
+            if mode == "cold":
+                flush.fill_(float(r))
+            pairs[r][0].record(stream)
+            step()
+            pairs[r][1].record(stream)
+        torch.cuda.synchronize()
+        lat[mode] = [a.elapsed_time(b_) for a, b_ in pairs]
+    del flush
+    step_ms = {m: percentiles(v) for m, v in lat.items()}
+    step_ms["cold_tokens_per_s"] = round(inp.real_tokens / (step_ms["cold"]["p50"] / 1e3), 1)
+    step_ms["reps"] = reps
+
     # per-kernel breakdown: the same kernels through the per-step entry points,
     # bracketed by HIP events on the stream they are launched on
-    stream = torch.cuda.current_stream(dev)
     names = ["chunk_cb", "chunk_state", "state_passing"]   # the kernels ssd_fwd launches
     if inp.seq_idx is not None:
         names.append("seq_final")
@@ -231,7 +295,8 @@ def main():
             ach = wk["flops"] / sec / 1e12
             kernels[n] = dict(ms=round(kms[n], 5), bound="mfma", achieved=round(ach, 2),
                               peak=mfma_peak, unit="TFLOP/s", frac=round(ach / mfma_peak, 4),
-                              hbm_gbs=round(wk["bytes"] / sec / 1e9, 1))
+                              hbm_gbs=round(wk["bytes"] / sec / 1e9, 1),
+                              mfma_busy_pct=measured_mfma(n, cfg["name"]))
         else:
             ach = wk["bytes"] / sec / 1e9
             kernels[n] = dict(ms=round(kms[n], 5), bound="hbm", achieved=round(ach, 1),
@@ -241,7 +306,8 @@ def main():
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
                 "unit": kd["unit"], "frac": kd["frac"],
                 "traffic": measured_traffic(dom, cfg["name"]), "traffic_unit": "HBM bytes per launch",
-                "algorithmic_bytes": int(work[dom]["bytes"])}
+                "algorithmic_bytes": int(work[dom]["bytes"]),
+                "mfma_busy_pct": measured_mfma(dom, cfg["name"])}
     total_flops = sum(w.get("flops", 0.0) for w in work.values())
 
     cpu = None
@@ -259,6 +325,7 @@ def main():
                    "real_tokens": inp.real_tokens},
         "tflops": round(total_flops / (ms_per_step / 1e3) / 1e12, 2),
         "roofline": roofline,
+        "step_ms": step_ms,
         "cpu_baseline": cpu,
         "kernels": kernels,
     }

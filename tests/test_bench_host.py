@@ -1,0 +1,62 @@
+"""Host-side pieces of bench.py: work counts, percentiles, counter records, the
+one-GPU guard. No GPU needed."""
+import glob
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_algorithmic_work_long_workload():
+    # 16K tokens, 32 heads of 64, N = 256, one group, chunk 256, bf16
+    shape = dict(batch=1, seqlen=16384, nheads=32, headdim=64, dstate=256, ngroups=1, chunk=256)
+    w = bench.algorithmic_work(shape, 2, False)
+    T, H, P, N, Q = 16384, 32, 64, 256, 256
+    # chunk_state: one multiply-add per (t, h, p, n)
+    assert w["chunk_state"]["flops"] == 2 * T * H * P * N
+    # chunk_scan: the causal half (with diagonal) of the Q x Q block product, plus C h
+    assert w["chunk_scan"]["flops"] == pytest.approx(2 * T * H * P * (Q + 1) / 2 + 2 * T * H * N * P)
+    # state_passing reads and writes every bf16 state once, plus the fp32 chunk sums and
+    # the fp32 initial and final states
+    nc = T // Q
+    assert w["state_passing"]["bytes"] == 2 * nc * H * P * N * 2 + H * nc * 4 + 2 * H * P * N * 4
+
+
+def test_percentiles():
+    p = bench.percentiles([float(i) for i in range(101)])
+    assert (p["p10"], p["p50"], p["p90"]) == (10.0, 50.0, 90.0)
+    assert bench.percentiles([3.0]) == {"p10": 3.0, "p50": 3.0, "p90": 3.0}
+
+
+@pytest.mark.parametrize("pattern,prefix", [("*hbm_traffic*.md", "traffic-record: "),
+                                            ("*mfma_util*.md", "mfma-record: ")])
+def test_counter_records_parse(pattern, prefix):
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", pattern)))
+    assert paths, f"no committed {pattern} records"
+    src = bench.kernel_source_hash()
+    for path in paths:
+        recs = [json.loads(l[len(prefix):]) for l in open(path) if l.startswith(prefix)]
+        assert recs, path
+        for r in recs:
+            assert {"kernel", "workload", "source_sha256"} <= set(r)
+            if r["source_sha256"] != src:
+                continue   # taken from older kernels: the bench ignores it
+            if prefix.startswith("traffic"):
+                assert bench.measured_traffic(r["kernel"], r["workload"]) == int(r["fetch_bytes"] + r["write_bytes"])
+            else:
+                assert bench.measured_mfma(r["kernel"], r["workload"]) == r["mfma_busy_pct"]
+    assert bench.measured_traffic("chunk_scan", "no such workload") is None
+    assert bench.measured_mfma("chunk_scan", "no such workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
