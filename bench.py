@@ -103,6 +103,26 @@ def percentiles(ms):
     return {"p10": round(pick(0.1), 5), "p50": round(pick(0.5), 5), "p90": round(pick(0.9), 5)}
 
 
+def roofline_point(wk, sec, esz):
+    """Place one kernel launch on the roofline.  The binding roof follows from the
+    kernel's arithmetic intensity: below the ridge point (peak FLOP/s over peak
+    bytes/s) HBM bounds it and `frac` is achieved bytes/s over the HBM peak; at or
+    above it, achieved FLOP/s over the MFMA peak of the compute dtype.  Both rates
+    are returned either way."""
+    mfma_peak = PEAK["bf16_mfma_tflops"] if esz == 2 else PEAK["fp32_mfma_tflops"]
+    ridge = mfma_peak * 1e12 / (PEAK["hbm_gbs"] * 1e9)
+    flops, nbytes = wk.get("flops", 0.0), wk["bytes"]
+    e = {"hbm_gbs": round(nbytes / sec / 1e9, 1), "hbm_frac": round(nbytes / sec / 1e9 / PEAK["hbm_gbs"], 4)}
+    if flops:
+        e.update(tflops=round(flops / sec / 1e12, 2), mfma_frac=round(flops / sec / 1e12 / mfma_peak, 4),
+                 flop_per_byte=round(flops / nbytes, 1) if nbytes else None, ridge_flop_per_byte=round(ridge, 1))
+    if flops and (not nbytes or flops / nbytes >= ridge):
+        e.update(bound="mfma", achieved=e["tflops"], peak=mfma_peak, unit="TFLOP/s", frac=e["mfma_frac"])
+    else:
+        e.update(bound="hbm", achieved=e["hbm_gbs"], peak=PEAK["hbm_gbs"], unit="GB/s", frac=e["hbm_frac"])
+    return e
+
+
 def algorithmic_work(shape, esz, packed):
     """Per-launch algorithmic FLOPs (multiply-add = 2) and HBM bytes of each kernel.
 
@@ -116,19 +136,18 @@ def algorithmic_work(shape, esz, packed):
     dcs = 2 * b * H * nc * Q * 4             # delta + cs
     cbb = b * nc * G * Q * Q * esz * (Q // 64 + 1) / (2 * (Q // 64))  # lower block triangle
     w = {
-        "chunk_cumsum": dict(bound="hbm", bytes=b * T * H * esz + H * 4 + dcs),
-        "chunk_cb": dict(bound="mfma", flops=2.0 * b * nc * Q * G * Q * N * causal,
+        "chunk_cumsum": dict(bytes=b * T * H * esz + H * 4 + dcs),
+        "chunk_cb": dict(flops=2.0 * b * nc * Q * G * Q * N * causal,
                          bytes=2 * b * T * G * N * esz + cbb),
         # chunk_state runs the cumsum step too: it reads dt and writes delta and cs
-        "chunk_state": dict(bound="mfma", flops=2.0 * b * T * H * P * N,
+        "chunk_state": dict(flops=2.0 * b * T * H * P * N,
                             bytes=b * T * H * P * esz + b * T * G * N * esz + b * T * H * esz + dcs + st),
-        "state_passing": dict(bound="hbm", bytes=2 * st + b * H * nc * 4 + 2 * b * H * P * N * 4),
-        "chunk_scan": dict(bound="mfma",
-                           flops=2.0 * b * T * H * P * Q * causal + 2.0 * b * T * H * N * P,
+        "state_passing": dict(bytes=2 * st + b * H * nc * 4 + 2 * b * H * P * N * 4),
+        "chunk_scan": dict(flops=2.0 * b * T * H * P * Q * causal + 2.0 * b * T * H * N * P,
                            bytes=2 * b * T * H * P * esz + b * T * G * N * esz + dcs + st + cbb),
     }
     if packed:
-        w["seq_final"] = dict(bound="mfma", flops=0.0, bytes=0)
+        w["seq_final"] = dict(flops=0.0, bytes=0)
     return w
 
 
@@ -286,25 +305,16 @@ def main():
 
     esz = 2 if g.x.dtype == torch.bfloat16 else 4
     work = algorithmic_work(inp.shape, esz, inp.seq_idx is not None)
-    mfma_peak = PEAK["bf16_mfma_tflops"] if esz == 2 else PEAK["fp32_mfma_tflops"]
     kernels = {}
     for n in names:
-        wk = work[n]
-        sec = kms[n] / 1e3
-        if wk["bound"] == "mfma" and wk.get("flops"):
-            ach = wk["flops"] / sec / 1e12
-            kernels[n] = dict(ms=round(kms[n], 5), bound="mfma", achieved=round(ach, 2),
-                              peak=mfma_peak, unit="TFLOP/s", frac=round(ach / mfma_peak, 4),
-                              hbm_gbs=round(wk["bytes"] / sec / 1e9, 1),
-                              mfma_busy_pct=measured_mfma(n, cfg["name"]))
-        else:
-            ach = wk["bytes"] / sec / 1e9
-            kernels[n] = dict(ms=round(kms[n], 5), bound="hbm", achieved=round(ach, 1),
-                              peak=PEAK["hbm_gbs"], unit="GB/s", frac=round(ach / PEAK["hbm_gbs"], 4))
+        kernels[n] = dict(ms=round(kms[n], 5), **roofline_point(work[n], kms[n] / 1e3, esz))
+        if work[n].get("flops"):
+            kernels[n]["mfma_busy_pct"] = measured_mfma(n, cfg["name"])
     dom = max(names, key=lambda n: kms[n])
     kd = kernels[dom]
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
-                "unit": kd["unit"], "frac": kd["frac"],
+                "unit": kd["unit"], "frac": kd["frac"], "mfma_frac": kd.get("mfma_frac"),
+                "hbm_frac": kd["hbm_frac"], "flop_per_byte": kd.get("flop_per_byte"),
                 "traffic": measured_traffic(dom, cfg["name"]), "traffic_unit": "HBM bytes per launch",
                 "algorithmic_bytes": int(work[dom]["bytes"]),
                 "mfma_busy_pct": measured_mfma(dom, cfg["name"])}

@@ -60,3 +60,18 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_roofline_point_picks_the_binding_roof():
+    # bf16 ridge point: 2500 TFLOP/s over 8000 GB/s = 312.5 FLOP/B
+    below = bench.roofline_point({"flops": 100e9, "bytes": 1e9}, 1e-3, 2)     # 100 FLOP/B
+    assert below["bound"] == "hbm" and below["unit"] == "GB/s"
+    assert below["achieved"] == pytest.approx(1000.0) and below["frac"] == pytest.approx(0.125)
+    assert below["mfma_frac"] == pytest.approx(100 / 2500, abs=1e-4)
+    above = bench.roofline_point({"flops": 1000e9, "bytes": 1e9}, 1e-3, 2)    # 1000 FLOP/B
+    assert above["bound"] == "mfma" and above["unit"] == "TFLOP/s"
+    assert above["frac"] == pytest.approx(0.4) and above["hbm_frac"] == pytest.approx(0.125)
+    # fp32 has its own ridge: 157.3 TFLOP/s over 8000 GB/s ~ 19.7 FLOP/B
+    assert bench.roofline_point({"flops": 100e9, "bytes": 1e9}, 1e-3, 4)["bound"] == "mfma"
+    copy = bench.roofline_point({"bytes": 4e9}, 1e-3, 2)
+    assert copy["bound"] == "hbm" and copy["frac"] == pytest.approx(0.5) and "mfma_frac" not in copy
