@@ -14,6 +14,8 @@ input already resident in HBM.  Prints ONE JSON line:
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same workload
   kernels      per-kernel breakdown (average ms per launch, achieved rate, fraction,
                counter-measured MFMA busy % where a record for these sources exists)
+  decode       the decode step (one token per sequence, state carried) on its own
+               seeded workload: time per launch, tokens/s and its HBM roofline
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
 """
@@ -188,6 +190,47 @@ def run_cpu_baseline(inp, budget_s=20.0):
             "seconds_measured": round(sum(times), 3)}
 
 
+def run_decode(dev, reps, warmup):
+    """Time the decode step (ssd_step) on the seeded decode workload: HIP events
+    around each launch on the launch stream, the state carried from launch to
+    launch as in serving."""
+    import torch
+    from ssd_chunked_scan_amd import ssd
+    from ssd_chunked_scan_amd import workloads as wl
+
+    s = wl.decode_inputs()
+    g = s.to(dev)
+    state = g.state.clone()
+    y = torch.empty_like(g.x)
+    b, H, P = s.x.shape
+    G, N = s.B.shape[1], s.B.shape[2]
+    esz = 2 if s.x.dtype == torch.bfloat16 else 4
+    stream = torch.cuda.current_stream(dev)
+
+    def one():
+        ssd.step(g.x, g.dt, g.A, g.B, g.C, state, D=g.D, y=y)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b_ in ev:
+        a.record(stream)
+        one()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b_) for a, b_ in ev]
+    avg = sum(ms) / len(ms)
+    # the state is read and written once; x and y once; dt, B and C once
+    nbytes = 2 * b * H * P * N * 4 + 2 * b * H * P * esz + b * H * esz + 2 * b * G * N * esz + 2 * H * 4
+    ach = nbytes / (avg / 1e3) / 1e9
+    return {"workload": s.name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "ngroups": G,
+            "ms": round(avg, 5), "step_ms": percentiles(ms), "tokens_per_s": round(b / (avg / 1e3), 1),
+            "roofline": {"kernel": "ssd_step", "bound": "hbm", "achieved": round(ach, 1),
+                         "peak": PEAK["hbm_gbs"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_gbs"], 4),
+                         "traffic": measured_traffic("ssd_step", s.name), "algorithmic_bytes": int(nbytes)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +239,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB (3 times), as the "
@@ -319,6 +363,7 @@ def main():
                 "algorithmic_bytes": int(work[dom]["bytes"]),
                 "mfma_busy_pct": measured_mfma(dom, cfg["name"])}
     total_flops = sum(w.get("flops", 0.0) for w in work.values())
+    decode = None if args.no_decode else run_decode(dev, reps, 5)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -338,6 +383,7 @@ def main():
         "step_ms": step_ms,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "decode": decode,
     }
     print(json.dumps(line), flush=True)
 

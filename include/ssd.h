@@ -172,6 +172,39 @@ ssd_status ssd_seq_final_states(const ssd_fwd_args *args, const float *delta, co
 ssd_status ssd_chunk_scan(const ssd_fwd_args *args, const float *delta, const float *cs,
                           const void *cb, const void *states, void *stream);
 
+/*
+ * Decode: one step of the recurrence for one new token per batch row (the
+ * constant-size recurrent mode of section 3.1 of "Mamba 2 -- Transformers are
+ * SSMs"; the chunked entry points above are its parallel form).  For every
+ * batch row b and head h (group g = h*G/H):
+ *
+ *     Delta = softplus(dt[b,h])  (or dt[b,h]),   a = exp(Delta * A[h])
+ *     state[b,h,p,n] <- a * state[b,h,p,n] + Delta * x[b,h,p] * B[b,g,n]
+ *     y[b,h,p]        = sum_n C[b,g,n] * state[b,h,p,n] + D[h] * x[b,h,p]
+ *
+ * with the state read and overwritten in place, in fp32.  Calling it for tokens
+ * 0..T-1 of a sequence, starting from initial_states, gives the y and the
+ * final_states of ssd_fwd over those T tokens (up to rounding order).
+ * Supported: batch >= 1, H % G == 0, P and N multiples of 16, N <= 256,
+ * batch*nheads < 2^31.  Every pointer 16-byte aligned; y and the state must not
+ * overlap each other or any input.
+ */
+typedef struct {
+    int64_t batch, nheads, headdim, dstate, ngroups; /* b, H, P, N, G */
+    int32_t dtype;          /* ssd_dtype of x, dt, B, C and y */
+    int32_t dt_softplus;    /* 1: Delta = softplus(dt); 0: Delta = dt */
+    const void *x;          /* [b,H,P] dtype */
+    const void *dt;         /* [b,H]   dtype */
+    const float *A;         /* [H] fp32 */
+    const void *B;          /* [b,G,N] dtype */
+    const void *C;          /* [b,G,N] dtype */
+    const float *D;         /* [H] fp32, or NULL for no skip term */
+    float *state;           /* [b,H,P,N] fp32, read and overwritten */
+    void *y;                /* [b,H,P] dtype, out */
+} ssd_step_args;
+
+ssd_status ssd_step(const ssd_step_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

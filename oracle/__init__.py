@@ -129,6 +129,18 @@ def forward(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, nseq=None
     return OracleResult(y, fs, ces)
 
 
+def step(x, dt, A, B, C, state, D=None, dt_softplus=True):
+    """One step of the recurrence for one new token per batch row (the
+    recurrent, constant-memory mode of section 3.1 of "Mamba 2 -- Transformers
+    are SSMs"): the literal recurrence above run over a sequence of length 1
+    that starts from ``state``.  Shapes: x[b,H,P], dt[b,H], A[H], B,C[b,G,N],
+    state[b,H,P,N].  Returns (y[b,H,P], new state[b,H,P,N]) in fp64; ``state`` is
+    not modified."""
+    x, dt, B, C = _f64(x), _f64(dt), _f64(B), _f64(C)
+    r = forward(x[:, None], dt[:, None], A, B[:, None], C[:, None], D, state, dt_softplus=dt_softplus)
+    return r.y[:, 0], r.final_states
+
+
 def chunk_cumsum(dt, A, chunk, dt_softplus=True, seq_idx=None):
     """Delta and the within-chunk (and within-segment) inclusive cumsum of
     Delta*A, both [b,H,nc,Q] fp64."""

@@ -312,6 +312,26 @@ ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, 
     return run_scan<E>(s, a, delta, cs, cb, states, st);
 }
 
+template <typename E>
+ssd_status run_step(const ssd_step_args *a, hipStream_t st)
+{
+    const int N = (int)a->dstate, P = (int)a->headdim;
+    const int need = N / 4;   // lanes per state row
+    auto launch = [&](auto nl) {
+        constexpr int NL = decltype(nl)::value;
+        const dim3 grid((unsigned)(a->batch * a->nheads), (unsigned)((P + step_rows<NL>() - 1) / step_rows<NL>()));
+        hipLaunchKernelGGL((k_ssd_step<E, NL>), grid, dim3(kThreads), 0, st, (const E *)a->x, (const E *)a->dt,
+                           a->A, (const E *)a->B, (const E *)a->C, a->D, a->state, (E *)a->y, (int)a->nheads,
+                           (int)a->ngroups, P, N, (int)a->dt_softplus);
+        return launched();
+    };
+    if (need <= 4) return launch(std::integral_constant<int, 4>{});
+    if (need <= 8) return launch(std::integral_constant<int, 8>{});
+    if (need <= 16) return launch(std::integral_constant<int, 16>{});
+    if (need <= 32) return launch(std::integral_constant<int, 32>{});
+    return launch(std::integral_constant<int, 64>{});
+}
+
 const char *const kStatusText[] = {
     "ok",
     "a required pointer is NULL",
@@ -462,6 +482,34 @@ ssd_status ssd_chunk_scan(const ssd_fwd_args *args, const float *delta, const fl
     return s.dtype == SSD_DTYPE_BF16
                ? run_scan<bf16>(s, args, delta, cs, (const bf16 *)cb, (const bf16 *)states, st)
                : run_scan<float>(s, args, delta, cs, (const float *)cb, (const float *)states, st);
+}
+
+ssd_status ssd_step(const ssd_step_args *a, void *stream)
+{
+    if (!a) return SSD_ERR_NULL_POINTER;
+    if (a->dtype != SSD_DTYPE_F32 && a->dtype != SSD_DTYPE_BF16) return SSD_ERR_BAD_DTYPE;
+    if (a->batch < 1 || a->nheads < 1 || a->headdim < 16 || a->dstate < 16 || a->ngroups < 1)
+        return SSD_ERR_BAD_SHAPE;
+    if (a->headdim % 16 != 0 || a->dstate % 16 != 0 || a->dstate > kMaxStateDim || a->headdim > 4096)
+        return SSD_ERR_BAD_SHAPE;
+    if (a->batch > kMaxDim || a->nheads > kMaxDim || a->batch * a->nheads > INT32_MAX) return SSD_ERR_BAD_SHAPE;
+    if (a->nheads % a->ngroups != 0) return SSD_ERR_GROUPS;
+    if (!a->x || !a->dt || !a->A || !a->B || !a->C || !a->state || !a->y) return SSD_ERR_NULL_POINTER;
+    const void *ptrs[] = {a->x, a->dt, a->A, a->B, a->C, a->D, a->state, a->y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+    const size_t esz = a->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    const int64_t bH = a->batch * a->nheads;
+    const Range xr{a->x, (size_t)(bH * a->headdim) * esz}, dtr{a->dt, (size_t)bH * esz},
+        Ar{a->A, (size_t)a->nheads * 4}, Br{a->B, (size_t)(a->batch * a->ngroups * a->dstate) * esz},
+        Cr{a->C, (size_t)(a->batch * a->ngroups * a->dstate) * esz}, Dr{a->D, (size_t)a->nheads * 4},
+        sr{a->state, (size_t)(bH * a->headdim * a->dstate) * 4}, yr{a->y, xr.n};
+    const Range ins[] = {xr, dtr, Ar, Br, Cr, Dr};
+    for (const Range &o : ins)
+        if (overlaps(sr, o) || overlaps(yr, o)) return SSD_ERR_ALIASING;
+    if (overlaps(sr, yr)) return SSD_ERR_ALIASING;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return a->dtype == SSD_DTYPE_BF16 ? run_step<bf16>(a, st) : run_step<float>(a, st);
 }
 
 }  // extern "C"

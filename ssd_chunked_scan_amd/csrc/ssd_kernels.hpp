@@ -1328,4 +1328,72 @@ __global__ void k_fill_final(float *__restrict__ out, const float *__restrict__ 
     if (i < n) out[i] = init ? init[i] : 0.f;
 }
 
+// ---------------------------------------------------------------------------
+// Decode step: one new token per batch row, the state updated in place
+// ---------------------------------------------------------------------------
+// The recurrence itself, one step of it (section 3.1 of "Mamba 2 --
+// Transformers are SSMs"): with a = exp(Delta A_h),
+//   state[p][n] <- a state[p][n] + Delta x_p B_n,   y_p = sum_n C_n state[p][n] + D_h x_p.
+// One workgroup per (b, h, block of RP*PASSES rows p).  A state row of N fp32 is
+// covered by NL lanes (the power of two >= N/4), four consecutive n per lane, so
+// every state access is 16 bytes; RP = 256/NL rows per pass.  Every state load of
+// the workgroup is issued before any arithmetic; y_p is the sum of the row's
+// lanes, combined with xor shuffles inside each NL-lane group.
+template <int NL> constexpr int step_passes() { return NL / 4 < 8 ? NL / 4 : 8; }
+template <int NL> constexpr int step_rows() { return (kThreads / NL) * step_passes<NL>(); }
+
+template <typename E, int NL>
+__global__ __launch_bounds__(kThreads) void k_ssd_step(
+    const E *__restrict__ x, const E *__restrict__ dt, const float *__restrict__ A, const E *__restrict__ Bm,
+    const E *__restrict__ Cm, const float *__restrict__ D, float *__restrict__ state, E *__restrict__ y, int H,
+    int G, int P, int N, int softplus)
+{
+    constexpr int RP = kThreads / NL, PASSES = step_passes<NL>();
+    const int bh = blockIdx.x;   // b * H + h
+    const int h = bh % H, b = bh / H;
+    const int g = h / (H / G);
+    const int p0 = blockIdx.y * RP * PASSES;
+    const int li = threadIdx.x % NL, r = threadIdx.x / NL;
+    const int n = 4 * li;
+    const bool nin = n < N;   // N is a multiple of 16, so n + 3 < N too
+    float *srow = state + (int64_t)bh * P * N;
+
+    floatx4 hv[PASSES];
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int p = p0 + r + i * RP;
+        hv[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (p < P && nin) hv[i] = *reinterpret_cast<const floatx4 *>(srow + (int64_t)p * N + n);
+    }
+    float bv[4] = {0.f, 0.f, 0.f, 0.f}, cv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (nin) {
+        load4_f32(Bm + ((int64_t)b * G + g) * N + n, bv);
+        load4_f32(Cm + ((int64_t)b * G + g) * N + n, cv);
+    }
+    float xv[PASSES];
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int p = p0 + r + i * RP;
+        xv[i] = p < P ? to_float(x[(int64_t)bh * P + p]) : 0.f;
+    }
+    const float z = to_float(dt[bh]);
+    const float delta = softplus ? softplus_f(z) : z;
+    const float a = exp2_(delta * A[h] * kLog2e);
+    const float Dh = D ? D[h] : 0.f;
+
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int p = p0 + r + i * RP;
+        const float dx = delta * xv[i];
+        floatx4 hn;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hn[q] = fmaf(a, hv[i][q], dx * bv[q]);
+        if (p < P && nin) *reinterpret_cast<floatx4 *>(srow + (int64_t)p * N + n) = hn;
+        float part = cv[0] * hn[0] + cv[1] * hn[1] + cv[2] * hn[2] + cv[3] * hn[3];
+#pragma unroll
+        for (int m = NL / 2; m > 0; m >>= 1) part += __shfl_xor(part, m, NL);
+        if (li == 0 && p < P) y[(int64_t)bh * P + p] = from_float<E>(part + Dh * xv[i]);
+    }
+}
+
 }  // namespace ssd

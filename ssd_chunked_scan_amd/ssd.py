@@ -6,9 +6,10 @@ the current HIP stream.  Tensors must already be contiguous, on the GPU and of
 the documented dtypes; nothing is copied or converted silently.  If the library
 is missing the first call raises, there is no fallback.
 
-Names follow the C ABI: ``fwd`` (= ``ssd_fwd``) and the per-step entry points
+Names follow the C ABI: ``fwd`` (= ``ssd_fwd``), the per-step entry points
 ``chunk_cumsum``, ``chunk_cb``, ``chunk_state``, ``state_passing``,
-``seq_final_states``, ``chunk_scan``.
+``seq_final_states``, ``chunk_scan``, and the decode step ``step`` (=
+``ssd_step``).
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
 EXPORTED = ["ssd_abi_version", "ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd",
             "ssd_chunk_cumsum", "ssd_chunk_cb", "ssd_chunk_state", "ssd_state_passing",
-            "ssd_seq_final_states", "ssd_chunk_scan"]
+            "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step"]
 
 
 class FwdArgs(ctypes.Structure):
@@ -40,6 +41,18 @@ class FwdArgs(ctypes.Structure):
         ("initial_states", ctypes.c_void_p), ("seq_idx", ctypes.c_void_p), ("nseq", ctypes.c_int64),
         ("y", ctypes.c_void_p), ("final_states", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class StepArgs(ctypes.Structure):
+    """Mirror of ``ssd_step_args``."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("dt_softplus", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+        ("state", ctypes.c_void_p), ("y", ctypes.c_void_p),
     ]
 
 
@@ -74,6 +87,7 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_state_passing.argtypes = [P, vp, vp, vp]
     lib.ssd_seq_final_states.argtypes = [P, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.ssd_step.argtypes = [ctypes.POINTER(StepArgs), vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -270,4 +284,47 @@ def chunk_scan(p: Problem, delta, cs, cb, states, y=None, stream=None):
         p.call("ssd_chunk_scan", _ptr(delta), _ptr(cs), _ptr(cb), _ptr(states), stream=stream)
     finally:
         p.args.y = None
+    return y
+
+
+# ---------------------------------------------------------------------------
+# decode: one recurrence step per batch row, state updated in place
+# ---------------------------------------------------------------------------
+
+def step_args(x, dt, A, B, C, state, D=None, dt_softplus=True, y=None):
+    """Validated ``StepArgs`` (and y) for ``ssd_step``: x [b,H,P], dt [b,H], A [H],
+    B and C [b,G,N], state [b,H,P,N] fp32 (updated in place), D [H] or None."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, nheads, headdim]")
+    b, H, P = x.shape
+    if B.dim() != 3:
+        raise ValueError("B must be [batch, ngroups, dstate]")
+    G, N = B.shape[1], B.shape[2]
+    if x.dtype not in _DTYPES:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    _check(x, "x", device=dev)
+    _check(dt, "dt", x.dtype, (b, H), dev)
+    _check(A, "A", torch.float32, (H,), dev)
+    _check(B, "B", x.dtype, (b, G, N), dev)
+    _check(C, "C", x.dtype, (b, G, N), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    _check(state, "state", torch.float32, (b, H, P, N), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (b, H, P), dev)
+    a = StepArgs(batch=b, nheads=H, headdim=P, dstate=N, ngroups=G, dtype=_DTYPES[x.dtype],
+                 dt_softplus=1 if dt_softplus else 0, x=_ptr(x), dt=_ptr(dt), A=_ptr(A), B=_ptr(B),
+                 C=_ptr(C), D=_ptr(D), state=_ptr(state), y=_ptr(y))
+    return a, y
+
+
+def step(x, dt, A, B, C, state, D=None, dt_softplus=True, y=None, stream=None):
+    """y = one decode step (``ssd_step``); ``state`` is updated in place."""
+    a, y = step_args(x, dt, A, B, C, state, D, dt_softplus, y)
+    lib = load_library()
+    st = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    rc = lib.ssd_step(ctypes.byref(a), ctypes.c_void_p(st))
+    if rc != 0:
+        raise SSDError(rc, "ssd_step")
     return y

@@ -48,6 +48,30 @@ WORKLOADS = {
 }
 
 
+# Decode (one token per sequence, the state carried): the 2.7B-scale heads at a
+# serving batch of 64 sequences; the carried state ~ N(0, 0.5).  Seed 2000.
+DECODE = dict(name="decode_2.7B_bf16_b64_H80_N128", batch=64, nheads=80, headdim=64, dstate=128,
+              ngroups=1, dtype="bf16", dt_mean=-2.0, init_std=0.5)
+
+
+@dataclass
+class StepInputs:
+    x: torch.Tensor                 # [b,H,P]  dtype
+    dt: torch.Tensor                # [b,H]    dtype (raw, softplus applied downstream)
+    A: torch.Tensor                 # [H] fp32
+    B: torch.Tensor                 # [b,G,N]  dtype
+    C: torch.Tensor                 # [b,G,N]  dtype
+    D: Optional[torch.Tensor]       # [H] fp32
+    state: torch.Tensor             # [b,H,P,N] fp32, the carried state
+    dt_softplus: bool = True
+    name: str = ""
+
+    def to(self, device) -> "StepInputs":
+        mv = lambda t: None if t is None else t.to(device).contiguous()
+        return StepInputs(mv(self.x), mv(self.dt), mv(self.A), mv(self.B), mv(self.C), mv(self.D),
+                          mv(self.state), self.dt_softplus, self.name)
+
+
 @dataclass
 class Inputs:
     x: torch.Tensor                 # [b,T,H,P]  workload dtype
@@ -146,3 +170,25 @@ def workload(idx: int, **overrides) -> Inputs:
     seed = cfg.pop("seed", 1000 + idx)
     return make_inputs(seed=seed, name=name, **cfg)
 
+
+def token(inp: "Inputs", t: int, state: Optional[torch.Tensor] = None) -> StepInputs:
+    """Token t of every batch row of ``inp`` as decode-step inputs, carrying
+    ``state`` (default: ``inp``'s initial states, or zeros)."""
+    b, T, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    if state is None:
+        state = inp.initial_states if inp.initial_states is not None else torch.zeros(b, H, P, N)
+    c = lambda a: a[:, t].contiguous()
+    return StepInputs(c(inp.x), c(inp.dt), inp.A, c(inp.B), c(inp.C), inp.D, state.contiguous(),
+                      inp.dt_softplus, inp.name)
+
+
+def decode_inputs(seed: int = 2000, **overrides) -> StepInputs:
+    """The seeded decode-step inputs (``DECODE``, optionally with shape
+    overrides): one token per batch row drawn by the same recipe as the
+    forward workloads, and a carried state ~ N(0, init_std)."""
+    cfg = dict(DECODE)
+    cfg.update(overrides)
+    inp = make_inputs(cfg["batch"], 1, cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"], 64,
+                      cfg["dtype"], seed, dt_mean=cfg["dt_mean"], init_std=cfg["init_std"], name=cfg["name"])
+    return token(inp, 0)

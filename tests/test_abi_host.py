@@ -118,3 +118,40 @@ def test_binding_rejects_host_tensors_and_copies():
     x = torch.zeros(1, 64, 2, 16)
     with pytest.raises(ValueError, match="GPU"):
         ssd.Problem(x, x[..., 0], torch.zeros(2), x[:, :, :1], x[:, :, :1], 64)
+
+
+def _step_args(**kw):
+    base = dict(batch=8, nheads=4, headdim=64, dstate=128, ngroups=1, dtype=1, dt_softplus=1)
+    base.update({k: v for k, v in kw.items() if k in base})
+    a = ssd.StepArgs(**base)
+    addr = 0x10000000
+    for name in ("x", "dt", "A", "B", "C", "D", "state", "y"):
+        setattr(a, name, kw.get(name, addr))
+        addr += 0x10000000
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), DTYPE),
+    (dict(nheads=6, ngroups=4), GROUPS),
+    (dict(headdim=24), SHAPE), (dict(dstate=40), SHAPE), (dict(dstate=272), SHAPE),
+    (dict(batch=0), SHAPE), (dict(headdim=0), SHAPE), (dict(batch=1 << 20, nheads=1 << 12), SHAPE),
+    (dict(x=0), NULLP), (dict(dt=0), NULLP), (dict(A=0), NULLP), (dict(B=0), NULLP), (dict(C=0), NULLP),
+    (dict(state=0), NULLP), (dict(y=0), NULLP),
+    (dict(x=0x10000008), MISAL), (dict(state=0x70000004), MISAL), (dict(D=0x60000002), MISAL),
+    (dict(y=0x10000000), ALIAS),                 # y == x
+    (dict(state=0x40000000), ALIAS),             # state == B
+    (dict(y=0x70000000 + 1024), ALIAS),          # y inside the state
+])
+def test_step_rejects_invalid_arguments(lib, kw, code):
+    assert lib.ssd_step(ctypes.byref(_step_args(**kw)), None) == code
+    assert lib.ssd_step(None, None) == NULLP
+
+
+def test_step_binding_checks_shapes():
+    x = torch.zeros(2, 4, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        ssd.step_args(x, torch.zeros(2, 4), torch.zeros(4), torch.zeros(2, 1, 64), torch.zeros(2, 1, 64),
+                      torch.zeros(2, 4, 64, 64))
+    with pytest.raises(ValueError, match="batch, nheads, headdim"):
+        ssd.step_args(torch.zeros(2, 4, 1, 64), None, None, None, None, None)

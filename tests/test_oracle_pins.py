@@ -480,3 +480,49 @@ def test_chunk_cb_rebuilds_chunk_outputs(G, H):
                     W[t, s] = math.exp(cs[0, h, c, t] - cs[0, h, c, s]) * cb[0, c, g, t, s] * delta[0, h, c, s]
             y = W @ x[0, s0:e, h, :] + D[h] * x[0, s0:e, h, :]
             assert rel(y, one.y[0, :, h, :]) < 1e-13
+
+
+def test_step_replays_the_recurrence():
+    """oracle.step applied token after token, carrying its state, reproduces the
+    forward over the whole sequence: y of every token and the final state.  A
+    swapped axis or a mis-shaped operand in the step's marshalling fails here."""
+    inp = wl.make_inputs(2, 9, 4, 16, 16, 2, 64, "fp32", 5, init_std=0.5)
+    ref = _run(inp)
+    state = inp.initial_states.double().numpy()
+    for t in range(9):
+        s = wl.token(inp, t)
+        y, state = oracle.step(s.x, s.dt, s.A, s.B, s.C, state, s.D, s.dt_softplus)
+        assert np.allclose(y, ref.y[:, t], rtol=1e-12, atol=1e-14)
+    assert np.allclose(state, ref.final_states, rtol=1e-12, atol=1e-14)
+
+
+def test_step_closed_forms():
+    """Two cases with a closed form ("Mamba 2 -- Transformers are SSMs", section
+    3.1, one step of the recurrence):
+    - zero state, x one-hot at row p: only row p of the new state is nonzero and it
+      equals Delta * B_g (head h uses group h*G/H), so y_p = Delta * C_g.B_g + D x_p;
+    - A = 0 with the raw step size: nothing decays, state' = state + dt x B^T."""
+    b, H, P, N, G = 1, 4, 3, 5, 2
+    rng = np.random.default_rng(3)
+    Bv = rng.standard_normal((b, G, N))
+    Cv = rng.standard_normal((b, G, N))
+    dt = np.array([[0.3, -0.2, 1.1, 0.05]])
+    A = np.array([-1.0, -2.0, -0.5, -4.0])
+    D = np.array([0.5, -1.0, 2.0, 0.0])
+    x = np.zeros((b, H, P))
+    x[0, :, 1] = 1.0
+    y, st = oracle.step(x, dt, A, Bv, Cv, np.zeros((b, H, P, N)), D, dt_softplus=True)
+    for h in range(H):
+        g = h * G // H
+        delta = math.log1p(math.exp(dt[0, h]))
+        want = np.zeros((P, N))
+        want[1] = delta * Bv[0, g]
+        assert np.allclose(st[0, h], want, rtol=1e-14, atol=1e-15)
+        assert y[0, h, 1] == pytest.approx(delta * float(Cv[0, g] @ Bv[0, g]) + D[h], rel=1e-13)
+        assert y[0, h, 0] == 0.0 and y[0, h, 2] == 0.0
+    x = rng.standard_normal((b, H, P))
+    s0 = rng.standard_normal((b, H, P, N))
+    _, st = oracle.step(x, dt, np.zeros(H), Bv, Cv, s0, None, dt_softplus=False)
+    for h in range(H):
+        g = h * G // H
+        assert np.allclose(st[0, h], s0[0, h] + dt[0, h] * np.outer(x[0, h], Bv[0, g]), rtol=1e-13, atol=1e-14)
