@@ -9,6 +9,10 @@ this module only converts arrays to contiguous fp64 and back.  Inputs given in
 bf16 or fp32 are upcast exactly, so the oracle sees the very values the GPU
 sees.
 
+``backward`` is the reverse-mode derivative of that recurrence (the chain rule
+applied step by step in reverse; the pages give no backward equations), and
+``step`` is the recurrence over one token (the decode step).
+
 ``forward`` follows the literal recurrence of the "Mamba 2 -- Transformers are
 SSMs" paper story (ai.tomabc.com), section 3.1: ``h_t = a_t h_{t-1} +
 Delta_t B_t x_t^T``, ``y_t = C_t^T h_t`` (+ ``D x_t``), with ``a_t =
@@ -57,6 +61,8 @@ def load():
         lib.ssd_oracle_chunk_cumsum.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 5
         lib.ssd_oracle_chunk_cumsum.restype = ctypes.c_int
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
+        lib.ssd_oracle_backward.argtypes = [ctypes.POINTER(_BwdArgs)]
+        lib.ssd_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -127,6 +133,53 @@ def forward(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, nseq=None
     if rc != 0:
         raise ValueError(f"ssd_oracle_forward failed with status {rc}")
     return OracleResult(y, fs, ces)
+
+
+class _BwdArgs(ctypes.Structure):
+    _fields_ = [("f", _Args), ("dy", ctypes.c_void_p), ("dfinal", ctypes.c_void_p), ("dx", ctypes.c_void_p),
+                ("ddt", ctypes.c_void_p), ("dA", ctypes.c_void_p), ("dB", ctypes.c_void_p),
+                ("dC", ctypes.c_void_p), ("dD", ctypes.c_void_p), ("dinit", ctypes.c_void_p)]
+
+
+@dataclass
+class OracleGrads:
+    dx: np.ndarray       # [b,T,H,P]
+    ddt: np.ndarray      # [b,T,H]
+    dA: np.ndarray       # [H]
+    dB: np.ndarray       # [b,T,G,N]
+    dC: np.ndarray       # [b,T,G,N]
+    dD: Optional[np.ndarray]      # [H] (None when D is None)
+    dinit: np.ndarray    # [b,H,P,N]
+
+
+def backward(x, dt, A, B, C, dy, D=None, initial_states=None, dfinal=None, seq_idx=None, nseq=None,
+             dt_softplus=True) -> OracleGrads:
+    """Gradients of L = sum(y * dy) + sum(final_states * dfinal) with respect to
+    every input of ``forward``: the chain rule applied to the recurrence, one
+    step at a time in reverse (see ``ssd_oracle_backward`` in ``ssd_oracle.c``)."""
+    x, dt, A, B, C, dy = map(_f64, (x, dt, A, B, C, dy))
+    D, init, dfin = _f64(D), _f64(initial_states), _f64(dfinal)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dy.shape == x.shape
+    sidx = None
+    if seq_idx is not None:
+        if hasattr(seq_idx, "detach"):
+            seq_idx = seq_idx.detach().cpu().numpy()
+        sidx = np.ascontiguousarray(np.asarray(seq_idx).reshape(-1), dtype=np.int32)
+        if nseq is None:
+            nseq = int(sidx.max()) + 1
+    out = OracleGrads(np.zeros_like(x), np.zeros((b, T, H)), np.zeros(H), np.zeros((b, T, G, N)),
+                      np.zeros((b, T, G, N)), None if D is None else np.zeros(H), np.zeros((b, H, P, N)))
+    f = _Args(b, T, H, P, N, G, int(bool(dt_softplus)),
+              _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(sidx),
+              int(nseq or 0), None, 0, 0, None, None, None)
+    args = _BwdArgs(f, _ptr(dy), _ptr(dfin), _ptr(out.dx), _ptr(out.ddt), _ptr(out.dA), _ptr(out.dB),
+                    _ptr(out.dC), _ptr(out.dD), _ptr(out.dinit))
+    rc = load().ssd_oracle_backward(ctypes.byref(args))
+    if rc != 0:
+        raise ValueError(f"ssd_oracle_backward failed with status {rc}")
+    return out
 
 
 def step(x, dt, A, B, C, state, D=None, dt_softplus=True):

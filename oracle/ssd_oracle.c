@@ -210,3 +210,179 @@ int ssd_oracle_chunk_cumsum(int64_t batch, int64_t T, int64_t H, int64_t Q, int3
             }
     return ORACLE_OK;
 }
+
+/*
+ * Reverse-mode derivative of the forward recurrence above (no chunking): the
+ * gradients of L = sum y * dy + sum final_states * dfinal with respect to every
+ * input.  The pages give no backward equations, so this is the chain rule
+ * applied to the recurrence of ssd_oracle_forward, step by step in reverse:
+ *
+ *   g_t   = dL/dh_t = C_t dy_t^T  (+ dfinal at a sequence's last token)
+ *                     + [carry into t+1] a_{t+1} g_{t+1}
+ *   dx_t  = Delta_t g_t B_t + D dy_t          dB_t += Delta_t g_t^T x_t
+ *   dC_t += h_t^T dy_t                        dDelta_t = x_t . (g_t B_t) + A dl_t
+ *   dl_t  = [carry into t] a_t <g_t, h_{t-1}> (l_t = Delta_t A = log a_t)
+ *   dA   += Delta_t dl_t                      dD += dy_t . x_t
+ *   ddt_t = dDelta_t * sigmoid(dt_t)  (softplus' = sigmoid; or dDelta_t for raw dt)
+ *   dinit = a_0 g_0
+ *
+ * dB and dC sum over the heads of a group, dA and dD over batch rows and time.
+ * The forward states h_t of one (b, h, p) row are kept (T x N doubles), so the
+ * derivative needs no identity beyond the chain rule.  Partial sums are reduced
+ * in a fixed order, so results do not depend on the thread count.
+ */
+typedef struct {
+    ssd_oracle_args f;       /* forward problem (its y / final_states / chunk fields are ignored) */
+    const double *dy;        /* [b,T,H,P] */
+    const double *dfinal;    /* [b,H,P,N], or [nseq,H,P,N] with seq_idx; NULL = zero */
+    double *dx;              /* [b,T,H,P] */
+    double *ddt;             /* [b,T,H] */
+    double *dA;              /* [H] */
+    double *dB, *dC;         /* [b,T,G,N] */
+    double *dD;              /* [H] (may be NULL) */
+    double *dinit;           /* [b,H,P,N] (may be NULL) */
+} ssd_oracle_bwd_args;
+
+int ssd_oracle_backward(const ssd_oracle_bwd_args *ba)
+{
+    if (!ba) return ORACLE_BAD_ARGS;
+    const ssd_oracle_args *a = &ba->f;
+    if (!a->x || !a->dt || !a->A || !a->B || !a->C || !ba->dy) return ORACLE_BAD_ARGS;
+    if (!ba->dx || !ba->ddt || !ba->dA || !ba->dB || !ba->dC) return ORACLE_BAD_ARGS;
+    const int64_t Bt = a->batch, T = a->seqlen, H = a->nheads, P = a->headdim;
+    const int64_t N = a->dstate, G = a->ngroups;
+    if (Bt < 1 || T < 1 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0) return ORACLE_BAD_ARGS;
+    if (a->seq_idx && (Bt != 1 || a->nseq < 1)) return ORACLE_BAD_ARGS;
+    const int64_t units = Bt * H;
+    /* per-(b,h) partial sums, reduced in a fixed order afterwards */
+    double *pdB = (double *)calloc((size_t)(units * T * N), sizeof(double));
+    double *pdC = (double *)calloc((size_t)(units * T * N), sizeof(double));
+    double *pdA = (double *)calloc((size_t)units, sizeof(double));
+    double *pdD = (double *)calloc((size_t)units, sizeof(double));
+    if (!pdB || !pdC || !pdA || !pdD) {
+        free(pdB); free(pdC); free(pdA); free(pdD);
+        return ORACLE_NO_MEMORY;
+    }
+    int status = ORACLE_OK;
+
+#pragma omp parallel
+    {
+        double *hs = (double *)malloc((size_t)(T * N) * sizeof(double));  /* h_t of one row */
+        double *g = (double *)malloc((size_t)N * sizeof(double));
+        double *dDelta = (double *)malloc((size_t)T * sizeof(double));
+        double *dl = (double *)malloc((size_t)T * sizeof(double));
+        if (!hs || !g || !dDelta || !dl) {
+#pragma omp atomic write
+            status = ORACLE_NO_MEMORY;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            if (!hs || !g || !dDelta || !dl) continue;
+            const int64_t h = u % H, b = u / H, g_ = h * G / H;
+            const double Ah = a->A[h], Dh = a->D ? a->D[h] : 0.0;
+            double *uB = pdB + u * T * N, *uC = pdC + u * T * N;
+            for (int64_t t = 0; t < T; ++t) dDelta[t] = dl[t] = 0.0;
+            for (int64_t p = 0; p < P; ++p) {
+                /* forward sweep of this row, keeping every h_t */
+                for (int64_t t = 0; t < T; ++t) {
+                    const int64_t bt = b * T + t;
+                    const double z = a->dt[bt * H + h];
+                    const double delta = a->dt_softplus ? softplus(z) : z;
+                    const double decay = exp(delta * Ah);
+                    const int keep = !(a->seq_idx && t > 0 && a->seq_idx[t] != a->seq_idx[t - 1]);
+                    const double xv = a->x[(bt * H + h) * P + p];
+                    const double *Bv = a->B + (bt * G + g_) * N;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double prev = t == 0 ? (a->initial_states ? a->initial_states[((b * H + h) * P + p) * N + n] : 0.0)
+                                                   : hs[(t - 1) * N + n];
+                        hs[t * N + n] = (keep ? decay * prev : 0.0) + delta * Bv[n] * xv;
+                    }
+                }
+                /* reverse sweep */
+                for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
+                for (int64_t t = T - 1; t >= 0; --t) {
+                    const int64_t bt = b * T + t;
+                    const double z = a->dt[bt * H + h];
+                    const double delta = a->dt_softplus ? softplus(z) : z;
+                    const double decay = exp(delta * Ah);
+                    const int keep = !(a->seq_idx && t > 0 && a->seq_idx[t] != a->seq_idx[t - 1]);
+                    const double xv = a->x[(bt * H + h) * P + p];
+                    const double dyv = ba->dy[(bt * H + h) * P + p];
+                    const double *Bv = a->B + (bt * G + g_) * N;
+                    const double *Cv = a->C + (bt * G + g_) * N;
+                    /* dfinal enters at the last token of the row (or of each segment) */
+                    if (ba->dfinal) {
+                        int64_t row = -1;
+                        if (!a->seq_idx) {
+                            if (t == T - 1) row = b;
+                        } else if (t == T - 1 || a->seq_idx[t + 1] != a->seq_idx[t]) {
+                            row = a->seq_idx[t];
+                            if (row < 0 || row >= a->nseq) row = -1;
+                        }
+                        if (row >= 0)
+                            for (int64_t n = 0; n < N; ++n) g[n] += ba->dfinal[((row * H + h) * P + p) * N + n];
+                    }
+                    for (int64_t n = 0; n < N; ++n) g[n] += Cv[n] * dyv;
+                    double gB = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        gB += g[n] * Bv[n];
+                        uC[t * N + n] += hs[t * N + n] * dyv;
+                        uB[t * N + n] += delta * xv * g[n];
+                    }
+                    ba->dx[(bt * H + h) * P + p] = delta * gB + Dh * dyv;
+                    dDelta[t] += xv * gB;
+                    pdD[u] += dyv * xv;
+                    if (keep) {
+                        double gh = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double prev = t == 0 ? (a->initial_states ? a->initial_states[((b * H + h) * P + p) * N + n] : 0.0)
+                                                       : hs[(t - 1) * N + n];
+                            gh += g[n] * prev;
+                        }
+                        dl[t] += decay * gh;
+                        for (int64_t n = 0; n < N; ++n) g[n] *= decay;
+                    } else {
+                        for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
+                    }
+                }
+                if (ba->dinit)
+                    for (int64_t n = 0; n < N; ++n) ba->dinit[((b * H + h) * P + p) * N + n] = g[n];
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t bt = b * T + t;
+                const double z = a->dt[bt * H + h];
+                const double delta = a->dt_softplus ? softplus(z) : z;
+                const double dd = dDelta[t] + Ah * dl[t];
+                const double sig = z >= 0.0 ? 1.0 / (1.0 + exp(-z)) : exp(z) / (1.0 + exp(z));
+                ba->ddt[bt * H + h] = a->dt_softplus ? dd * sig : dd;
+                pdA[u] += delta * dl[t];
+            }
+        }
+        free(hs); free(g); free(dDelta); free(dl);
+    }
+    if (status == ORACLE_OK) {
+        for (int64_t h = 0; h < H; ++h) {
+            double sa = 0.0, sd = 0.0;
+            for (int64_t b = 0; b < Bt; ++b) {
+                sa += pdA[b * H + h];
+                sd += pdD[b * H + h];
+            }
+            ba->dA[h] = sa;
+            if (ba->dD) ba->dD[h] = sd;
+        }
+        for (int64_t b = 0; b < Bt; ++b)
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t g_ = 0; g_ < G; ++g_)
+                    for (int64_t n = 0; n < N; ++n) {
+                        double sb = 0.0, sc = 0.0;
+                        for (int64_t h = g_ * (H / G); h < (g_ + 1) * (H / G); ++h) {
+                            sb += pdB[((b * H + h) * T + t) * N + n];
+                            sc += pdC[((b * H + h) * T + t) * N + n];
+                        }
+                        ba->dB[((b * T + t) * G + g_) * N + n] = sb;
+                        ba->dC[((b * T + t) * G + g_) * N + n] = sc;
+                    }
+    }
+    free(pdB); free(pdC); free(pdA); free(pdD);
+    return status;
+}
