@@ -205,6 +205,48 @@ typedef struct {
 
 ssd_status ssd_step(const ssd_step_args *args, void *stream);
 
+/*
+ * Backward: the gradients of L = sum(y * dy) + sum(final_states * dfinal) with
+ * respect to every input of ssd_fwd, for a forward WITHOUT seq_idx (packed
+ * streams return SSD_ERR_SEQ_IDX).  The pages give no backward equations; these
+ * are the chain rule applied to the recurrence at the top of this header,
+ * organised by chunks like the forward:
+ *
+ *   g_t = dL/dh_t,  dx_t = Delta_t g_t B_t + D dy_t,  dB_t = sum_heads Delta_t g_t^T x_t,
+ *   dC_t = sum_heads h_t^T dy_t,  dDelta_t = x_t.(g_t B_t) + A dl_t with
+ *   dl_t = a_t <g_t, h_{t-1}>,  ddt = dDelta * sigmoid(dt) (dt_softplus) or dDelta,
+ *   dA = sum Delta dl,  dD = sum dy.x,  dinit = a_0 g_0.
+ *
+ * `args` describes the forward exactly as it was run (shape, dtype, x, dt, A, B,
+ * C, D, initial_states; seq_idx NULL) and args->y must hold its output y (an
+ * input here).  Its final_states, workspace and workspace_bytes fields are
+ * ignored: the chunk intermediates are recomputed in the backward's own
+ * workspace.
+ */
+typedef struct {
+    const void *dy;                /* [b,T,H,P] dtype */
+    const float *dfinal_states;    /* [b,H,P,N] fp32, or NULL for zero */
+    void *dx;                      /* [b,T,H,P] dtype, out */
+    void *ddt;                     /* [b,T,H]   dtype, out (gradient with respect to dt as passed) */
+    float *dA;                     /* [H] fp32, out */
+    void *dB;                      /* [b,T,G,N] dtype, out */
+    void *dC;                      /* [b,T,G,N] dtype, out */
+    float *dD;                     /* [H] fp32, out, or NULL */
+    float *dinitial_states;        /* [b,H,P,N] fp32, out, or NULL */
+    void *workspace;               /* device scratch, >= ssd_bwd_workspace_size */
+    size_t workspace_bytes;
+} ssd_bwd_args;
+
+/* Workspace bytes ssd_bwd needs for the forward problem `args` (shape and dtype
+ * fields only). */
+ssd_status ssd_bwd_workspace_size(const ssd_fwd_args *args, size_t *bytes);
+
+/* The backward pass.  All outputs are overwritten; gradients summed over heads
+ * (dB, dC), over batch rows and time (dA, dD) are reduced in a fixed order, so
+ * results are deterministic.  Outputs must not overlap the inputs, each other
+ * or the workspace. */
+ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *grads, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@
 #include <type_traits>
 
 #include "ssd_kernels.hpp"
+#include "ssd_bwd_kernels.hpp"
 
 using namespace ssd;
 
@@ -273,11 +274,32 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
             if (s.packed)
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, true>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
-                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
+                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
+                                   (float *)nullptr, (float *)nullptr);
             else
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
-                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp);
+                                   (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
+                                   (float *)nullptr, (float *)nullptr);
+            return launched();
+        });
+    });
+}
+
+// chunk_scan in a dot mode (non-packed): DOT = 1 with P1ONLY (entering-state dot
+// only, no y), or DOT = 2 (y written, both dots) on a chunk-reversed problem.
+template <typename E, int DOT, bool P1ONLY>
+ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
+                        const E *hin, const E *vec, float *dot1, float *dot2, hipStream_t st)
+{
+    const int ntp = (int)((s.P + 63) / 64);
+    dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
+    return with_q(s.Q, [&](auto q) {
+        return with_nt(s.N, [&](auto nt) {
+            constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+            hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false, DOT, P1ONLY>), grid, dim3(scan_threads<Q>()), 0, st,
+                               (const E *)a->x, delta, cs, cb, hin, a->D, (const int32_t *)nullptr, (E *)a->y,
+                               (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, vec, dot1, dot2);
             return launched();
         });
     });
@@ -330,6 +352,177 @@ ssd_status run_step(const ssd_step_args *a, hipStream_t st)
     if (need <= 16) return launch(std::integral_constant<int, 16>{});
     if (need <= 32) return launch(std::integral_constant<int, 32>{});
     return launch(std::integral_constant<int, 64>{});
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+struct BwdWorkspace {
+    size_t delta, cs, cb, states, gstates, cbr, dyr, br, cr, csr, dlr, ypr, yo, zo, xyp, rpart, cpart, bnd, dyx,
+        mrow, mcol, dA_part, dD_part, total;
+};
+
+BwdWorkspace bwd_workspace_layout(const Shape &s)
+{
+    BwdWorkspace w;
+    const size_t dcs = (size_t)(s.b * s.H * s.nc * s.Q) * 4;
+    const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * (s.Q + 2 * nt_of(s.N))) * s.esz;
+    const size_t sts = (size_t)(s.b * s.nc * s.H * s.P * s.N) * s.esz;
+    const size_t xs = (size_t)(s.b * s.T * s.H * s.P) * s.esz;
+    const size_t bcs = (size_t)(s.b * s.T * s.G * s.N) * s.esz;
+    const size_t ms = (size_t)(s.b * s.nc * s.G * s.Q * s.Q) * s.esz;
+    const size_t bh = (size_t)(s.b * s.H) * 4;
+    const size_t ntp = (size_t)((s.P + 63) / 64), qt = (size_t)(s.Q / 64);
+    size_t o = 0;
+    auto take = [&](size_t n) { const size_t at = o; o = align256(o + n); return at; };
+    w.delta = take(dcs);
+    w.cs = take(dcs);
+    w.cb = take(cbs);
+    w.states = take(sts);
+    w.gstates = take(sts);
+    w.cbr = take(cbs);
+    w.dyr = take(xs);
+    w.br = take(bcs);
+    w.cr = take(bcs);
+    w.csr = take(dcs);
+    w.dlr = take(dcs);
+    w.ypr = take(xs);
+    w.yo = take(ntp * dcs);
+    w.zo = take(ntp * dcs);
+    w.xyp = take(ntp * dcs);
+    w.rpart = take(qt * dcs);
+    w.cpart = take(qt * dcs);
+    w.bnd = take((size_t)(s.b * s.H * s.nc) * 4);
+    w.dyx = take(dcs);
+    w.mrow = take(ms);
+    w.mcol = take(ms);
+    w.dA_part = take(bh);
+    w.dD_part = take(bh);
+    w.total = o;
+    return w;
+}
+
+template <typename E>
+ssd_status run_state_grad(const Shape &s, const ssd_fwd_args *ar, const float *cs, const E *cbr, E *u,
+                          hipStream_t st)
+{
+    const int ntp = (int)((s.P + 63) / 64);
+    dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
+    return with_q(s.Q, [&](auto q) {
+        return with_nt(s.N, [&](auto nt) {
+            constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+            hipLaunchKernelGGL((k_chunk_state<E, Q, NT, false, true>), grid, dim3(kThreads), 0, st, (const E *)ar->x,
+                               cbr, (const E *)nullptr, ar->A, (const int32_t *)nullptr, (float *)nullptr,
+                               const_cast<float *>(cs), u, (int32_t *)nullptr, 0, (int)s.T, (int)s.H, (int)s.G,
+                               (int)s.P, (int)s.N, (int)s.nc, ntp, 0);
+            return launched();
+        });
+    });
+}
+
+template <typename E>
+ssd_status run_passing_rev(const Shape &s, const float *cs, E *gstates, const float *dfinal, float *dinit,
+                           hipStream_t st)
+{
+    const int64_t PN = s.P * s.N;
+    constexpr int VE = 4;
+    const int64_t vecs = s.b * s.H * PN / VE;
+    hipLaunchKernelGGL((k_state_passing<E, VE, true>), dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, gstates,
+                       cs, dfinal, dinit, (const int32_t *)nullptr, (int)s.T, (int)s.H, PN, (int)s.nc, (int)s.Q,
+                       vecs);
+    return launched();
+}
+
+template <typename E>
+ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *g, const BwdWorkspace &w,
+                     hipStream_t st)
+{
+    char *ws = static_cast<char *>(g->workspace);
+    auto F32 = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+    auto EP = [&](size_t off) { return reinterpret_cast<E *>(ws + off); };
+    float *delta = F32(w.delta), *cs = F32(w.cs), *csr = F32(w.csr), *dlr = F32(w.dlr);
+    float *yo = F32(w.yo), *zo = F32(w.zo), *xyp = F32(w.xyp), *rpart = F32(w.rpart), *cpart = F32(w.cpart);
+    float *bnd = F32(w.bnd), *dyx = F32(w.dyx), *dA_part = F32(w.dA_part), *dD_part = F32(w.dD_part);
+    E *cb = EP(w.cb), *states = EP(w.states), *gstates = EP(w.gstates), *cbr = EP(w.cbr), *dyr = EP(w.dyr);
+    E *br = EP(w.br), *cr = EP(w.cr), *ypr = EP(w.ypr), *mrow = EP(w.mrow), *mcol = EP(w.mcol);
+    ssd_status r;
+    // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
+    ssd_fwd_args f = *a;
+    f.final_states = nullptr;
+    if ((r = run_cb<E>(s, &f, cb, st)) != SSD_OK) return r;
+    if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st)) != SSD_OK) return r;
+    if ((r = run_passing<E>(s, &f, cs, states, nullptr, st)) != SSD_OK) return r;
+    // 2. every chunk's tokens in reversed order: dy, B, C, and the reversed cs / delta
+    constexpr int V = kVec16<E>;
+    const int64_t vx = s.b * s.T * s.H * s.P / V, vbc = s.b * s.T * s.G * s.N / V;
+    hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vx, 256)), dim3(256), 0, st, (const E *)g->dy, dyr,
+                       (int)s.T, (int)s.Q, s.H * s.P, vx);
+    hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vbc, 256)), dim3(256), 0, st, (const E *)a->B, br,
+                       (int)s.T, (int)s.Q, s.G * s.N, vbc);
+    hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vbc, 256)), dim3(256), 0, st, (const E *)a->C, cr,
+                       (int)s.T, (int)s.Q, s.G * s.N, vbc);
+    const int64_t ncs = s.b * s.H * s.nc * s.Q;
+    hipLaunchKernelGGL(k_bwd_reverse_cs, dim3(grid1(ncs, 256)), dim3(256), 0, st, cs, csr, dlr, (int)s.T, (int)s.Q,
+                       (int)s.nc, ncs);
+    if ((r = launched()) != SSD_OK) return r;
+    // 3. reversed-order problem: x <- dy, B <- C, C <- B, unit step size, no skip term
+    ssd_fwd_args rv = *a;
+    rv.x = dyr;
+    rv.B = cr;
+    rv.C = br;
+    rv.D = nullptr;
+    rv.y = ypr;
+    rv.initial_states = nullptr;
+    rv.final_states = nullptr;
+    if ((r = run_cb<E>(s, &rv, cbr, st)) != SSD_OK) return r;
+    // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
+    if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st)) != SSD_OK) return r;
+    if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, st)) != SSD_OK) return r;
+    // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y'
+    if ((r = run_scan_dot<E, 2, false>(s, &rv, dlr, csr, cbr, gstates, (const E *)a->x, zo, xyp, st)) != SSD_OK)
+        return r;
+    // 6. dy . (entering-state term of y), from the forward's entering states
+    if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st)) != SSD_OK)
+        return r;
+    // 7. dx, dy . x
+    const int64_t waves = s.b * s.T * s.H;
+    hipLaunchKernelGGL(k_bwd_token<E>, dim3(grid1(waves, kThreads / 64)), dim3(kThreads), 0, st, (const E *)a->x,
+                       (const E *)g->dy, (const E *)ypr, delta, a->D, (E *)g->dx, dyx, (int)s.T, (int)s.H, (int)s.P,
+                       (int)s.Q, (int)s.nc, waves);
+    // 8. M (summed over the group's heads) with the row / column sums of S; the boundary terms
+    const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
+    const int nnt = (int)((s.N + 63) / 64);
+    if ((r = with_q(s.Q, [&](auto q) {
+             return with_nt(s.N, [&](auto nt) {
+                 constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+                 hipLaunchKernelGGL((k_bwd_m<E, Q, NT>), dim3((unsigned)(ntri * s.nc * s.G), (unsigned)s.b),
+                                    dim3(kThreads), 0, st, (const E *)g->dy, (const E *)a->x, delta, cs, (const E *)cb,
+                                    mrow, mcol, rpart, cpart, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc);
+                 return launched();
+             });
+         })) != SSD_OK)
+        return r;
+    hipLaunchKernelGGL(k_bwd_bnd<E>, dim3((unsigned)(s.b * s.nc * s.H)), dim3(kThreads), 0, st, (const E *)gstates,
+                       (const E *)states, cs, bnd, (int)s.H, (int)s.nc, (int)s.Q, s.P * s.N);
+    // 9. dl, ddt, dA, dD
+    hipLaunchKernelGGL(k_bwd_dl<E>, dim3((unsigned)(s.b * s.H)), dim3(kThreads), 0, st, rpart, cpart, yo, zo, xyp,
+                       bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T, (int)s.H,
+                       (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), (int)a->dt_softplus);
+    hipLaunchKernelGGL(k_bwd_sum_heads, dim3(grid1(s.H, 64)), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
+                       (int)s.b, (int)s.H);
+    if ((r = launched()) != SSD_OK) return r;
+    // 10. dC and dB
+    return with_q(s.Q, [&](auto q) {
+        constexpr int Q = decltype(q)::value;
+        const dim3 grid((unsigned)(s.nc * s.G * qt * nnt), (unsigned)s.b);
+        hipLaunchKernelGGL((k_bwd_bc<E, Q, 0>), grid, dim3(kThreads), 0, st, (const E *)a->B, (const E *)mrow,
+                           (const E *)states, (const E *)g->dy, delta, cs, (E *)g->dC, (int)s.T, (int)s.H, (int)s.G,
+                           (int)s.P, (int)s.N, (int)s.nc, nnt);
+        hipLaunchKernelGGL((k_bwd_bc<E, Q, 1>), grid, dim3(kThreads), 0, st, (const E *)a->C, (const E *)mcol,
+                           (const E *)gstates, (const E *)a->x, delta, cs, (E *)g->dB, (int)s.T, (int)s.H,
+                           (int)s.G, (int)s.P, (int)s.N, (int)s.nc, nnt);
+        return launched();
+    });
 }
 
 const char *const kStatusText[] = {
@@ -510,6 +703,64 @@ ssd_status ssd_step(const ssd_step_args *a, void *stream)
     if (overlaps(sr, yr)) return SSD_ERR_ALIASING;
     hipStream_t st = static_cast<hipStream_t>(stream);
     return a->dtype == SSD_DTYPE_BF16 ? run_step<bf16>(a, st) : run_step<float>(a, st);
+}
+
+ssd_status ssd_bwd_workspace_size(const ssd_fwd_args *args, size_t *bytes)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if (s.packed) return SSD_ERR_SEQ_IDX;
+    if (!bytes) return SSD_ERR_NULL_POINTER;
+    *bytes = bwd_workspace_layout(s).total;
+    return SSD_OK;
+}
+
+ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if (s.packed) return SSD_ERR_SEQ_IDX;
+    if (!g) return SSD_ERR_NULL_POINTER;
+    if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB | kNeedC)) != SSD_OK) return r;
+    const bool empty = s.T == 0;
+    if (!g->dA) return SSD_ERR_NULL_POINTER;
+    if (!empty && (!args->y || !g->dy || !g->dx || !g->ddt || !g->dB || !g->dC)) return SSD_ERR_NULL_POINTER;
+    const void *ptrs[] = {args->y, g->dy, g->dfinal_states, g->dx, g->ddt, g->dA, g->dB, g->dC, g->dD,
+                          g->dinitial_states, g->workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+    const Sizes z = tensor_sizes(s);
+    const size_t st = (size_t)(s.b * s.H * s.P * s.N) * 4;
+    const BwdWorkspace w = bwd_workspace_layout(s);
+    if (!empty) {
+        if (!g->workspace) return SSD_ERR_NULL_POINTER;
+        if (g->workspace_bytes < w.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    }
+    const Range ins[] = {{args->x, z.x}, {args->dt, z.dt}, {args->A, z.A}, {args->B, z.bc}, {args->C, z.bc},
+                         {args->D, z.D}, {args->initial_states, z.init}, {args->y, z.y}, {g->dy, z.x},
+                         {g->dfinal_states, st}};
+    const Range outs[] = {{g->dx, z.x}, {g->ddt, z.dt}, {g->dA, z.A}, {g->dB, z.bc}, {g->dC, z.bc},
+                          {g->dD, z.D}, {g->dinitial_states, st}, {empty ? nullptr : g->workspace, w.total}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range &in : ins)
+            if (overlaps(outs[i], in)) return SSD_ERR_ALIASING;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlaps(outs[i], outs[j])) return SSD_ERR_ALIASING;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (empty) {
+        // no tokens: the final state is the initial state, nothing else depends on the inputs
+        hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dA, (const float *)nullptr, s.H);
+        if (g->dD)
+            hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dD, (const float *)nullptr, s.H);
+        if (g->dinitial_states)
+            hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.b * s.H * s.P * s.N, 256)), dim3(256), 0, hs,
+                               g->dinitial_states, g->dfinal_states, s.b * s.H * s.P * s.N);
+        return launched();
+    }
+    return s.dtype == SSD_DTYPE_BF16 ? bwd_typed<bf16>(s, args, g, w, hs) : bwd_typed<float>(s, args, g, w, hs);
 }
 
 }  // extern "C"

@@ -359,10 +359,13 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm,
 // plain 32-byte reads.
 template <typename E, int KR, int COLS, int TH = kThreads> struct KTile;
 
+// The range ends with the last row's last valid column: the tile's own columns
+// never exceed the row pitch, and with a pitch below COLS a longer range would
+// let the rows past `rows` (which must read as zero) start inside it.
 template <typename E, int COLS>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ktile_rsrc(const E *src, int64_t ld, int rows)
 {
-    return make_rsrc(src, rows > 0 ? ((int64_t)(rows - 1) * ld + COLS) * (int64_t)sizeof(E) : 0);
+    return make_rsrc(src, rows > 0 ? ((int64_t)(rows - 1) * ld + (ld < COLS ? ld : COLS)) * (int64_t)sizeof(E) : 0);
 }
 
 template <int KR, int COLS, int TH>
@@ -677,7 +680,12 @@ __device__ __forceinline__ void seg_end_mark(const int32_t *__restrict__ seq_idx
 // buffer, RING K steps ahead, one contiguous block per wave and step.  Wave w
 // owns n rows w*NT/4 .. +NT/4 of D[n][p] (A = B^T, B = (w x)^T):
 //   acc[i][j][r]  <->  n = w*NT/4 + i*16 + 4*(lane/16) + r,  p = j*16 + lane%16.
-template <typename E, int Q, int NT, bool PACKED>
+// GRAD = true is the same product for the backward pass's per-chunk gradient
+// states U_c = sum_t exp(cs_t) dy_t C_t^T, fed with the chunk's tokens in
+// reversed order (x = dy reversed, B^T = C^T reversed): the weight of reversed
+// position s is exp(cs[len-1-s]) from the given cs, no cumsum step runs, and
+// delta and cs are only read.
+template <typename E, int Q, int NT, bool PACKED, bool GRAD = false>
 __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const E *__restrict__ x, const E *__restrict__ cbuf, const E *__restrict__ dt, const float *__restrict__ A,
     const int32_t *__restrict__ seq_idx, float *__restrict__ delta, float *__restrict__ cs,
@@ -710,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     // cumsum step below must not wait for the tiles
     float dv[4], cv[4];
     int sv[4];
-    if (wave == 0) chunk_cumsum_load<E>(dt, seq_idx, b, c, h, T, H, Q, dv, sv);
+    if (!GRAD && wave == 0) chunk_cumsum_load<E>(dt, seq_idx, b, c, h, T, H, Q, dv, sv);
     const int64_t ldx = (int64_t)H * P;
     XT xs;
     xs.init(ldx, P - p0);
@@ -737,13 +745,20 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     // Packed streams: wave 1 of one workgroup per chunk records the segment ends
     // among the chunk's positions (for the per-segment final states), while wave
     // 0 runs the cumsum step.
-    if (PACKED && seg_end && h == 0 && tp == 0 && wave == 1)
+    if (!GRAD && PACKED && seg_end && h == 0 && tp == 0 && wave == 1)
         for (int t = t0 + lane; t < t0 + len; t += 64) seg_end_mark(seq_idx, seg_end, t, T, nseq);
 
     // Delta and cs of this chunk and head (the cumsum step, bit-identical to
     // k_chunk_cumsum) by wave 0 while the loads above fly; the first p-tile's
     // workgroup also stores them for state_passing and chunk_scan
-    if (wave == 0) {
+    if (GRAD && wave == 0) {
+        const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+        for (int s = lane; s < Q; s += 64) {
+            const bool keep = s < len;
+            m[s] = keep;
+            w[s] = keep ? __builtin_amdgcn_exp2f(cs[row + (len - 1 - s)] * kLog2e) : 0.f;
+        }
+    } else if (wave == 0) {
         chunk_cumsum_compute(A, PACKED, c, h, T, Q, softplus, dv, cv, sv);
         if (tp == 0) store_cumsum_wave(delta, cs, ((int64_t)b * H + h) * nc + c, Q, dv, cv);
         constexpr int per = Q / 64;
@@ -842,7 +857,12 @@ template <int VE> __device__ __forceinline__ void store_final(float *p, const fl
     for (int i = 0; i < VE; i += 4) store4_f32(p + i, v + i);
 }
 
-template <typename E, int VE>
+// REV = true runs the same scan over the chunks in reverse order, which is the
+// backward pass's gradient-state scan: with U_c in `states` and dL/d(final
+// state) in `init`, slot c receives G_c = dL/d(state after chunk c) and
+// `final_states` receives dL/d(initial state); G_{c-1} = exp(cs_last(c)) G_c +
+// U_c has the same form as the forward step.  (REV takes no seq_idx.)
+template <typename E, int VE, bool REV = false>
 __global__ __launch_bounds__(kThreads) void k_state_passing(
     E *__restrict__ states, const float *__restrict__ cs, const float *__restrict__ init,
     float *__restrict__ final_states, const int32_t *__restrict__ seq_idx,
@@ -858,6 +878,7 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
     const int64_t e0 = (gid - (int64_t)bh * vph) * VE;
     const int h = bh % H;
     const int b = bh / H;
+    auto chunk = [&](int k) { return REV ? nc - 1 - k : k; };   // the k-th chunk visited
     float hs[VE];
 #pragma unroll
     for (int v = 0; v < VE; ++v) hs[v] = 0.f;
@@ -868,25 +889,25 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
     R buf[D];
 #pragma unroll
     for (int k = 0; k < D; ++k)
-        if (k < nc) buf[k] = *reinterpret_cast<const R *>(lane_base + (int64_t)k * cstride);
+        if (k < nc) buf[k] = *reinterpret_cast<const R *>(lane_base + (int64_t)chunk(k) * cstride);
     int sprev = seq_idx ? seq_idx[0] : 0;
     for (int cb = 0; cb < nc; cb += 64) {
-        // the per-chunk scalars of 64 chunks: lane i holds chunk cb + i
+        // the per-chunk scalars of 64 visited chunks: lane i holds visit cb + i
         const int cl = cb + lane;
-        const float lamv = cl < nc ? lamp[(int64_t)cl * Q] : 0.f;
-        const int slv = (seq_idx && cl < nc) ? seq_idx[min(cl * Q + Q, T) - 1] : 0;
+        const float lamv = cl < nc ? lamp[(int64_t)chunk(cl) * Q] : 0.f;
+        const int slv = (!REV && seq_idx && cl < nc) ? seq_idx[min(cl * Q + Q, T) - 1] : 0;
         for (int k0 = 0; k0 < 64 && cb + k0 < nc; k0 += D) {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
-                const int c = cb + k0 + j;
-                if (c < nc) {
+                const int k = cb + k0 + j;
+                if (k < nc) {
                     float sv[VE];
                     unpack_vec<E, VE>(buf[j], sv);
-                    if (c + D < nc) buf[j] = *reinterpret_cast<const R *>(lane_base + (int64_t)(c + D) * cstride);
-                    store_vec<VE>(lane_base + (int64_t)c * cstride, hs);
+                    if (k + D < nc) buf[j] = *reinterpret_cast<const R *>(lane_base + (int64_t)chunk(k + D) * cstride);
+                    store_vec<VE>(lane_base + (int64_t)chunk(k) * cstride, hs);
                     const float lm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lamv), k0 + j));
                     const int sc = __builtin_amdgcn_readlane(slv, k0 + j);
-                    const bool keep = !seq_idx || sc == sprev;
+                    const bool keep = REV || !seq_idx || sc == sprev;
                     sprev = sc;
                     const float d = exp_neg(lm);
 #pragma unroll
@@ -1022,12 +1043,21 @@ template <int Q> constexpr int scan_threads() { return Q * 2; }
 
 // NT = N rounded up to 64 (compile time, so every K loop unrolls and every LDS
 // fragment offset is an immediate); columns N..NT-1 are masked.
-template <typename E, int Q, int NT, bool PACKED>
+// Dot modes (used by the backward pass; DOT = 0 is the forward): with v = `vec`
+// at each token's position (DOT = 1) or at the mirrored position len-1-t of a
+// chunk whose tokens were reversed (DOT = 2), the kernel also writes, per token,
+// fp32 dot products over this workgroup's 64 p (one [b,H,nc,Q] slice per p tile,
+// indexed by the token's original position):
+//   dot1 = v . (the entering-state term alone),  dot2 (DOT = 2) = v . (the whole
+//   output before the D skip term).
+// P1ONLY computes dot1 only: no x tile, no intra-chunk terms, no y.
+template <typename E, int Q, int NT, bool PACKED, int DOT = 0, bool P1ONLY = false>
 __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
     const E *__restrict__ cbuf, const E *__restrict__ hin,
     const float *__restrict__ D, const int32_t *__restrict__ seq_idx, E *__restrict__ y,
-    int T, int H, int G, int P, int N, int nc, int ntp)
+    int T, int H, int G, int P, int N, int nc, int ntp, const E *__restrict__ vec = nullptr,
+    float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr)
 {
     using F = frag_t<E>;
     constexpr int TH = scan_threads<Q>();
@@ -1085,7 +1115,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     for (int i = 0; i < HG; ++i) hraw[i] = bload16(hrs, hoff(i));
     XT xs;
     xs.init((int64_t)H * P, P - p0);
-    xs.load(XT::rsrc(x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len));
+    if constexpr (!P1ONLY) xs.load(XT::rsrc(x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len));
     float c_i = 0.f, d_i = 0.f;
     int s_i = 0;
     if (threadIdx.x < Q) {
@@ -1138,7 +1168,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
         for (int i = 0; i < HG; ++i)
             *reinterpret_cast<uint4 *>(hs + (hr + (i0 + i) * RPP) * HP + hv * V) = hraw[i];
     }
-    xs.template store<false, false>(xt, nullptr, nullptr);
+    if constexpr (!P1ONLY) xs.template store<false, false>(xt, nullptr, nullptr);
     if (threadIdx.x < Q) {
         csb[threadIdx.x] = c_i;
         db[threadIdx.x] = d_i;
@@ -1146,7 +1176,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     }
     __syncthreads();
     // V_j[s] for s < 32 floor(j/2): thread s fills its column for every row j that has it
-    if (threadIdx.x < 32 * KSB) {
+    if (!P1ONLY && threadIdx.x < 32 * KSB) {
         const int s = threadIdx.x;
         const float css = csb[s], dss = db[s];
         const int sqs = PACKED ? sq[s] : 0;
@@ -1178,6 +1208,42 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
             for (int k = 0; k < NSB; ++k) bload_frag(crs, c_off(k, ks + RING), cr[ks % RING][k]);
         }
+    }
+
+    // v . acc over this tile's 64 p for each token of the wave's live sub-blocks,
+    // each acc scaled by a per-token factor; lane (li, lg) holds p = 16 pb + 4 lg + q
+    auto dot_out = [&](float *dst, auto scale) {
+        const int64_t rowb = ((((int64_t)tp * gridDim.y + b) * H + h) * nc + c) * Q;
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+            if (!live[k]) continue;
+            const int t = 16 * jb[k] + li;
+            const int tv = DOT == 2 ? len - 1 - t : t;   // the token's original position
+            const float f = scale(k, t);
+            float sum = 0.f;
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int p = p0 + 16 * pb + 4 * lg;
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+                if (t < len && p < P) load4_f32(vec + (((int64_t)b * T + t0 + tv) * H + h) * P + p, v);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sum += v[q] * acc[k][pb][q];
+            }
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            if (lg == 0 && t < len) dst[rowb + tv] = sum * f;
+        }
+    };
+    if constexpr (DOT != 0) {
+        // after the e^{cs_t0} scale below, the entering-state term of token t is
+        // acc * exp(cs_t - cs_t0): take its dot product now
+        auto sc1 = [&](int k, int t) {
+            const int tj = 16 * jb[k];
+            const bool mo = !PACKED || sq[tj] == seq_prev;
+            return mo ? exp2_(csb[tj]) * exp2_(csb[min(t, Q - 1)] - csb[tj]) : 0.f;
+        };
+        dot_out(dot1, sc1);
+        if constexpr (P1ONLY) return;
     }
 
     // CB fragments: the diagonal step of both sub-blocks, and the first RING
@@ -1269,6 +1335,8 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], XT::frag_at(xt, xoff[pb], ks * 32), wfr);
     }
+
+    if constexpr (DOT == 2) dot_out(dot2, [](int, int) { return 1.f; });
 
     // ---- epilogue: store y ----
     if constexpr (sizeof(E) == 2) {

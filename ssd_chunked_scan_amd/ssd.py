@@ -8,8 +8,8 @@ is missing the first call raises, there is no fallback.
 
 Names follow the C ABI: ``fwd`` (= ``ssd_fwd``), the per-step entry points
 ``chunk_cumsum``, ``chunk_cb``, ``chunk_state``, ``state_passing``,
-``seq_final_states``, ``chunk_scan``, and the decode step ``step`` (=
-``ssd_step``).
+``seq_final_states``, ``chunk_scan``, the decode step ``step`` (= ``ssd_step``)
+and the backward ``bwd`` (= ``ssd_bwd``).
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
 EXPORTED = ["ssd_abi_version", "ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd",
             "ssd_chunk_cumsum", "ssd_chunk_cb", "ssd_chunk_state", "ssd_state_passing",
-            "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step"]
+            "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step", "ssd_bwd_workspace_size", "ssd_bwd"]
 
 
 class FwdArgs(ctypes.Structure):
@@ -53,6 +53,16 @@ class StepArgs(ctypes.Structure):
         ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
         ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
         ("state", ctypes.c_void_p), ("y", ctypes.c_void_p),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    """Mirror of ``ssd_bwd_args``."""
+    _fields_ = [
+        ("dy", ctypes.c_void_p), ("dfinal_states", ctypes.c_void_p), ("dx", ctypes.c_void_p),
+        ("ddt", ctypes.c_void_p), ("dA", ctypes.c_void_p), ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p),
+        ("dD", ctypes.c_void_p), ("dinitial_states", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -88,6 +98,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_seq_final_states.argtypes = [P, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp]
     lib.ssd_step.argtypes = [ctypes.POINTER(StepArgs), vp]
+    lib.ssd_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_bwd.argtypes = [P, ctypes.POINTER(BwdArgs), vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -328,3 +340,56 @@ def step(x, dt, A, B, C, state, D=None, dt_softplus=True, y=None, stream=None):
     if rc != 0:
         raise SSDError(rc, "ssd_step")
     return y
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def bwd_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().ssd_bwd_workspace_size(ctypes.byref(p.args), ctypes.byref(n))
+    if rc != 0:
+        raise SSDError(rc, "ssd_bwd_workspace_size")
+    return int(n.value)
+
+
+def bwd(x, dt, A, B, C, chunk, y, dy, D=None, initial_states=None, dfinal_states=None, dt_softplus=True,
+        grads=None, workspace=None, stream=None, want_dinit=True):
+    """Gradients of sum(y * dy) + sum(final_states * dfinal_states) (see ``ssd_bwd``
+    in ``include/ssd.h``).  ``y`` is the forward output.  Returns a dict with dx,
+    ddt, dA, dB, dC, dD (None without D) and dinitial_states (None unless
+    ``want_dinit``); ``grads`` may pass those tensors pre-allocated."""
+    p = Problem(x, dt, A, B, C, chunk, D, initial_states, None, None, dt_softplus)
+    _check(y, "y", x.dtype, x.shape, p.device)
+    _check(dy, "dy", x.dtype, x.shape, p.device)
+    _check(dfinal_states, "dfinal_states", torch.float32, (p.b, p.H, p.P, p.N), p.device)
+    g = dict(grads or {})
+    g.setdefault("dx", p.empty(x.shape))
+    g.setdefault("ddt", p.empty(dt.shape))
+    g.setdefault("dA", p.empty((p.H,), torch.float32))
+    g.setdefault("dB", p.empty(B.shape))
+    g.setdefault("dC", p.empty(C.shape))
+    g.setdefault("dD", p.empty((p.H,), torch.float32) if D is not None else None)
+    g.setdefault("dinitial_states", p.empty((p.b, p.H, p.P, p.N), torch.float32) if want_dinit else None)
+    _check(g["dx"], "dx", x.dtype, x.shape, p.device)
+    _check(g["ddt"], "ddt", x.dtype, dt.shape, p.device)
+    _check(g["dA"], "dA", torch.float32, (p.H,), p.device)
+    _check(g["dB"], "dB", x.dtype, B.shape, p.device)
+    _check(g["dC"], "dC", x.dtype, C.shape, p.device)
+    _check(g["dD"], "dD", torch.float32, (p.H,), p.device)
+    _check(g["dinitial_states"], "dinitial_states", torch.float32, (p.b, p.H, p.P, p.N), p.device)
+    need = bwd_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=p.device)
+    _check(workspace, "workspace", torch.uint8, None, p.device)
+    p.args.y = _ptr(y)
+    ga = BwdArgs(dy=_ptr(dy), dfinal_states=_ptr(dfinal_states), dx=_ptr(g["dx"]), ddt=_ptr(g["ddt"]),
+                 dA=_ptr(g["dA"]), dB=_ptr(g["dB"]), dC=_ptr(g["dC"]), dD=_ptr(g["dD"]),
+                 dinitial_states=_ptr(g["dinitial_states"]), workspace=_ptr(workspace),
+                 workspace_bytes=workspace.numel())
+    st = stream if stream is not None else torch.cuda.current_stream(p.device).cuda_stream
+    rc = load_library().ssd_bwd(ctypes.byref(p.args), ctypes.byref(ga), ctypes.c_void_p(st))
+    if rc != 0:
+        raise SSDError(rc, "ssd_bwd")
+    return g

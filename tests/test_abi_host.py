@@ -155,3 +155,43 @@ def test_step_binding_checks_shapes():
                       torch.zeros(2, 4, 64, 64))
     with pytest.raises(ValueError, match="batch, nheads, headdim"):
         ssd.step_args(torch.zeros(2, 4, 1, 64), None, None, None, None, None)
+
+
+def _bwd_args(**kw):
+    addr = 0xa0000000
+    g = ssd.BwdArgs()
+    for name in ("dy", "dfinal_states", "dx", "ddt", "dA", "dB", "dC", "dD", "dinitial_states", "workspace"):
+        setattr(g, name, kw.get(name, addr))
+        addr += 0x10000000
+    g.workspace_bytes = kw.get("workspace_bytes", 1 << 40)
+    return g
+
+
+@pytest.mark.parametrize("fkw,gkw,code", [
+    (dict(seq_idx=0x90000000, nseq=1), dict(), SEQ),            # packed streams have no backward
+    (dict(chunk=96), dict(), CHUNK),
+    (dict(y=0), dict(), NULLP),                                 # the forward output is an input here
+    (dict(), dict(dy=0), NULLP), (dict(), dict(dx=0), NULLP), (dict(), dict(dA=0), NULLP),
+    (dict(), dict(dB=0), NULLP), (dict(), dict(workspace=0), NULLP),
+    (dict(), dict(dx=0xa0000008), MISAL),
+    (dict(), dict(workspace_bytes=64), WS),
+    (dict(), dict(dx=0x10000000), ALIAS),                       # dx == x
+    (dict(), dict(dC=0xa0000000 + 256), ALIAS),                 # dC inside dy
+    (dict(), dict(dB=0xa0000000 + 0x20000000), ALIAS),          # dB == dx
+])
+def test_bwd_rejects_invalid_arguments(lib, fkw, gkw, code):
+    a = _args(**fkw)
+    if "y" in fkw:
+        a.y = fkw["y"]
+    assert lib.ssd_bwd(ctypes.byref(a), ctypes.byref(_bwd_args(**gkw)), None) == code
+
+
+def test_bwd_workspace_size(lib):
+    a = _args(batch=2, seqlen=2048, nheads=24, headdim=64, dstate=64, chunk=64)
+    n = ctypes.c_size_t()
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == OK
+    m = ctypes.c_size_t()
+    assert lib.ssd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(m)) == OK
+    assert n.value > m.value
+    packed = _args(seq_idx=0x90000000, nseq=2)
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(packed), ctypes.byref(n)) == SEQ

@@ -433,3 +433,33 @@ def test_full_workloads_sampled(idx):
                         np.broadcast_to(mask[0], (ref.final_states.shape[0], H)))
     _log(f"    sampled heads {int(mask.sum())}: max rel-L2 y={ey:.3e} states={es:.3e}")
     assert ey <= TOL[dtype] and es <= TOL[dtype]
+
+
+def _nan_tail(t, extra=4096):
+    """A copy of t on the GPU whose storage is followed by NaNs: the head of a
+    larger NaN-filled buffer (still contiguous), so any read past the tensor's
+    end shows up in the outputs."""
+    t = t.to("cuda:0")
+    buf = torch.full((t.numel() + extra,), float("nan"), dtype=t.dtype, device=t.device)
+    buf[:t.numel()] = t.reshape(-1)
+    return buf[:t.numel()].view(t.shape)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fwd_reads_nothing_past_the_last_row(dtype):
+    """Row pitches below one 64-column tile (H*P = 32, G*N = 16, N = 16) with a
+    ragged last chunk: the rows past the sequence end must read as zeros, not
+    as whatever follows the tensors in memory, and the workspace may hold
+    anything."""
+    inp = small(dtype, 70, H=2, P=16, N=16, G=1, chunk=64, b=1, seed=70, init_std=0.3)
+    x, dt, B, C = (_nan_tail(t) for t in (inp.x, inp.dt, inp.B, inp.C))
+    p = ssd.Problem(x, dt, inp.A.cuda(), B, C, 64, inp.D.cuda(), inp.initial_states.cuda())
+    ws = torch.full((ssd.workspace_bytes(p) // 4 + 1,), float("nan"), dtype=torch.float32,
+                    device="cuda:0").view(torch.uint8)
+    y, fs = ssd.fwd(x, dt, inp.A.cuda(), B, C, 64, D=inp.D.cuda(), initial_states=inp.initial_states.cuda(),
+                    workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all() and torch.isfinite(fs).all()
+    ref = run_oracle(inp)
+    assert max_rel_y(y, ref.y, inp) <= TOL[DT[dtype]]
+    assert max_rel_states(fs, ref.final_states) <= TOL[DT[dtype]]
