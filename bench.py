@@ -14,6 +14,7 @@ input already resident in HBM.  Prints ONE JSON line:
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same workload
   kernels      per-kernel breakdown (average ms per launch, achieved rate, fraction,
                counter-measured MFMA busy % where a record for these sources exists)
+  backward     ssd_bwd on the same workload (all input gradients): time per call
   decode       the decode step (one token per sequence, state carried) on its own
                seeded workload: time per launch, tokens/s and its HBM roofline
 
@@ -190,6 +191,49 @@ def run_cpu_baseline(inp, budget_s=20.0):
             "seconds_measured": round(sum(times), 3)}
 
 
+def run_backward(dev, inp, g, reps, warmup):
+    """Time ssd_bwd (every input gradient; the chunk intermediates recomputed
+    inside) on the workload's inputs with a seeded dy and dfinal, between HIP
+    events on the launch stream; outputs and workspace preallocated."""
+    import numpy as np
+    import torch
+    from ssd_chunked_scan_amd import ssd
+
+    nseq = inp.nseq if inp.seq_idx is not None else None
+    if nseq is not None:
+        return None   # the backward takes no packed streams
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states)
+    rng = np.random.default_rng(7)
+    dy = torch.from_numpy(rng.standard_normal(tuple(inp.x.shape)).astype(np.float32)).to(dev).to(g.x.dtype)
+    b, T, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    dfin = torch.from_numpy(rng.standard_normal((b, H, P, N)).astype(np.float32)).to(dev)
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states)
+    ws = torch.empty(ssd.bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    grads = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, D=g.D, initial_states=g.initial_states,
+                    dfinal_states=dfin, workspace=ws)
+    stream = torch.cuda.current_stream(dev)
+
+    def one():
+        ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, D=g.D, initial_states=g.initial_states,
+                dfinal_states=dfin, grads=grads, workspace=ws)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b_ in ev:
+        a.record(stream)
+        one()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b_) for a, b_ in ev]
+    avg = sum(ms) / len(ms)
+    return {"ms": round(avg, 5), "step_ms": percentiles(ms), "tokens_per_s": round(inp.real_tokens / (avg / 1e3), 1),
+            "workspace_bytes": int(ws.numel()),
+            "note": "all input gradients; the forward's chunk intermediates are recomputed inside"}
+
+
 def run_decode(dev, reps, warmup):
     """Time the decode step (ssd_step) on the seeded decode workload: HIP events
     around each launch on the launch stream, the state carried from launch to
@@ -240,6 +284,7 @@ def main():
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB (3 times), as the "
@@ -364,6 +409,7 @@ def main():
                 "mfma_busy_pct": measured_mfma(dom, cfg["name"])}
     total_flops = sum(w.get("flops", 0.0) for w in work.values())
     decode = None if args.no_decode else run_decode(dev, reps, 5)
+    backward = None if args.no_backward else run_backward(dev, inp, g, max(5, min(reps, 20)), 3)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -383,6 +429,7 @@ def main():
         "step_ms": step_ms,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "backward": backward,
         "decode": decode,
     }
     print(json.dumps(line), flush=True)

@@ -396,8 +396,8 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     w.dyx = take(dcs);
     w.mrow = take(ms);
     w.mcol = take(ms);
-    w.dA_part = take(bh);
-    w.dD_part = take(bh);
+    w.dA_part = take(bh * (size_t)s.nc);
+    w.dD_part = take(bh * (size_t)s.nc);
     w.total = o;
     return w;
 }
@@ -485,10 +485,23 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st)) != SSD_OK)
         return r;
     // 7. dx, dy . x
-    const int64_t waves = s.b * s.T * s.H;
-    hipLaunchKernelGGL(k_bwd_token<E>, dim3(grid1(waves, kThreads / 64)), dim3(kThreads), 0, st, (const E *)a->x,
-                       (const E *)g->dy, (const E *)ypr, delta, a->D, (E *)g->dx, dyx, (int)s.T, (int)s.H, (int)s.P,
-                       (int)s.Q, (int)s.nc, waves);
+    {
+        auto tok = [&](auto lw) {
+            constexpr int L = decltype(lw)::value;
+            const int64_t waves = s.b * s.T * ((s.H + 64 / L - 1) / (64 / L));
+            hipLaunchKernelGGL((k_bwd_token<E, L>), dim3(grid1(waves, kThreads / 64)), dim3(kThreads), 0, st,
+                               (const E *)a->x, (const E *)g->dy, (const E *)ypr, delta, a->D, (E *)g->dx, dyx,
+                               (int)s.T, (int)s.H, (int)s.P, (int)s.Q, (int)s.nc, waves);
+            return launched();
+        };
+        const int64_t need = s.P / 4;   // lanes per head
+        if (need <= 4) r = tok(std::integral_constant<int, 4>{});
+        else if (need <= 8) r = tok(std::integral_constant<int, 8>{});
+        else if (need <= 16) r = tok(std::integral_constant<int, 16>{});
+        else if (need <= 32) r = tok(std::integral_constant<int, 32>{});
+        else r = tok(std::integral_constant<int, 64>{});
+        if (r != SSD_OK) return r;
+    }
     // 8. M (summed over the group's heads) with the row / column sums of S; the boundary terms
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     const int nnt = (int)((s.N + 63) / 64);
@@ -505,11 +518,12 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     hipLaunchKernelGGL(k_bwd_bnd<E>, dim3((unsigned)(s.b * s.nc * s.H)), dim3(kThreads), 0, st, (const E *)gstates,
                        (const E *)states, cs, bnd, (int)s.H, (int)s.nc, (int)s.Q, s.P * s.N);
     // 9. dl, ddt, dA, dD
-    hipLaunchKernelGGL(k_bwd_dl<E>, dim3((unsigned)(s.b * s.H)), dim3(kThreads), 0, st, rpart, cpart, yo, zo, xyp,
-                       bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T, (int)s.H,
-                       (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), (int)a->dt_softplus);
-    hipLaunchKernelGGL(k_bwd_sum_heads, dim3(grid1(s.H, 64)), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
-                       (int)s.b, (int)s.H);
+    const int64_t dlrows = s.b * s.H * s.nc;
+    hipLaunchKernelGGL(k_bwd_dl<E>, dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart, yo, zo,
+                       xyp, bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T,
+                       (int)s.H, (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), dlrows, (int)a->dt_softplus);
+    hipLaunchKernelGGL(k_bwd_sum_heads, dim3((unsigned)s.H), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
+                       (int)s.b, (int)s.H, (int)s.nc);
     if ((r = launched()) != SSD_OK) return r;
     // 10. dC and dB
     return with_q(s.Q, [&](auto q) {

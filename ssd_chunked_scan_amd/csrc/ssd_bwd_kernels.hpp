@@ -76,35 +76,51 @@ __global__ void k_bwd_reverse_cs(const float *__restrict__ cs, float *__restrict
 // ---------------------------------------------------------------------------
 // per token: dx = Delta y' + D dy, and dy . x
 // ---------------------------------------------------------------------------
-// One wave per (b, t, h); lanes over p.  y'_s comes from the reversed scan, so it
-// is read at the mirrored position.  dy . x goes to a [b,H,nc,Q] row.
-template <typename E>
+// Lanes work on four consecutive p (8- or 16-byte accesses); a wave covers
+// 64 / L heads of one token, L = the power of two >= P/4 lanes per head (for P
+// above 256, L = 64 and each lane takes several four-element groups).  y'_s
+// comes from the reversed scan, so it is read at the mirrored position.  dy . x
+// of each (token, head) goes to a [b,H,nc,Q] row.
+template <typename E, int L>
 __global__ __launch_bounds__(kThreads) void k_bwd_token(
     const E *__restrict__ x, const E *__restrict__ dy, const E *__restrict__ yrev, const float *__restrict__ delta,
     const float *__restrict__ D, E *__restrict__ dx, float *__restrict__ dyx, int T, int H, int P, int Q, int nc,
-    int64_t total)
+    int64_t total_waves)
 {
+    constexpr int HPW = 64 / L;   // heads per wave
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (wid >= total) return;   // whole wave
-    const int lane = threadIdx.x & 63;
-    const int h = (int)(wid % H);
-    const int64_t bt = wid / H;
+    if (wid >= total_waves) return;   // whole wave
+    const int lane = threadIdx.x & 63, seg = lane / L, sl = lane % L;
+    const int hgroups = (H + HPW - 1) / HPW;
+    const int hg = (int)(wid % hgroups);
+    const int64_t bt = wid / hgroups;
+    const int h = hg * HPW + seg;
     const int b = (int)(bt / T), t = (int)(bt % T);
     const int c = t / Q, k = t % Q, len = min(Q, T - c * Q);
     const int tr = c * Q + (len - 1 - k);
-    const int64_t srow = (((int64_t)b * H + h) * nc + c) * Q + k;
-    const float dl = delta[srow];
-    const float Dh = D ? D[h] : 0.f;
-    const int64_t o = (bt * H + h) * P, orv = (((int64_t)b * T + tr) * H + h) * P;
     float sdx = 0.f;
-    for (int p = lane; p < P; p += 64) {
-        const float xv = to_float(x[o + p]), dv = to_float(dy[o + p]);
-        dx[o + p] = from_float<E>(dl * to_float(yrev[orv + p]) + Dh * dv);
-        sdx += dv * xv;
+    int64_t srow = 0;
+    if (h < H) {
+        srow = (((int64_t)b * H + h) * nc + c) * Q + k;
+        const float dl = delta[srow];
+        const float Dh = D ? D[h] : 0.f;
+        const int64_t o = (bt * H + h) * P, orv = (((int64_t)b * T + tr) * H + h) * P;
+        for (int p = 4 * sl; p < P; p += 4 * L) {
+            float xv[4], dv[4], yv[4], ov[4];
+            load4_f32(x + o + p, xv);
+            load4_f32(dy + o + p, dv);
+            load4_f32(yrev + orv + p, yv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                ov[q] = dl * yv[q] + Dh * dv[q];
+                sdx += dv[q] * xv[q];
+            }
+            store4_f32(dx + o + p, ov);
+        }
     }
 #pragma unroll
-    for (int m = 32; m > 0; m >>= 1) sdx += __shfl_xor(sdx, m);
-    if (lane == 0) dyx[srow] = sdx;
+    for (int m = L / 2; m > 0; m >>= 1) sdx += __shfl_xor(sdx, m, L);
+    if (sl == 0 && h < H) dyx[srow] = sdx;
 }
 
 // e^{cs_last(c)} <G_c, Hin_c> for every (b, c, h): one workgroup each.
@@ -145,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bnd(const E *__restrict__ gst,
 // with r_j / c_j the row / column sums of S (k_bwd_m), yo_j = dy_j . (entering-
 // state term of y_j), zo_s = x_s . (the G_c term of y'_s), bnd_c = e^{cs_last}
 // <G_c, Hin_c>.  Then dDelta = A dl + x . y' and ddt = dDelta * sigmoid(dt).
-// One workgroup per (b, h); wave w takes chunks w, w + 4, ...; lane l holds the
-// tokens l*per .. l*per + per - 1 (per = Q/64); the scans run in fp64.
+// One wave per (b, h, c); lane l holds the tokens l*per .. l*per + per - 1 (per =
+// Q/64); the scans run in fp64; dA and dD partials go to [b,H,nc].
 __device__ __forceinline__ double wave_incl_scan(double v)
 {
     const int lane = threadIdx.x & 63;
@@ -164,98 +180,97 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     const float *__restrict__ zo, const float *__restrict__ xyp, const float *__restrict__ bnd,
     const float *__restrict__ dyx, const float *__restrict__ delta, const E *__restrict__ dt,
     const float *__restrict__ A, E *__restrict__ ddt, float *__restrict__ dA_part, float *__restrict__ dD_part, int T,
-    int H, int Q, int nc, int ntp, int softplus)
+    int H, int Q, int nc, int ntp, int64_t rows, int softplus)
 {
-    __shared__ double red[2][kThreads / 64];
-    const int bh = blockIdx.x, h = bh % H, b = bh / H;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // (b * H + h) * nc + c
+    if (wid >= rows) return;   // whole wave
+    const int lane = threadIdx.x & 63;
+    const int c = (int)(wid % nc);
+    const int64_t bh = wid / nc;
+    const int h = (int)(bh % H), b = (int)(bh / H);
     const int per = Q / 64, QT = Q / 64;
-    const int64_t slice = (int64_t)gridDim.x * nc * Q;   // one tile / p-tile slice
+    const int64_t slice = rows * Q;   // one tile / p-tile slice: [b,H,nc,Q]
     const float Ah = A[h];
-    double sa = 0.0, sd = 0.0;
-    for (int c = wave; c < nc; c += kThreads / 64) {
-        const int len = min(Q, T - c * Q);
-        const int64_t row = ((int64_t)bh * nc + c) * Q;
-        double av[4] = {0, 0, 0, 0}, zv[4] = {0, 0, 0, 0};
-        float xv[4] = {0, 0, 0, 0};
-        double asum = 0.0, zsum = 0.0;
-        for (int e = 0; e < per; ++e) {
-            const int j = lane * per + e;
-            if (j >= len) continue;
-            double r = 0.0, cc = 0.0, y1 = 0.0, z1 = 0.0, xy = 0.0;
-            for (int si = 0; si <= j / 64; ++si) r += rpart[si * slice + row + j];
-            for (int ti = j / 64; ti < QT; ++ti) cc += cpart[ti * slice + row + j];
-            for (int tp = 0; tp < ntp; ++tp) {
-                y1 += yo[tp * slice + row + j];
-                z1 += zo[tp * slice + row + j];
-                xy += xyp[tp * slice + row + j];
-            }
-            av[e] = r - cc + y1;
-            zv[e] = delta[row + j] * z1;
-            xv[e] = (float)xy;
-            asum += av[e];
-            zsum += zv[e];
+    const int len = min(Q, T - c * Q);
+    const int64_t row = wid * Q;
+    double av[4] = {0, 0, 0, 0}, zv[4] = {0, 0, 0, 0};
+    float xv[4] = {0, 0, 0, 0};
+    double asum = 0.0, zsum = 0.0;
+    for (int e = 0; e < per; ++e) {
+        const int j = lane * per + e;
+        if (j >= len) continue;
+        double r = 0.0, cc = 0.0, y1 = 0.0, z1 = 0.0, xy = 0.0;
+        for (int si = 0; si <= j / 64; ++si) r += rpart[si * slice + row + j];
+        for (int ti = j / 64; ti < QT; ++ti) cc += cpart[ti * slice + row + j];
+        for (int tp = 0; tp < ntp; ++tp) {
+            y1 += yo[tp * slice + row + j];
+            z1 += zo[tp * slice + row + j];
+            xy += xyp[tp * slice + row + j];
         }
-        // suffix sums of a (inclusive) and prefix sums of z (exclusive) over the chunk
-        const double ain = wave_incl_scan(asum), zin = wave_incl_scan(zsum);
-        const double atot = __shfl(ain, 63);
-        double asuf = atot - ain + asum;   // sum of a over this lane's tokens and all later lanes
-        double zpre = zin - zsum;          // sum of z over earlier lanes
-        const double b0 = bnd[(int64_t)bh * nc + c];
-        for (int e = 0; e < per; ++e) {
-            const int j = lane * per + e;
-            if (j < len) {
-                const double dl = asuf + zpre + b0;
-                const float dd = Ah * (float)dl + xv[e];
-                const int t = c * Q + j;
-                float gr = dd;
-                if (softplus) {
-                    const float zt = to_float(dt[((int64_t)b * T + t) * H + h]);
-                    gr = dd / (1.f + __builtin_amdgcn_exp2f(-zt * kLog2e));   // dDelta * sigmoid(dt)
-                }
-                ddt[((int64_t)b * T + t) * H + h] = from_float<E>(gr);
-                sa += (double)delta[row + j] * dl;
-                sd += dyx[row + j];
-            }
-            asuf -= av[e];
-            zpre += zv[e];
-        }
+        av[e] = r - cc + y1;
+        zv[e] = delta[row + j] * z1;
+        xv[e] = (float)xy;
+        asum += av[e];
+        zsum += zv[e];
     }
-    // workgroup sums of the partials
+    // suffix sums of a (inclusive) and prefix sums of z (exclusive) over the chunk
+    const double ain = wave_incl_scan(asum), zin = wave_incl_scan(zsum);
+    const double atot = __shfl(ain, 63);
+    double asuf = atot - ain + asum;   // sum of a over this lane's tokens and all later lanes
+    double zpre = zin - zsum;          // sum of z over earlier lanes
+    const double b0 = bnd[wid];
+    double sa = 0.0, sd = 0.0;
+    for (int e = 0; e < per; ++e) {
+        const int j = lane * per + e;
+        if (j < len) {
+            const double dl = asuf + zpre + b0;
+            const float dd = Ah * (float)dl + xv[e];
+            const int t = c * Q + j;
+            float gr = dd;
+            if (softplus) {
+                const float zt = to_float(dt[((int64_t)b * T + t) * H + h]);
+                gr = dd / (1.f + __builtin_amdgcn_exp2f(-zt * kLog2e));   // dDelta * sigmoid(dt)
+            }
+            ddt[((int64_t)b * T + t) * H + h] = from_float<E>(gr);
+            sa += (double)delta[row + j] * dl;
+            sd += dyx[row + j];
+        }
+        asuf -= av[e];
+        zpre += zv[e];
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         sa += __shfl_xor(sa, o);
         sd += __shfl_xor(sd, o);
     }
     if (lane == 0) {
-        red[0][wave] = sa;
-        red[1][wave] = sd;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double a = 0.0, d = 0.0;
-        for (int w = 0; w < kThreads / 64; ++w) {
-            a += red[0][w];
-            d += red[1][w];
-        }
-        dA_part[bh] = (float)a;
-        dD_part[bh] = (float)d;
+        dA_part[wid] = (float)sa;
+        dD_part[wid] = (float)sd;
     }
 }
 
-// dA[h] = sum_b dA_part[b, h], dD[h] likewise (a fixed order, so deterministic).
+// dA[h] = sum over (b, c) of dA_part[b, h, c], dD[h] likewise, one wave per head
+// (a fixed order, so deterministic).
 __global__ void k_bwd_sum_heads(const float *__restrict__ dA_part, const float *__restrict__ dD_part,
-                                float *__restrict__ dA, float *__restrict__ dD, int batch, int H)
+                                float *__restrict__ dA, float *__restrict__ dD, int batch, int H, int nc)
 {
-    const int h = blockIdx.x * blockDim.x + threadIdx.x;
-    if (h >= H) return;
-    float a = 0.f, d = 0.f;
-    for (int b = 0; b < batch; ++b) {
-        a += dA_part[b * H + h];
-        d += dD_part[b * H + h];
+    const int h = blockIdx.x, lane = threadIdx.x;
+    double a = 0.0, d = 0.0;
+    for (int b = 0; b < batch; ++b)
+        for (int c = lane; c < nc; c += 64) {
+            const int64_t i = ((int64_t)b * H + h) * nc + c;
+            a += dA_part[i];
+            d += dD_part[i];
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a += __shfl_xor(a, o);
+        d += __shfl_xor(d, o);
     }
-    dA[h] = a;
-    if (dD) dD[h] = d;
+    if (lane == 0) {
+        dA[h] = (float)a;
+        if (dD) dD[h] = (float)d;
+    }
 }
 
 // ---------------------------------------------------------------------------
