@@ -306,6 +306,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
     __shared__ __align__(16) E ss[64 * PITCH];
     __shared__ float stage[64 * 65];
     __shared__ float rsum[64], csum[64];
+    __shared__ float hcs[2][64], hds[64];   // the head's cs at the t rows / s rows, delta at the s rows
     const int units = NTRI * nc * G;
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
@@ -325,7 +326,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const int trows = min(64, len - ti * 64), srows = min(64, len - si * 64);
 
     uint4 rt[NPASS], rs[NPASS];
+    float hval = 0.f;   // this thread's element of the next head's cs / delta rows (threads < 192)
     auto issue = [&](int k) {
+        if (k % PC == 0 && threadIdx.x < 192) {
+            const int h = g * hpg + k / PC, part = threadIdx.x >> 6, e = threadIdx.x & 63;
+            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+            const int pos = (part == 0 ? ti : si) * 64 + e;
+            hval = pos < len ? (part == 2 ? delta[row + pos] : cs[row + pos]) : 0.f;
+        }
         const int h = g * hpg + k / PC, p0 = (k % PC) * 64;
         const int64_t ld = (int64_t)H * P;
         const auto trs = make_rsrc(dy + (((int64_t)b * T + t0 + ti * 64) * H + h) * P + p0,
@@ -379,6 +387,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
             *reinterpret_cast<uint4 *>(ts + (hr + i * RPP) * PITCH + hv * V) = rt[i];
             *reinterpret_cast<uint4 *>(ss + (hr + i * RPP) * PITCH + hv * V) = rs[i];
         }
+        if (k % PC == 0 && threadIdx.x < 192) {
+            const int part = threadIdx.x >> 6, e = threadIdx.x & 63;
+            if (part == 2) hds[e] = hval;
+            else hcs[part][e] = hval;
+        }
         if (k + 1 < steps) issue(k + 1);
         __syncthreads();
 #pragma unroll
@@ -397,20 +410,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
         if (k % PC == PC - 1) {
             // this head is complete: add it with its decays and step sizes, and
             // sum its S = W CB by rows and by columns
-            const int h = g * hpg + k / PC;
-            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
             float rs[2][4] = {}, cl[2] = {};
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int s = si * 64 + s_w + 16 * j + li;
-                const float css = s < len ? cs[row + s] : 0.f, ds = s < len ? delta[row + s] : 0.f;
+                const float css = hcs[1][s_w + 16 * j + li], ds = hds[s_w + 16 * j + li];
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = ti * 64 + t_w + 16 * i + 4 * lg + r;
                         if (s <= t && t < len) {
-                            const float w = __builtin_amdgcn_exp2f((cs[row + t] - css) * kLog2e) * ds;
+                            const float w = __builtin_amdgcn_exp2f((hcs[0][t_w + 16 * i + 4 * lg + r] - css) * kLog2e) * ds;
                             const float wv = acc[i][j][r] * w;
                             tot[i][j][r] += wv;
                             const float sv = wv * cbv[i][j][r];
