@@ -10,8 +10,11 @@ bf16 or fp32 are upcast exactly, so the oracle sees the very values the GPU
 sees.
 
 ``backward`` is the reverse-mode derivative of that recurrence (the chain rule
-applied step by step in reverse; the pages give no backward equations), and
-``step`` is the recurrence over one token (the decode step).
+applied step by step in reverse; the pages give no backward equations),
+``step`` is the recurrence over one token (the decode step), and
+``conv1d_silu`` / ``gated`` are the block's steps on either side of the SSD
+(causal depthwise convolution + SiLU before it, the SiLU gate after it), in
+plain fp64 numpy.
 
 ``forward`` follows the literal recurrence of the "Mamba 2 -- Transformers are
 SSMs" paper story (ai.tomabc.com), section 3.1: ``h_t = a_t h_{t-1} +
@@ -225,3 +228,60 @@ def chunk_cb(B, C, chunk):
     Bp = np.pad(B, ((0, 0), (0, pad), (0, 0), (0, 0))).reshape(b, nc, chunk, G, N)
     Cp = np.pad(C, ((0, 0), (0, pad), (0, 0), (0, 0))).reshape(b, nc, chunk, G, N)
     return np.einsum("bctgn,bcsgn->bcgts", Cp, Bp)
+
+
+# ---------------------------------------------------------------------------
+# the Mamba-2 block around the SSD ("SSM 家族全景图（下）：Mamba-2 与 Jamba",
+# section five, the block's data flow): a causal one-dimensional convolution and
+# a SiLU on the main path before the SSD, a SiLU on the gate path, and the
+# elementwise product of the two paths.  Plain fp64 numpy, no C.
+# ---------------------------------------------------------------------------
+
+def silu(v):
+    """SiLU(v) = v / (1 + e^-v), elementwise, fp64."""
+    v = _f64(v)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def causal_conv1d(xbc, weight, bias=None, seq_idx=None):
+    """Depthwise causal convolution over time, before the activation:
+    ``v[b,t,c] = bias[c] + sum_k weight[c,k] * xbc[b, t-(K-1)+k, c]`` over taps k
+    in [0, K), an input position counting only when it is >= 0 and, with
+    ``seq_idx`` (batch 1), in the same segment as t (the convolution restarts
+    with every packed sequence).  xbc [b,T,C], weight [C,K] -> v [b,T,C] fp64."""
+    xbc, weight = _f64(xbc), _f64(weight)
+    b, T, Cc = xbc.shape
+    K = weight.shape[1]
+    seg = None
+    if seq_idx is not None:
+        if hasattr(seq_idx, "detach"):
+            seq_idx = seq_idx.detach().cpu().numpy()
+        seg = np.asarray(seq_idx).reshape(-1)
+    v = np.zeros((b, T, Cc), np.float64)
+    if bias is not None:
+        v += _f64(bias)[None, None, :]
+    for t in range(T):
+        for k in range(K):
+            s = t - (K - 1) + k
+            if s < 0 or (seg is not None and seg[s] != seg[t]):
+                continue
+            v[:, t, :] += weight[None, :, k] * xbc[:, s, :]
+    return v
+
+
+def conv1d_silu(xbc, weight, nheads, headdim, ngroups, dstate, bias=None, seq_idx=None):
+    """SiLU(causal_conv1d(...)) split along channels into x [b,T,H,P] (the first
+    H*P channels), B and C [b,T,G,N] (the next G*N each), fp64."""
+    a = silu(causal_conv1d(xbc, weight, bias, seq_idx))
+    b, T, _ = a.shape
+    hp, gn = nheads * headdim, ngroups * dstate
+    x = a[:, :, :hp].reshape(b, T, nheads, headdim)
+    Bm = a[:, :, hp:hp + gn].reshape(b, T, ngroups, dstate)
+    Cm = a[:, :, hp + gn:hp + 2 * gn].reshape(b, T, ngroups, dstate)
+    return x, Bm, Cm
+
+
+def gated(y, z):
+    """The gate of the block: y * SiLU(z), elementwise, fp64."""
+    return _f64(y) * silu(z)

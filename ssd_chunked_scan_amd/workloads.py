@@ -22,6 +22,10 @@ packed variable-length sequences):
 Packed workloads concatenate sequences of lengths U[lo, hi] into one stream
 (batch 1), pad it to a multiple of the chunk length, and label the padding as a
 segment of its own with x = B = C = 0.
+
+The block around the SSD (``block_inputs``, its own seed) draws the
+pre-convolution channels xBC ~ N(0, 1), depthwise taps and bias ~ U[-1/sqrt(w),
+1/sqrt(w)] for w taps, and the gate input z ~ N(0, 1).
 """
 from __future__ import annotations
 
@@ -192,3 +196,38 @@ def decode_inputs(seed: int = 2000, **overrides) -> StepInputs:
     inp = make_inputs(cfg["batch"], 1, cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"], 64,
                       cfg["dtype"], seed, dt_mean=cfg["dt_mean"], init_std=cfg["init_std"], name=cfg["name"])
     return token(inp, 0)
+
+
+@dataclass
+class BlockInputs:
+    """The Mamba-2 block's tensors on either side of the SSD for one ``Inputs``:
+    the pre-convolution main path xBC = [x | B | C], its depthwise taps and bias,
+    and the gate path z.  dt, A, D, initial states and the packing come from the
+    ``Inputs`` (its x, B and C are not used: the convolution produces them)."""
+    xbc: torch.Tensor               # [b,T,H*P + 2*G*N] workload dtype
+    weight: torch.Tensor            # [H*P + 2*G*N, width] fp32
+    bias: Optional[torch.Tensor]    # [H*P + 2*G*N] fp32
+    z: torch.Tensor                 # [b,T,H,P] workload dtype
+    width: int = 4
+
+
+def block_inputs(inp: Inputs, seed: int, width: int = 4, with_bias: bool = True) -> BlockInputs:
+    """Seeded block tensors drawn in fp64 from ``PCG64(seed)`` in the order
+    xbc -> weight -> bias -> z: xbc, z ~ N(0, 1); weight and bias ~ U[-1/sqrt(width),
+    1/sqrt(width)] (the usual fan-in scale of a depthwise convolution).  In packed
+    inputs the padding tokens' xbc is zero, like the forward's padding."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    b, T, H, P = inp.x.shape
+    G, N = inp.B.shape[2], inp.B.shape[3]
+    CC = H * P + 2 * G * N
+    dtype = "bf16" if inp.x.dtype == torch.bfloat16 else "fp32"
+    xbc = rng.standard_normal((b, T, CC))
+    bound = 1.0 / math.sqrt(width)
+    w = rng.uniform(-bound, bound, size=(CC, width))
+    bias = rng.uniform(-bound, bound, size=CC)
+    z = rng.standard_normal((b, T, H, P))
+    if inp.seq_idx is not None and inp.real_tokens < T:
+        xbc[:, inp.real_tokens:] = 0.0
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a.astype(np.float32)))
+    return BlockInputs(xbc=_cast(xbc, dtype), weight=f32(w), bias=f32(bias) if with_bias else None,
+                       z=_cast(z, dtype), width=width)

@@ -633,3 +633,104 @@ def test_backward_finite_differences():
             fd = (lp - lm) / (2 * eps)
             got = getattr(gr, gname).reshape(-1)[i]
             assert got == pytest.approx(fd, rel=1e-6, abs=1e-8), (k, i)
+
+
+# ---------------------------------------------------------------------------
+# the block's convolution prologue and gate epilogue ([scwac], section five, the
+# Mamba-2 block's data flow)
+# ---------------------------------------------------------------------------
+
+def _conv_case(seed, b=2, T=29, Cc=12, K=4):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((b, T, Cc)), rng.uniform(-0.5, 0.5, (Cc, K)), rng.uniform(-0.5, 0.5, Cc))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_conv_is_numpy_convolve_per_channel(K):
+    """Without segments every channel is a full linear convolution with the taps
+    reversed, cut to the first T outputs (numpy's routine)."""
+    xbc, w, bias = _conv_case(10 + K, K=K)
+    v = oracle.causal_conv1d(xbc, w, bias)
+    b, T, Cc = xbc.shape
+    for i in range(b):
+        for c in range(Cc):
+            ref = np.convolve(xbc[i, :, c], w[c, ::-1])[:T] + bias[c]
+            np.testing.assert_allclose(v[i, :, c], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv_is_torch_depthwise_conv1d():
+    """The same convolution as torch's grouped conv1d (one group per channel,
+    K-1 zeros of padding, first T outputs), and SiLU as torch's, in fp64."""
+    import torch
+    import torch.nn.functional as F
+    xbc, w, bias = _conv_case(3, b=3, T=41, Cc=20, K=4)
+    xt = torch.from_numpy(xbc).transpose(1, 2)          # [b, C, T]
+    ref = F.conv1d(xt, torch.from_numpy(w)[:, None, :], torch.from_numpy(bias), padding=3, groups=20)
+    ref = F.silu(ref[..., :41]).transpose(1, 2).numpy()
+    got = oracle.silu(oracle.causal_conv1d(xbc, w, bias))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_silu_closed_forms():
+    # SiLU(0) = 0; sigma(ln 3) = 3/4; SiLU(v) - SiLU(-v) = v; the tails
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert oracle.silu(np.array([math.log(3.0)]))[0] == pytest.approx(0.75 * math.log(3.0), rel=1e-15)
+    v = np.linspace(-7, 7, 57)
+    np.testing.assert_allclose(oracle.silu(v) - oracle.silu(-v), v, rtol=0, atol=1e-14)
+    assert oracle.silu(np.array([60.0]))[0] == pytest.approx(60.0, rel=1e-20)
+    assert abs(oracle.silu(np.array([-60.0]))[0]) < 1e-24
+    assert oracle.silu(np.array([-800.0]))[0] == 0.0      # e^800 overflows to inf: -800/inf = -0
+
+
+def test_conv_is_causal_and_local():
+    """A change of the input at t* moves exactly the outputs t* .. t*+K-1."""
+    K, ts = 4, 11
+    xbc, w, bias = _conv_case(5, K=K)
+    v0 = oracle.causal_conv1d(xbc, w, bias)
+    x2 = xbc.copy()
+    x2[:, ts, :] += 1.0
+    v1 = oracle.causal_conv1d(x2, w, bias)
+    T = xbc.shape[1]
+    np.testing.assert_array_equal(v0[:, :ts], v1[:, :ts])
+    np.testing.assert_array_equal(v0[:, ts + K:], v1[:, ts + K:])
+    # the difference is the taps themselves: d v[t*+j] = w[:, K-1-j]
+    for j in range(K):
+        np.testing.assert_allclose(v1[:, ts + j] - v0[:, ts + j], np.broadcast_to(w[:, K - 1 - j], (2, 12)),
+                                   rtol=1e-12, atol=1e-12)
+    assert T > ts + K
+
+
+def test_conv_restarts_in_every_packed_sequence():
+    """Packed: the output equals each sequence convolved on its own."""
+    xbc, w, bias = _conv_case(6, b=1, T=30, K=4)
+    lens = [7, 2, 1, 14, 6]
+    seq = np.concatenate([np.full(L, i, np.int32) for i, L in enumerate(lens)])
+    got = oracle.causal_conv1d(xbc, w, bias, seq_idx=seq)
+    o = 0
+    for L in lens:
+        np.testing.assert_array_equal(got[:, o:o + L], oracle.causal_conv1d(xbc[:, o:o + L], w, bias))
+        o += L
+
+
+def test_conv1d_silu_splits_x_then_B_then_C():
+    """One tap of weight 1 and no bias turns the convolution into SiLU of the input
+    itself; channel k of xbc holds the value k/100, so every output names the
+    channel it came from: x takes 0 .. H*P-1 (head-major), B the next G*N (group-
+    major), C the last G*N."""
+    b, T, H, P, G, N = 1, 3, 2, 3, 2, 2
+    Cc = H * P + 2 * G * N
+    xbc = np.broadcast_to(np.arange(Cc) / 100.0, (b, T, Cc)).copy()
+    x, Bm, Cm = oracle.conv1d_silu(xbc, np.ones((Cc, 1)), H, P, G, N)
+    s = lambda k: (k / 100.0) / (1.0 + math.exp(-k / 100.0))
+    assert x[0, 2, 1, 2] == pytest.approx(s(1 * P + 2), rel=1e-15)
+    assert Bm[0, 0, 1, 0] == pytest.approx(s(H * P + 1 * N + 0), rel=1e-15)
+    assert Cm[0, 1, 0, 1] == pytest.approx(s(H * P + G * N + 1), rel=1e-15)
+
+
+def test_gate_is_y_times_torch_silu():
+    import torch
+    rng = np.random.default_rng(8)
+    y, z = rng.standard_normal((2, 5, 3, 4)), rng.standard_normal((2, 5, 3, 4)) * 4
+    ref = y * torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(oracle.gated(y, z), ref, rtol=1e-13, atol=1e-15)
+    assert np.all(oracle.gated(y, np.zeros_like(z)) == 0.0)
