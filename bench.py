@@ -275,6 +275,75 @@ def run_decode(dev, reps, warmup):
                          "traffic": measured_traffic("ssd_step", s.name), "algorithmic_bytes": int(nbytes)}}
 
 
+def _event_ms(fn, reps, warmup, stream):
+    """Per-call times of fn (ms) between HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b_ in ev:
+        a.record(stream)
+        fn()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b_) for a, b_ in ev]
+
+
+def run_block(dev, inp, g, reps, warmup):
+    """The Mamba-2 block's steps around the SSD on the workload's shape: the
+    convolution prologue (ssd_conv1d_silu) and the forward with the SiLU(z) gate
+    fused into its last kernel (ssd_fwd_gated), each timed alone and chained,
+    beside the plain forward and an unfused gate (torch's y * silu(z)) for
+    comparison.  Seeded block inputs; HIP events on the launch stream."""
+    import torch
+    from ssd_chunked_scan_amd import ssd
+    from ssd_chunked_scan_amd import workloads as wl
+
+    blk = wl.block_inputs(inp, seed=4000)
+    b, T, H, P = inp.x.shape
+    G, N = inp.B.shape[2], inp.B.shape[3]
+    nseq = inp.nseq if inp.seq_idx is not None else None
+    xbc, wt, bias, z = (t.to(dev) for t in (blk.xbc, blk.weight, blk.bias, blk.z))
+    x, Bm, Cm = ssd.conv1d_silu(xbc, wt, H, P, G, N, bias=bias, seq_idx=g.seq_idx)
+    p = ssd.Problem(x, g.dt, g.A, Bm, Cm, inp.chunk, g.D, g.initial_states, g.seq_idx, nseq)
+    ws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    yg = torch.empty_like(x)
+    fin = torch.empty(p.final_shape(), dtype=torch.float32, device=dev)
+    kw = dict(D=g.D, initial_states=g.initial_states, seq_idx=g.seq_idx, nseq=nseq, final_states=fin, workspace=ws)
+    stream = torch.cuda.current_stream(dev)
+
+    conv = lambda: ssd.conv1d_silu(xbc, wt, H, P, G, N, bias=bias, seq_idx=g.seq_idx, x=x, B=Bm, C=Cm)
+    gated = lambda: ssd.fwd_gated(x, g.dt, g.A, Bm, Cm, inp.chunk, z, y=yg, **kw)
+    plain = lambda: ssd.fwd(x, g.dt, g.A, Bm, Cm, inp.chunk, y=y, **kw)
+    unfused_gate = lambda: torch.mul(y, torch.nn.functional.silu(z), out=yg)
+
+    def chain():
+        conv()
+        gated()
+
+    ms = {k: sum(v) / len(v) for k, v in (("conv", _event_ms(conv, reps, warmup, stream)),
+                                         ("fwd_gated", _event_ms(gated, reps, warmup, stream)),
+                                         ("fwd", _event_ms(plain, reps, warmup, stream)),
+                                         ("unfused_gate", _event_ms(unfused_gate, reps, warmup, stream)),
+                                         ("block", _event_ms(chain, reps, warmup, stream)))}
+    esz = 2 if x.dtype == torch.bfloat16 else 4
+    CC = H * P + 2 * G * N
+    conv_bytes = 2 * b * T * CC * esz + CC * blk.width * 4 + CC * 4 + (T * 4 if nseq else 0)
+    ach = conv_bytes / (ms["conv"] / 1e3) / 1e9
+    return {"conv_ms": round(ms["conv"], 5), "fwd_gated_ms": round(ms["fwd_gated"], 5),
+            "fwd_ms": round(ms["fwd"], 5), "gate_cost_ms": round(ms["fwd_gated"] - ms["fwd"], 5),
+            "unfused_gate_ms": round(ms["unfused_gate"], 5), "block_ms": round(ms["block"], 5),
+            "block_tokens_per_s": round(inp.real_tokens / (ms["block"] / 1e3), 1), "conv_width": blk.width,
+            "conv_roofline": {"kernel": "conv1d_silu", "bound": "hbm", "achieved": round(ach, 1),
+                              "peak": PEAK["hbm_gbs"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_gbs"], 4),
+                              "traffic": measured_traffic("conv1d_silu", inp.name),
+                              "algorithmic_bytes": int(conv_bytes)},
+            "note": "block_ms = conv1d_silu + fwd_gated back to back; unfused_gate_ms is torch's "
+                    "y * silu(z) on the plain forward's y, for comparison only"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +354,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-block", action="store_true", help="skip the block (conv + gate) measurement")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB (3 times), as the "
@@ -410,6 +480,7 @@ def main():
     total_flops = sum(w.get("flops", 0.0) for w in work.values())
     decode = None if args.no_decode else run_decode(dev, reps, 5)
     backward = None if args.no_backward else run_backward(dev, inp, g, max(5, min(reps, 20)), 3)
+    block = None if args.no_block else run_block(dev, inp, g, max(5, min(reps, 50)), 3)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -431,6 +502,7 @@ def main():
         "kernels": kernels,
         "backward": backward,
         "decode": decode,
+        "block": block,
     }
     print(json.dumps(line), flush=True)
 

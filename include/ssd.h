@@ -247,6 +247,46 @@ ssd_status ssd_bwd_workspace_size(const ssd_fwd_args *args, size_t *bytes);
  * or the workspace. */
 ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *grads, void *stream);
 
+/*
+ * The Mamba-2 block around the SSD ("SSM 家族全景图（下）：Mamba-2 与 Jamba",
+ * section five, the block's data flow): the main path passes a causal
+ * one-dimensional convolution and a SiLU before the SSD; the gate path passes a
+ * SiLU; the two are multiplied elementwise.
+ *
+ * ssd_fwd_gated: ssd_fwd whose output is y * SiLU(z), the multiply fused into
+ * the last kernel before the single rounding of y (SiLU(v) = v / (1 + e^-v)).
+ * z is [b,T,H,P] in the dtype and must not overlap y or final_states; the final
+ * states are not gated.  Everything else as ssd_fwd.
+ */
+ssd_status ssd_fwd_gated(const ssd_fwd_args *args, const void *z, void *stream);
+
+/*
+ * ssd_conv1d_silu: the convolution prologue, channels xBC = [x | B | C] of
+ * width H*P + 2*G*N, each convolved over time with its own `width` taps and
+ * passed through SiLU, then written split into the SSD's x, B and C:
+ *
+ *   v[b,t,c] = SiLU(bias[c] + sum_{k<width} weight[c][k] * xbc[b, t-(width-1)+k, c])
+ *
+ * with xbc taken as zero before the sequence start, and with seq_idx before the
+ * start of t's segment (the convolution restarts in every packed sequence).
+ * Supported: width 1..4, P and N multiples of 16, H % G == 0; seq_idx needs
+ * batch == 1.  Outputs must not overlap the inputs or each other.
+ */
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, ngroups, dstate, width; /* b, T, H, P, G, N, taps */
+    int32_t dtype;                 /* ssd_dtype of xbc, x, B and C */
+    int32_t reserved;
+    const void *xbc;               /* [b,T,H*P + 2*G*N] dtype */
+    const float *weight;           /* [H*P + 2*G*N, width] fp32 */
+    const float *bias;             /* [H*P + 2*G*N] fp32, or NULL */
+    const int32_t *seq_idx;        /* [T] int32 segment ids, or NULL */
+    void *x;                       /* [b,T,H,P] dtype, out */
+    void *B;                       /* [b,T,G,N] dtype, out */
+    void *C;                       /* [b,T,G,N] dtype, out */
+} ssd_conv_args;
+
+ssd_status ssd_conv1d_silu(const ssd_conv_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,7 @@
 
 #include "ssd_kernels.hpp"
 #include "ssd_bwd_kernels.hpp"
+#include "ssd_block_kernels.hpp"
 
 using namespace ssd;
 
@@ -275,12 +276,12 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, true>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
-                                   (float *)nullptr, (float *)nullptr);
+                                   (float *)nullptr, (float *)nullptr, (const E *)nullptr);
             else
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
-                                   (float *)nullptr, (float *)nullptr);
+                                   (float *)nullptr, (float *)nullptr, (const E *)nullptr);
             return launched();
         });
     });
@@ -299,7 +300,30 @@ ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delt
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
             hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false, DOT, P1ONLY>), grid, dim3(scan_threads<Q>()), 0, st,
                                (const E *)a->x, delta, cs, cb, hin, a->D, (const int32_t *)nullptr, (E *)a->y,
-                               (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, vec, dot1, dot2);
+                               (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, vec, dot1, dot2,
+                               (const E *)nullptr);
+            return launched();
+        });
+    });
+}
+
+// chunk_scan with the SiLU(z) gate fused into its epilogue.
+template <typename E>
+ssd_status run_scan_gated(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
+                          const E *hin, const E *z, hipStream_t st)
+{
+    const int ntp = (int)((s.P + 63) / 64);
+    dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
+    return with_q(s.Q, [&](auto q) {
+        return with_nt(s.N, [&](auto nt) {
+            constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
+            auto launch = [&](auto kern) {
+                hipLaunchKernelGGL(kern, grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x, delta, cs, cb, hin,
+                                   a->D, a->seq_idx, (E *)a->y, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
+                                   (int)s.nc, ntp, (const E *)nullptr, (float *)nullptr, (float *)nullptr, z);
+            };
+            if (s.packed) launch(k_chunk_scan<E, Q, NT, true, 0, false, true>);
+            else launch(k_chunk_scan<E, Q, NT, false, 0, false, true>);
             return launched();
         });
     });
@@ -316,7 +340,8 @@ ssd_status fill_final(const Shape &s, const ssd_fwd_args *a, hipStream_t st)
 }
 
 template <typename E>
-ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, hipStream_t st)
+ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, hipStream_t st,
+                     const E *gate = nullptr)
 {
     char *ws = static_cast<char *>(a->workspace);
     float *delta = reinterpret_cast<float *>(ws + w.delta);
@@ -331,6 +356,7 @@ ssd_status fwd_typed(const Shape &s, const ssd_fwd_args *a, const Workspace &w, 
     if ((r = run_passing<E>(s, a, cs, states, s.packed ? nullptr : a->final_states, st)) != SSD_OK) return r;
     if (seq_final)
         if ((r = run_seq_final<E>(s, a, delta, cs, states, seg_end, true, st)) != SSD_OK) return r;
+    if (gate) return run_scan_gated<E>(s, a, delta, cs, cb, states, gate, st);
     return run_scan<E>(s, a, delta, cs, cb, states, st);
 }
 
@@ -352,6 +378,32 @@ ssd_status run_step(const ssd_step_args *a, hipStream_t st)
     if (need <= 16) return launch(std::integral_constant<int, 16>{});
     if (need <= 32) return launch(std::integral_constant<int, 32>{});
     return launch(std::integral_constant<int, 64>{});
+}
+
+template <typename E>
+ssd_status run_conv(const ssd_conv_args *a, hipStream_t st)
+{
+    const int CX = (int)(a->nheads * a->headdim), CG = (int)(a->ngroups * a->dstate);
+    const int64_t nb = (a->seqlen + kConvTB - 1) / kConvTB;
+    const int64_t items = a->batch * nb * ((CX + 2 * CG) / (16 / (int)sizeof(E)));   // one 16-byte vector each
+    auto launch = [&](auto kk) {
+        constexpr int K = decltype(kk)::value;
+        if (a->seq_idx)
+            hipLaunchKernelGGL((k_conv1d_silu<E, K, true>), dim3(grid1(items, kThreads)), dim3(kThreads), 0, st,
+                               (const E *)a->xbc, a->weight, a->bias, a->seq_idx, (E *)a->x, (E *)a->B,
+                               (E *)a->C, (int)a->seqlen, CX, CG, items);
+        else
+            hipLaunchKernelGGL((k_conv1d_silu<E, K, false>), dim3(grid1(items, kThreads)), dim3(kThreads), 0, st,
+                               (const E *)a->xbc, a->weight, a->bias, a->seq_idx, (E *)a->x, (E *)a->B,
+                               (E *)a->C, (int)a->seqlen, CX, CG, items);
+        return launched();
+    };
+    switch (a->width) {
+    case 1: return launch(std::integral_constant<int, 1>{});
+    case 2: return launch(std::integral_constant<int, 2>{});
+    case 3: return launch(std::integral_constant<int, 3>{});
+    default: return launch(std::integral_constant<int, 4>{});
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -775,6 +827,70 @@ ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream
         return launched();
     }
     return s.dtype == SSD_DTYPE_BF16 ? bwd_typed<bf16>(s, args, g, w, hs) : bwd_typed<float>(s, args, g, w, hs);
+}
+
+ssd_status ssd_fwd_gated(const ssd_fwd_args *args, const void *z, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB | kNeedC | kNeedY | kCheckFinal)) != SSD_OK)
+        return r;
+    if (s.T > 0 && !z) return SSD_ERR_NULL_POINTER;
+    if (z && !aligned16(z)) return SSD_ERR_MISALIGNED;
+    const Sizes zs = tensor_sizes(s);
+    const Range zr{z, zs.x};
+    if (overlaps(zr, Range{args->y, zs.y}) || overlaps(zr, Range{args->final_states, zs.fin}))
+        return SSD_ERR_ALIASING;
+    const Workspace w = workspace_layout(s);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.T == 0) return fill_final(s, args, st);
+    if (!args->workspace) return SSD_ERR_NULL_POINTER;
+    if (args->workspace_bytes < w.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    const Range ws{args->workspace, w.total};
+    const Range others[] = {{args->x, zs.x}, {args->dt, zs.dt}, {args->A, zs.A}, {args->B, zs.bc}, {args->C, zs.bc},
+                            {args->D, zs.D}, {args->initial_states, zs.init}, {args->seq_idx, zs.seq},
+                            {args->y, zs.y}, {args->final_states, zs.fin}, zr};
+    for (const Range &o : others)
+        if (overlaps(ws, o)) return SSD_ERR_ALIASING;
+    return s.dtype == SSD_DTYPE_BF16 ? fwd_typed<bf16>(s, args, w, st, (const bf16 *)z)
+                                     : fwd_typed<float>(s, args, w, st, (const float *)z);
+}
+
+ssd_status ssd_conv1d_silu(const ssd_conv_args *a, void *stream)
+{
+    if (!a) return SSD_ERR_NULL_POINTER;
+    if (a->dtype != SSD_DTYPE_F32 && a->dtype != SSD_DTYPE_BF16) return SSD_ERR_BAD_DTYPE;
+    if (a->batch < 1 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 16 || a->ngroups < 1 || a->dstate < 16 ||
+        a->width < 1 || a->width > 4)
+        return SSD_ERR_BAD_SHAPE;
+    if (a->headdim % 16 != 0 || a->dstate % 16 != 0 || a->batch > kMaxDim || a->seqlen > kMaxDim)
+        return SSD_ERR_BAD_SHAPE;
+    const int64_t CC = a->nheads * a->headdim + 2 * a->ngroups * a->dstate;
+    if (CC > INT32_MAX / 4 || a->batch * a->seqlen * CC > ((int64_t)1 << 40))
+        return SSD_ERR_BAD_SHAPE;
+    if (a->nheads % a->ngroups != 0) return SSD_ERR_GROUPS;
+    if (a->seq_idx && a->batch != 1) return SSD_ERR_SEQ_IDX;
+    if (a->seqlen == 0) return SSD_OK;
+    if (!a->xbc || !a->weight || !a->x || !a->B || !a->C) return SSD_ERR_NULL_POINTER;
+    const void *ptrs[] = {a->xbc, a->weight, a->bias, a->seq_idx, a->x, a->B, a->C};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+    const size_t esz = a->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    const int64_t bt = a->batch * a->seqlen;
+    const Range in[] = {{a->xbc, (size_t)(bt * CC) * esz}, {a->weight, (size_t)(CC * a->width) * 4},
+                        {a->bias, (size_t)CC * 4}, {a->seq_idx, (size_t)a->seqlen * 4}};
+    const Range out[] = {{a->x, (size_t)(bt * a->nheads * a->headdim) * esz},
+                         {a->B, (size_t)(bt * a->ngroups * a->dstate) * esz},
+                         {a->C, (size_t)(bt * a->ngroups * a->dstate) * esz}};
+    for (size_t i = 0; i < 3; ++i) {
+        for (const Range &r : in)
+            if (overlaps(out[i], r)) return SSD_ERR_ALIASING;
+        for (size_t j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], out[j])) return SSD_ERR_ALIASING;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return a->dtype == SSD_DTYPE_BF16 ? run_conv<bf16>(a, st) : run_conv<float>(a, st);
 }
 
 }  // extern "C"

@@ -36,6 +36,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 // 2^x for arguments already scaled by log2(e) (v_exp_f32 alone).
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+// SiLU(v) = v / (1 + e^-v) with the hardware exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each) instead of a correctly rounded
+// divide.  v -> -inf gives -0 (the reciprocal of inf is 0).
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + exp2_(-v * kLog2e)); }
 
 template <typename E> struct Frag;
 template <> struct Frag<bf16> { using type = bf16x8; };

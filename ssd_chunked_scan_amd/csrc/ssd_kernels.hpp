@@ -1051,13 +1051,17 @@ template <int Q> constexpr int scan_threads() { return Q * 2; }
 //   dot1 = v . (the entering-state term alone),  dot2 (DOT = 2) = v . (the whole
 //   output before the D skip term).
 // P1ONLY computes dot1 only: no x tile, no intra-chunk terms, no y.
-template <typename E, int Q, int NT, bool PACKED, int DOT = 0, bool P1ONLY = false>
+// GATE multiplies every output by SiLU(z) (z = `gate`, laid out like y) before
+// its one rounding to E: the gate of the Mamba-2 block ("SSM 家族全景图（下）",
+// the block data flow of section five: the gated path passes a SiLU and the two
+// paths are multiplied elementwise).
+template <typename E, int Q, int NT, bool PACKED, int DOT = 0, bool P1ONLY = false, bool GATE = false>
 __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
     const E *__restrict__ cbuf, const E *__restrict__ hin,
     const float *__restrict__ D, const int32_t *__restrict__ seq_idx, E *__restrict__ y,
     int T, int H, int G, int P, int N, int nc, int ntp, const E *__restrict__ vec = nullptr,
-    float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr)
+    float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr, const E *__restrict__ gate = nullptr)
 {
     using F = frag_t<E>;
     constexpr int TH = scan_threads<Q>();
@@ -1270,6 +1274,49 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
             for (int q = 0; q < 4; ++q) acc[k][pb][q] = mo ? acc[k][pb][q] * e0 : 0.f;
     }
 
+    // Row-wise view of this wave's tile, used to turn y (and the gate's z) around
+    // in the entering-state region (bf16): lane (oct, chunk) takes 16 bytes, p0 +
+    // 8 chunk .. + 7, of row 16 j + 8 half + rsel.  Rows sit in LDS with their 8
+    // chunks of 16 bytes at chunk ^ ((t >> 1) & 7), so the 8-byte accesses of 16
+    // rows in the accumulator layout spread over all banks; the 16-byte row
+    // accesses take 8 rows per instruction, ordered so that the two lane octets
+    // sharing an LDS pass (0-7 with 16-23, ...) touch rows of opposite parity,
+    // i.e. opposite bank halves.
+    auto yoff = [](int t, int ch) { return t * 64 + 8 * (ch ^ ((t >> 1) & 7)); };
+    const int oct = lane >> 3, chunk = lane & 7;
+    const int rsel = (oct & 4) + ((oct & 1) << 1) + ((oct >> 1) & 1);   // 0,2,1,3,4,6,5,7
+    const bool pin = p0 + 8 * chunk < P;
+
+    // The gate's z (GATE), loaded before the diagonal step so that the loads
+    // overlap its MFMA work.  bf16: in the row-wise view above (whole 128-byte
+    // rows, 8 per instruction), turned around in LDS before use; fp32: four
+    // consecutive p of token t per (sub-block, p block), straight into the
+    // accumulator layout.
+    using E4 = E __attribute__((ext_vector_type(4)));
+    constexpr bool ZROW = sizeof(E) == 2;
+    E4 zr[NSB][4];
+    uint4 zrow[NSB][2];
+    auto load_z = [&](int k) {
+        if constexpr (ZROW) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int t = 16 * jb[k] + 8 * half + rsel;
+                zrow[k][half] = live[k] && t < len && pin
+                                    ? *reinterpret_cast<const uint4 *>(
+                                          gate + (((int64_t)b * T + t0 + t) * H + h) * P + p0 + 8 * chunk)
+                                    : uint4{0, 0, 0, 0};
+            }
+        } else {
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int t = 16 * jb[k] + li, p = p0 + 16 * pb + 4 * lg;
+                zr[k][pb] = live[k] && t < len && p < P
+                                ? *reinterpret_cast<const E4 *>(gate + (((int64_t)b * T + t0 + t) * H + h) * P + p)
+                                : E4{};
+            }
+        }
+    };
+
     __syncthreads();   // the V table is complete
     typename XT::Off xoff[4];
 #pragma unroll
@@ -1297,6 +1344,11 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
             for (int k = 0; k < NSB; ++k) bload_frag(cbrs, cb_off(k, ks + RING), cr[ks % RING][k]);
         }
+    }
+
+    if constexpr (GATE) {
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) load_z(k);
     }
 
     // ---- u_t scale, then the diagonal K step with per-element decays and D ----
@@ -1338,15 +1390,51 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 
     if constexpr (DOT == 2) dot_out(dot2, [](int, int) { return 1.f; });
 
+    if constexpr (GATE) {
+        // y *= SiLU(z) in fp32, before the one rounding of y
+        if constexpr (ZROW) {
+#pragma unroll
+            for (int k = 0; k < NSB; ++k)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    *reinterpret_cast<uint4 *>(hs + yoff(16 * jb[k] + 8 * half + rsel, chunk)) = zrow[k][half];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int k = 0; k < NSB; ++k) {
+                const int t = 16 * jb[k] + li;
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const floatx4 zf = __builtin_convertvector(
+                        *reinterpret_cast<const bf16x4 *>(hs + yoff(t, 2 * pb + (lg >> 1)) + 4 * (lg & 1)), floatx4);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[k][pb][q] *= silu(zf[q]);
+                }
+            }
+            // every lane has read its z before the same rows take y below
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        } else {
+#pragma unroll
+            for (int k = 0; k < NSB; ++k) {
+                if (!live[k]) continue;
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const floatx4 zf = __builtin_convertvector(zr[k][pb], floatx4);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[k][pb][q] *= silu(zf[q]);
+                }
+            }
+        }
+    }
+
     // ---- epilogue: store y ----
     if constexpr (sizeof(E) == 2) {
         // Each wave turns its own 32 rows around in the entering-state region (free
-        // since the barrier after step 4) so that y leaves as whole 128-byte rows.
-        // Rows have 8 chunks of 16 bytes stored at chunk ^ ((t >> 1) & 7): the 8-byte
-        // writes of 16 rows spread over all banks.  The 16-byte reads take 8 rows
-        // per instruction, ordered so that the two lane octets sharing an LDS pass
-        // (0-7 with 16-23, ...) read rows of opposite parity, i.e. opposite bank halves.
-        auto yoff = [](int t, int chunk) { return t * 64 + 8 * (chunk ^ ((t >> 1) & 7)); };
+        // since the barrier after step 4) so that y leaves as whole 128-byte rows
+        // (the row-wise view above).
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
             const int t = 16 * jb[k] + li;
@@ -1359,9 +1447,6 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int oct = lane >> 3, chunk = lane & 7;
-        const int rsel = (oct & 4) + ((oct & 1) << 1) + ((oct >> 1) & 1);   // 0,2,1,3,4,6,5,7
-        const bool pin = p0 + 8 * chunk < P;
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
 #pragma unroll

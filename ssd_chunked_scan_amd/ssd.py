@@ -26,7 +26,8 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
 EXPORTED = ["ssd_abi_version", "ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd",
             "ssd_chunk_cumsum", "ssd_chunk_cb", "ssd_chunk_state", "ssd_state_passing",
-            "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step", "ssd_bwd_workspace_size", "ssd_bwd"]
+            "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step", "ssd_bwd_workspace_size", "ssd_bwd",
+            "ssd_fwd_gated", "ssd_conv1d_silu"]
 
 
 class FwdArgs(ctypes.Structure):
@@ -66,6 +67,17 @@ class BwdArgs(ctypes.Structure):
     ]
 
 
+class ConvArgs(ctypes.Structure):
+    """Mirror of ``ssd_conv_args``."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("width", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("xbc", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("seq_idx", ctypes.c_void_p), ("x", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+    ]
+
+
 class SSDError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -100,6 +112,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_step.argtypes = [ctypes.POINTER(StepArgs), vp]
     lib.ssd_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.ssd_bwd.argtypes = [P, ctypes.POINTER(BwdArgs), vp]
+    lib.ssd_fwd_gated.argtypes = [P, vp, vp]
+    lib.ssd_conv1d_silu.argtypes = [ctypes.POINTER(ConvArgs), vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -206,7 +220,24 @@ def fwd(x, dt, A, B, C, chunk, D=None, initial_states=None, seq_idx=None, nseq=N
     ``y``, ``final_states`` and ``workspace`` may be passed pre-allocated (e.g.
     for timing loops); otherwise they are allocated with ``torch.empty``.
     """
+    return _fwd(None, x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus, y,
+                final_states, workspace, stream, want_final)
+
+
+def fwd_gated(x, dt, A, B, C, chunk, z, D=None, initial_states=None, seq_idx=None, nseq=None,
+              dt_softplus=True, y=None, final_states=None, workspace=None, stream=None,
+              want_final=True):
+    """y * SiLU(z), final_states (``ssd_fwd_gated``): the forward with the block's
+    gate fused into its last kernel; z is [b,T,H,P] like x."""
+    return _fwd(z, x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus, y,
+                final_states, workspace, stream, want_final)
+
+
+def _fwd(z, x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus, y, final_states,
+         workspace, stream, want_final):
     p = Problem(x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus)
+    if z is not None:
+        _check(z, "z", x.dtype, x.shape, p.device)
     if y is None:
         y = p.empty(x.shape)
     _check(y, "y", x.dtype, x.shape, p.device)
@@ -221,8 +252,51 @@ def fwd(x, dt, A, B, C, chunk, D=None, initial_states=None, seq_idx=None, nseq=N
     p.args.final_states = _ptr(final_states)
     p.args.workspace = _ptr(workspace)
     p.args.workspace_bytes = workspace.numel()
-    p.call("ssd_fwd", stream=stream)
+    if z is None:
+        p.call("ssd_fwd", stream=stream)
+    else:
+        p.call("ssd_fwd_gated", _ptr(z), stream=stream)
     return y, final_states
+
+
+# ---------------------------------------------------------------------------
+# the block's convolution prologue
+# ---------------------------------------------------------------------------
+
+def conv1d_silu(xbc, weight, nheads, headdim, ngroups, dstate, bias=None, seq_idx=None, x=None, B=None, C=None,
+                stream=None):
+    """x, B, C = split(SiLU(causal depthwise conv1d(xbc) + bias)) (``ssd_conv1d_silu``):
+    xbc [b,T,H*P + 2*G*N] fp32/bf16, weight [H*P + 2*G*N, width] fp32, bias fp32 or
+    None, seq_idx [T] int32 or None (batch 1); x [b,T,H,P], B and C [b,T,G,N]."""
+    if xbc.dim() != 3:
+        raise ValueError("xbc must be [batch, seqlen, channels]")
+    if xbc.dtype not in _DTYPES:
+        raise TypeError("xbc must be float32 or bfloat16")
+    b, T, CC = xbc.shape
+    dev = xbc.device
+    if CC != nheads * headdim + 2 * ngroups * dstate:
+        raise ValueError("xbc must have nheads*headdim + 2*ngroups*dstate channels")
+    _check(xbc, "xbc", device=dev)
+    if weight.dim() != 2:
+        raise ValueError("weight must be [channels, width]")
+    _check(weight, "weight", torch.float32, (CC, weight.shape[1]), dev)
+    _check(bias, "bias", torch.float32, (CC,), dev)
+    if seq_idx is not None:
+        _check(seq_idx, "seq_idx", torch.int32, (T,), dev)
+    x = torch.empty((b, T, nheads, headdim), dtype=xbc.dtype, device=dev) if x is None else x
+    B = torch.empty((b, T, ngroups, dstate), dtype=xbc.dtype, device=dev) if B is None else B
+    C = torch.empty((b, T, ngroups, dstate), dtype=xbc.dtype, device=dev) if C is None else C
+    _check(x, "x", xbc.dtype, (b, T, nheads, headdim), dev)
+    _check(B, "B", xbc.dtype, (b, T, ngroups, dstate), dev)
+    _check(C, "C", xbc.dtype, (b, T, ngroups, dstate), dev)
+    a = ConvArgs(batch=b, seqlen=T, nheads=nheads, headdim=headdim, ngroups=ngroups, dstate=dstate,
+                 width=weight.shape[1], dtype=_DTYPES[xbc.dtype], reserved=0, xbc=_ptr(xbc), weight=_ptr(weight),
+                 bias=_ptr(bias), seq_idx=_ptr(seq_idx), x=_ptr(x), B=_ptr(B), C=_ptr(C))
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    rc = load_library().ssd_conv1d_silu(ctypes.byref(a), ctypes.c_void_p(st))
+    if rc != 0:
+        raise SSDError(rc, "ssd_conv1d_silu")
+    return x, B, C
 
 
 # ---------------------------------------------------------------------------

@@ -195,3 +195,56 @@ def test_bwd_workspace_size(lib):
     assert n.value > m.value
     packed = _args(seq_idx=0x90000000, nseq=2)
     assert lib.ssd_bwd_workspace_size(ctypes.byref(packed), ctypes.byref(n)) == SEQ
+
+
+@pytest.mark.parametrize("z,code", [
+    (0, NULLP), (0xb0000008, MISAL),
+    (0x70000000, ALIAS),                 # z == y
+    (0x80000000 + 128, ALIAS),           # z inside final_states
+    (0x90000000, ALIAS),                 # z == workspace
+])
+def test_fwd_gated_rejects_invalid_gate(lib, z, code):
+    a = _args()
+    assert lib.ssd_fwd_gated(ctypes.byref(a), ctypes.c_void_p(z), None) == code
+
+
+def test_fwd_gated_checks_the_forward_arguments_too(lib):
+    assert lib.ssd_fwd_gated(ctypes.byref(_args(chunk=48)), ctypes.c_void_p(0xb0000000), None) == CHUNK
+    assert lib.ssd_fwd_gated(ctypes.byref(_args(y=0x10000000)), ctypes.c_void_p(0xb0000000), None) == ALIAS
+
+
+def _conv_args(**kw):
+    base = dict(batch=1, seqlen=256, nheads=4, headdim=64, ngroups=1, dstate=64, width=4, dtype=1)
+    base.update({k: v for k, v in kw.items() if k in base})
+    a = ssd.ConvArgs(**base)
+    addr = 0x10000000
+    for name in ("xbc", "weight", "bias", "x", "B", "C"):
+        setattr(a, name, kw.get(name, addr))
+        addr += 0x10000000
+    a.seq_idx = kw.get("seq_idx", 0)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), DTYPE),
+    (dict(width=0), SHAPE), (dict(width=5), SHAPE), (dict(headdim=8), SHAPE), (dict(dstate=24), SHAPE),
+    (dict(batch=0), SHAPE), (dict(seqlen=-1), SHAPE),
+    (dict(nheads=6, ngroups=4), GROUPS),
+    (dict(batch=2, seq_idx=0x90000000), SEQ),
+    (dict(xbc=0), NULLP), (dict(weight=0), NULLP), (dict(C=0), NULLP),
+    (dict(xbc=0x10000004), MISAL), (dict(bias=0x30000008), MISAL),
+    (dict(x=0x10000000 + 512), ALIAS),     # x inside xbc
+    (dict(B=0x60000000), ALIAS),           # B == C
+    (dict(C=0x20000000), ALIAS),           # C == weight
+    (dict(seqlen=0, xbc=0, x=0), OK),      # nothing to do, nothing read
+])
+def test_conv_rejects_invalid_arguments(lib, kw, code):
+    assert lib.ssd_conv1d_silu(ctypes.byref(_conv_args(**kw)), None) == code
+
+
+def test_conv_binding_checks_shapes():
+    xbc = torch.zeros(1, 8, 4 * 16 + 2 * 16)
+    with pytest.raises(ValueError, match="GPU"):
+        ssd.conv1d_silu(xbc, torch.zeros(96, 4), 4, 16, 1, 16)
+    with pytest.raises(ValueError, match="channels"):
+        ssd.conv1d_silu(xbc, torch.zeros(96, 4), 4, 16, 1, 32)
