@@ -864,10 +864,11 @@ ssd_status ssd_conv1d_silu(const ssd_conv_args *a, void *stream)
     if (a->batch < 1 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 16 || a->ngroups < 1 || a->dstate < 16 ||
         a->width < 1 || a->width > 4)
         return SSD_ERR_BAD_SHAPE;
-    if (a->headdim % 16 != 0 || a->dstate % 16 != 0 || a->batch > kMaxDim || a->seqlen > kMaxDim)
+    if (a->headdim % 16 != 0 || a->dstate % 16 != 0 || a->batch > kMaxDim || a->seqlen > kMaxDim ||
+        a->nheads > kMaxDim || a->headdim > kMaxDim || a->ngroups > kMaxDim || a->dstate > kMaxDim)
         return SSD_ERR_BAD_SHAPE;
     const int64_t CC = a->nheads * a->headdim + 2 * a->ngroups * a->dstate;
-    if (CC > INT32_MAX / 4 || a->batch * a->seqlen * CC > ((int64_t)1 << 40))
+    if (CC > INT32_MAX / 4 || a->batch * a->seqlen > ((int64_t)1 << 40) / CC)
         return SSD_ERR_BAD_SHAPE;
     if (a->nheads % a->ngroups != 0) return SSD_ERR_GROUPS;
     if (a->seq_idx && a->batch != 1) return SSD_ERR_SEQ_IDX;

@@ -54,7 +54,10 @@ __global__ __launch_bounds__(kThreads) void k_conv1d_silu(
 {
     constexpr int V = 16 / (int)sizeof(E);   // channels per thread
     constexpr int R = K - 1 + kConvTB;      // input rows per thread
-    const int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    // XCD-aware order: each XCD takes a contiguous range of workgroups, so the
+    // halo rows of a token block were fetched into the same L2 by the workgroup
+    // of the block before it
+    const int64_t it = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kThreads + threadIdx.x;
     if (it >= items) return;
     const int CC = CX + 2 * CG, GV = CC / V;
     const int nb = (T + kConvTB - 1) / kConvTB;

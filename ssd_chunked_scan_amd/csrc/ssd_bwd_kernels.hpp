@@ -411,45 +411,94 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
             // this head is complete: add it with its decays and step sizes, and
             // sum its S = W CB by rows and by columns
             float rs[2][4] = {}, cl[2] = {};
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int s = si * 64 + s_w + 16 * j + li;
-                const float css = hcs[1][s_w + 16 * j + li], ds = hds[s_w + 16 * j + li];
+            if (si < ti && (ti + 1) * 64 <= len) {
+                // a whole tile below the diagonal: W = e^{cs_t - ref} (Delta_s e^{ref - cs_s})
+                // with ref = cs at the s tile's last row, so for A <= 0 (cs
+                // non-increasing) both factors are at most 1 and none overflows
+                const float ref = hcs[1][63];
+                float at[2][4], bs[2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = ti * 64 + t_w + 16 * i + 4 * lg + r;
-                        if (s <= t && t < len) {
-                            const float w = __builtin_amdgcn_exp2f((hcs[0][t_w + 16 * i + 4 * lg + r] - css) * kLog2e) * ds;
-                            const float wv = acc[i][j][r] * w;
+                    for (int r = 0; r < 4; ++r)
+                        at[i][r] = __builtin_amdgcn_exp2f((hcs[0][t_w + 16 * i + 4 * lg + r] - ref) * kLog2e);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bs[j] = __builtin_amdgcn_exp2f((ref - hcs[1][s_w + 16 * j + li]) * kLog2e) * hds[s_w + 16 * j + li];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float wv = acc[i][j][r] * at[i][r] * bs[j];
                             tot[i][j][r] += wv;
                             const float sv = wv * cbv[i][j][r];
                             rs[i][r] += sv;
                             cl[j] += sv;
+                            acc[i][j][r] = 0.f;
                         }
-                        acc[i][j][r] = 0.f;
-                    }
-            }
-            // rows t: sum over the 16 lanes of a row group; columns s: over the 4 groups
+            } else {
+                // the diagonal tile or the ragged last one: the exact per-element
+                // decay, and only s <= t < len
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int j = 0; j < 2; ++j) {
+                    const int s = si * 64 + s_w + 16 * j + li;
+                    const float css = hcs[1][s_w + 16 * j + li], ds = hds[s_w + 16 * j + li];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = rs[i][r];
-                    v += __shfl_xor(v, 1);
-                    v += __shfl_xor(v, 2);
-                    v += __shfl_xor(v, 4);
-                    v += __shfl_xor(v, 8);
-                    if (li == 0) atomicAdd(&rsum[t_w + 16 * i + 4 * lg + r], v);
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t = ti * 64 + t_w + 16 * i + 4 * lg + r;
+                            if (s <= t && t < len) {
+                                const float w =
+                                    __builtin_amdgcn_exp2f((hcs[0][t_w + 16 * i + 4 * lg + r] - css) * kLog2e) * ds;
+                                const float wv = acc[i][j][r] * w;
+                                tot[i][j][r] += wv;
+                                const float sv = wv * cbv[i][j][r];
+                                rs[i][r] += sv;
+                                cl[j] += sv;
+                            }
+                            acc[i][j][r] = 0.f;
+                        }
                 }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float v = cl[j];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                if (lg == 0) atomicAdd(&csum[s_w + 16 * j + li], v);
             }
+            // Rows t (value m = 4 i + r) are summed over the 16 lanes li of a row
+            // group, columns s (value j) over the 4 groups lg, each by halving
+            // exchanges: at every xor step a lane keeps half of its values and
+            // adds its partner's copy of that half.  In the end lane li holds row
+            // value m = (li >> 1) & 7 and lane group lg column value j = lg >> 1.
+            float v8[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) v8[m] = rs[m >> 2][m & 3];
+            float v4[4], v2[2], v1, c1;
+            {
+                const bool up = li & 8;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    v4[m] = (up ? v8[m + 4] : v8[m]) + __shfl_xor(up ? v8[m] : v8[m + 4], 8);
+            }
+            {
+                const bool up = li & 4;
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    v2[m] = (up ? v4[m + 2] : v4[m]) + __shfl_xor(up ? v4[m] : v4[m + 2], 4);
+            }
+            {
+                const bool up = li & 2;
+                v1 = (up ? v2[1] : v2[0]) + __shfl_xor(up ? v2[0] : v2[1], 2);
+            }
+            v1 += __shfl_xor(v1, 1);
+            {
+                const bool up = lg & 2;
+                c1 = (up ? cl[1] : cl[0]) + __shfl_xor(up ? cl[0] : cl[1], 32);
+            }
+            c1 += __shfl_xor(c1, 16);
+            if ((li & 1) == 0) {
+                const int m = (li >> 1) & 7;
+                atomicAdd(&rsum[t_w + 16 * (m >> 2) + 4 * lg + (m & 3)], v1);
+            }
+            if ((lg & 1) == 0) atomicAdd(&csum[s_w + 16 * (lg >> 1) + li], c1);
         }
     }
     __syncthreads();

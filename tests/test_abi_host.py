@@ -229,6 +229,8 @@ def _conv_args(**kw):
     (dict(dtype=3), DTYPE),
     (dict(width=0), SHAPE), (dict(width=5), SHAPE), (dict(headdim=8), SHAPE), (dict(dstate=24), SHAPE),
     (dict(batch=0), SHAPE), (dict(seqlen=-1), SHAPE),
+    (dict(nheads=1 << 40, headdim=1 << 40), SHAPE),          # no int64 overflow in the channel count
+    (dict(batch=1 << 20, seqlen=1 << 20), SHAPE),            # beyond the supported element count
     (dict(nheads=6, ngroups=4), GROUPS),
     (dict(batch=2, seq_idx=0x90000000), SEQ),
     (dict(xbc=0), NULLP), (dict(weight=0), NULLP), (dict(C=0), NULLP),
