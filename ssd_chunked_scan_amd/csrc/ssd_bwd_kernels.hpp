@@ -533,9 +533,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
 // dC (MODE 0) and dB (MODE 1) of one (b, c, g), 64 rows x 64 columns n
 // ---------------------------------------------------------------------------
 // The output tile is computed transposed, D[n][r] (r = the output token), as one
-// long K loop of steps; each step stages a 64 (K) x 64 (n) operand tile in LDS
-// (read transposed) and streams the matching 16-byte fragments of the other
-// operand from memory, both loaded one step ahead into registers:
+// long K loop of steps; each step stages a 64 (K) x 64 (n) operand tile (read
+// transposed) and the matching 64 (r) x 64 (K) tile of the other operand in
+// LDS, both loaded one step ahead into registers with row-contiguous 16-byte
+// loads (whole 128-byte rows; loading the second operand as MFMA fragments,
+// 16 rows x 64 bytes per instruction, made the kernel three times slower):
 //   MODE 0, dC:  K = s over the s-tiles <= this tile:  B rows s   x  M[t][s]
 //                K = p over the group's heads:         Hin_h[p]   x  exp(cs_t) dy_h[t][p]
 //   MODE 1, dB:  K = t over the t-tiles >= this tile:  C rows t   x  M^T[s][t]
@@ -552,7 +554,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     using KT = KTile<E, 64, 64>;
     constexpr int ES = (int)sizeof(E);
     constexpr int QT = Q / 64;
+    constexpr int V = kVec16<E>;
+    constexpr int PITCH = 64 + 2 * V;   // rows 32 bytes past a multiple of 256 (bf16): conflict-free reads
+    constexpr int VPR = 64 / V, RPP = kThreads / VPR, NPASS = 64 / RPP;
     __shared__ __align__(16) E kt[KT::SIZE];
+    __shared__ __align__(16) E bt[64 * PITCH];   // the second operand, rows r
     const int units = nc * G * QT * nnt;
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
@@ -573,8 +579,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     KT ka, kb;   // the M-part and the state-part operand tiles (different row pitches)
     ka.init((int64_t)G * N, N - n0);
     kb.init(N, N - n0);
-    F fr[2][2];      // the streamed operand of the next step: [ks][j]
-    float sc[2];     // its per-column scales (state part)
+    // the second operand of the next step: rows r0 + hr + i RPP, 16 bytes at column hv V
+    const int hv = threadIdx.x % VPR, hr = threadIdx.x / VPR;
+    uint4 rb[NPASS];
+    float sc[2];     // the per-row scales of this lane's fragment rows (state part)
     auto issue = [&](int k) {
         if (k < nq) {
             const int q = q_lo + k, rows = min(64, len - q * 64);
@@ -582,28 +590,27 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
             const E *mb = mm + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
             const auto mrs = make_rsrc(mb, (int64_t)Q * Q * ES);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = r0 + c_w + 16 * j + li;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    bload_frag(mrs, r < len ? (uint32_t)(((int64_t)r * Q + q * 64 + ks * 32 + 8 * lg) * ES) : kOffNone,
-                               fr[ks][j]);
-                sc[j] = 1.f;
+            for (int i = 0; i < NPASS; ++i) {
+                const int r = r0 + hr + i * RPP;
+                rb[i] = bload16(mrs, r < len ? (uint32_t)(((int64_t)r * Q + q * 64 + hv * V) * ES) : kOffNone);
             }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sc[j] = 1.f;
         } else {
             const int hk = k - nq, h = g * hpg + hk / PC, p0 = (hk % PC) * 64;
             kb.load(KT::rsrc(states + ((((int64_t)b * nc + c) * H + h) * P + p0) * N + n0, N, min(64, P - p0)));
             const auto vrs = make_rsrc(vec + (((int64_t)b * T + t0) * H + h) * P,
                                        ((int64_t)(len - 1) * H * P + P) * ES);
+            const bool pin = p0 + hv * V < P;
+#pragma unroll
+            for (int i = 0; i < NPASS; ++i) {
+                const int r = r0 + hr + i * RPP;
+                rb[i] = bload16(vrs, (r < len && pin) ? (uint32_t)(((int64_t)r * H * P + p0 + hv * V) * ES) : kOffNone);
+            }
             const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int r = r0 + c_w + 16 * j + li;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int p = p0 + ks * 32 + 8 * lg;
-                    bload_frag(vrs, (r < len && p < P) ? (uint32_t)(((int64_t)r * H * P + p) * ES) : kOffNone, fr[ks][j]);
-                }
                 const int rr = r < len ? r : 0;
                 sc[j] = MODE == 0 ? __builtin_amdgcn_exp2f(cs[row + rr] * kLog2e)
                                   : delta[row + rr] * __builtin_amdgcn_exp2f((cs[row + Q - 1] - cs[row + rr]) * kLog2e);
@@ -621,14 +628,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
         const bool mpart = k < nq;
         if (mpart) ka.template store<false, false>(kt, nullptr, nullptr);
         else kb.template store<false, false>(kt, nullptr, nullptr);
-        F cur[2][2];
+#pragma unroll
+        for (int i = 0; i < NPASS; ++i) *reinterpret_cast<uint4 *>(bt + (hr + i * RPP) * PITCH + hv * V) = rb[i];
         float cs_[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            cs_[j] = sc[j];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) cur[ks][j] = fr[ks][j];
-        }
+        for (int j = 0; j < 2; ++j) cs_[j] = sc[j];
         if (k + 1 < steps) issue(k + 1);
         __syncthreads();
 #pragma unroll
@@ -637,7 +641,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
 #pragma unroll
             for (int i = 0; i < 2; ++i) fa[i] = KT::frag_at(kt, aoff[i], ks * 32);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fbv[j] = mpart ? cur[ks][j] : from_f32<F>(to_f32(cur[ks][j]) * cs_[j]);
+            for (int j = 0; j < 2; ++j) {
+                const F f = load_frag(bt + (c_w + 16 * j + li) * PITCH + ks * 32 + 8 * lg);
+                fbv[j] = mpart ? f : from_f32<F>(to_f32(f) * cs_[j]);
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
