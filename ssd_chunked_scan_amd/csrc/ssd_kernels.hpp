@@ -1196,6 +1196,61 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[k][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // Row-wise view of this wave's tile, used to turn y, the gate's z and the dot
+    // modes' v around in LDS (bf16): lane (oct, chunk) takes 16 bytes, p0 +
+    // 8 chunk .. + 7, of row 16 j + 8 half + rsel.  Rows sit in LDS with their 8
+    // chunks of 16 bytes at chunk ^ ((t >> 1) & 7), so the 8-byte accesses of 16
+    // rows in the accumulator layout spread over all banks; the 16-byte row
+    // accesses take 8 rows per instruction, ordered so that the two lane octets
+    // sharing an LDS pass (0-7 with 16-23, ...) touch rows of opposite parity,
+    // i.e. opposite bank halves.
+    auto yoff = [](int t, int ch) { return t * 64 + 8 * (ch ^ ((t >> 1) & 7)); };
+    const int oct = lane >> 3, chunk = lane & 7;
+    const int rsel = (oct & 4) + ((oct & 1) << 1) + ((oct >> 1) & 1);   // 0,2,1,3,4,6,5,7
+    const bool pin = p0 + 8 * chunk < P;
+
+    // Turn this wave's rows (row-wise view, rows[k][half]) around in the LDS
+    // region buf (the wave's own rows t of it) into the accumulator layout.
+    auto turn = [&](E *buf, const uint4 (&rows)[NSB][2], floatx4 (&out)[NSB][4]) {
+#pragma unroll
+        for (int k = 0; k < NSB; ++k)
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                *reinterpret_cast<uint4 *>(buf + yoff(16 * jb[k] + 8 * half + rsel, chunk)) = rows[k][half];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+            const int t = 16 * jb[k] + li;
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+                out[k][pb] = __builtin_convertvector(
+                    *reinterpret_cast<const bf16x4 *>(buf + yoff(t, 2 * pb + (lg >> 1)) + 4 * (lg & 1)), floatx4);
+        }
+        // every lane has read its values before the rows are written again
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // The dot modes' v in the row-wise view (bf16): token t's vec row, at the
+    // mirrored position for DOT = 2
+    uint4 vrow[NSB][2];
+    auto load_vrows = [&]() {
+#pragma unroll
+        for (int k = 0; k < NSB; ++k)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int t = 16 * jb[k] + 8 * half + rsel, tv = DOT == 2 ? len - 1 - t : t;
+                vrow[k][half] = live[k] && t < len && pin
+                                    ? *reinterpret_cast<const uint4 *>(
+                                          vec + (((int64_t)b * T + t0 + tv) * H + h) * P + p0 + 8 * chunk)
+                                    : uint4{0, 0, 0, 0};
+            }
+    };
+
+    if constexpr (P1ONLY && sizeof(E) == 2) load_vrows();
+
     // ---- step 4 part: Hin C^T over n (columns N..NT-1 are zero in both) ----
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -1216,7 +1271,9 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 
     // v . acc over this tile's 64 p for each token of the wave's live sub-blocks,
     // each acc scaled by a per-token factor; lane (li, lg) holds p = 16 pb + 4 lg + q
-    auto dot_out = [&](float *dst, auto scale) {
+    // v either loaded here (vv = nullptr: four p of token t per lane) or given
+    // in the accumulator layout (vv)
+    auto dot_out = [&](float *dst, auto scale, const floatx4 (*vv)[4] = nullptr) {
         const int64_t rowb = ((((int64_t)tp * gridDim.y + b) * H + h) * nc + c) * Q;
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
@@ -1229,7 +1286,12 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
             for (int pb = 0; pb < 4; ++pb) {
                 const int p = p0 + 16 * pb + 4 * lg;
                 float v[4] = {0.f, 0.f, 0.f, 0.f};
-                if (t < len && p < P) load4_f32(vec + (((int64_t)b * T + t0 + tv) * H + h) * P + p, v);
+                if (vv) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = vv[k][pb][q];
+                } else if (t < len && p < P) {
+                    load4_f32(vec + (((int64_t)b * T + t0 + tv) * H + h) * P + p, v);
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) sum += v[q] * acc[k][pb][q];
             }
@@ -1246,7 +1308,16 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
             const bool mo = !PACKED || sq[tj] == seq_prev;
             return mo ? exp2_(csb[tj]) * exp2_(csb[min(t, Q - 1)] - csb[tj]) : 0.f;
         };
-        dot_out(dot1, sc1);
+        if constexpr (P1ONLY && sizeof(E) == 2) {
+            // v (loaded before step 4) turns around in the entering-state region
+            // once every wave is done with it
+            floatx4 vv[NSB][4];
+            __syncthreads();
+            turn(hs, vrow, vv);
+            dot_out(dot1, sc1, vv);
+        } else {
+            dot_out(dot1, sc1);
+        }
         if constexpr (P1ONLY) return;
     }
 
@@ -1273,19 +1344,6 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[k][pb][q] = mo ? acc[k][pb][q] * e0 : 0.f;
     }
-
-    // Row-wise view of this wave's tile, used to turn y (and the gate's z) around
-    // in the entering-state region (bf16): lane (oct, chunk) takes 16 bytes, p0 +
-    // 8 chunk .. + 7, of row 16 j + 8 half + rsel.  Rows sit in LDS with their 8
-    // chunks of 16 bytes at chunk ^ ((t >> 1) & 7), so the 8-byte accesses of 16
-    // rows in the accumulator layout spread over all banks; the 16-byte row
-    // accesses take 8 rows per instruction, ordered so that the two lane octets
-    // sharing an LDS pass (0-7 with 16-23, ...) touch rows of opposite parity,
-    // i.e. opposite bank halves.
-    auto yoff = [](int t, int ch) { return t * 64 + 8 * (ch ^ ((t >> 1) & 7)); };
-    const int oct = lane >> 3, chunk = lane & 7;
-    const int rsel = (oct & 4) + ((oct & 1) << 1) + ((oct >> 1) & 1);   // 0,2,1,3,4,6,5,7
-    const bool pin = p0 + 8 * chunk < P;
 
     // The gate's z (GATE), loaded before the diagonal step so that the loads
     // overlap its MFMA work.  bf16: in the row-wise view above (whole 128-byte
@@ -1350,6 +1408,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
         for (int k = 0; k < NSB; ++k) load_z(k);
     }
+    if constexpr (DOT == 2 && sizeof(E) == 2) load_vrows();
 
     // ---- u_t scale, then the diagonal K step with per-element decays and D ----
     const float Dh = D ? D[h] : 0.f;
@@ -1388,34 +1447,28 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
         for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], XT::frag_at(xt, xoff[pb], ks * 32), wfr);
     }
 
-    if constexpr (DOT == 2) dot_out(dot2, [](int, int) { return 1.f; });
+    if constexpr (DOT == 2) {
+        if constexpr (sizeof(E) == 2) {
+            // the entering-state region is free since the barrier after step 4
+            floatx4 vv[NSB][4];
+            turn(hs, vrow, vv);
+            dot_out(dot2, [](int, int) { return 1.f; }, vv);
+        } else {
+            dot_out(dot2, [](int, int) { return 1.f; });
+        }
+    }
 
     if constexpr (GATE) {
         // y *= SiLU(z) in fp32, before the one rounding of y
         if constexpr (ZROW) {
+            floatx4 zf[NSB][4];
+            turn(hs, zrow, zf);
 #pragma unroll
             for (int k = 0; k < NSB; ++k)
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
-                    *reinterpret_cast<uint4 *>(hs + yoff(16 * jb[k] + 8 * half + rsel, chunk)) = zrow[k][half];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-            for (int k = 0; k < NSB; ++k) {
-                const int t = 16 * jb[k] + li;
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) {
-                    const floatx4 zf = __builtin_convertvector(
-                        *reinterpret_cast<const bf16x4 *>(hs + yoff(t, 2 * pb + (lg >> 1)) + 4 * (lg & 1)), floatx4);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[k][pb][q] *= silu(zf[q]);
-                }
-            }
-            // every lane has read its z before the same rows take y below
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    for (int q = 0; q < 4; ++q) acc[k][pb][q] *= silu(zf[k][pb][q]);
         } else {
 #pragma unroll
             for (int k = 0; k < NSB; ++k) {
