@@ -465,9 +465,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
             }
             // Rows t (value m = 4 i + r) are summed over the 16 lanes li of a row
             // group, columns s (value j) over the 4 groups lg, each by halving
-            // exchanges: at every xor step a lane keeps half of its values and
-            // adds its partner's copy of that half.  In the end lane li holds row
-            // value m = (li >> 1) & 7 and lane group lg column value j = lg >> 1.
+            // exchanges: at every step a lane keeps half of its values and adds
+            // its partner's copy of that half.  The row partners are li ^ 8, li ^ 7,
+            // li ^ 2 and li ^ 1 (DPP row rotate by 8, half-row mirror, and quad
+            // permutes: register moves inside a 16-lane row, no LDS); each step's
+            // partner differs in the bit that chose the kept half and agrees in the
+            // bits chosen before, so the four steps cover all 16 lanes once.  In
+            // the end lane li holds row value m = (li >> 1) & 7 and lane group lg
+            // column value j = lg >> 1.
             float v8[8];
 #pragma unroll
             for (int m = 0; m < 8; ++m) v8[m] = rs[m >> 2][m & 3];
@@ -476,19 +481,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
                 const bool up = li & 8;
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    v4[m] = (up ? v8[m + 4] : v8[m]) + __shfl_xor(up ? v8[m] : v8[m + 4], 8);
+                    v4[m] = (up ? v8[m + 4] : v8[m]) + dpp_mov<kDppRowRor8>(up ? v8[m] : v8[m + 4]);
             }
             {
                 const bool up = li & 4;
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    v2[m] = (up ? v4[m + 2] : v4[m]) + __shfl_xor(up ? v4[m] : v4[m + 2], 4);
+                    v2[m] = (up ? v4[m + 2] : v4[m]) + dpp_mov<kDppRowHalfMirror>(up ? v4[m] : v4[m + 2]);
             }
             {
                 const bool up = li & 2;
-                v1 = (up ? v2[1] : v2[0]) + __shfl_xor(up ? v2[0] : v2[1], 2);
+                v1 = (up ? v2[1] : v2[0]) + dpp_mov<kDppQuadXor2>(up ? v2[0] : v2[1]);
             }
-            v1 += __shfl_xor(v1, 1);
+            v1 += dpp_mov<kDppQuadXor1>(v1);
             {
                 const bool up = lg & 2;
                 c1 = (up ? cl[1] : cl[0]) + __shfl_xor(up ? cl[0] : cl[1], 32);

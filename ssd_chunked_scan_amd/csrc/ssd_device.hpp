@@ -36,6 +36,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 // 2^x for arguments already scaled by log2(e) (v_exp_f32 alone).
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+// A float from another lane of the same 16-lane row (DPP move; every source
+// lane is inside the row).  Controls: rotate the row by 8 (lane i <- i ^ 8),
+// mirror each half row (i <- i ^ 7 within the half), and the quad permutes
+// i <- i ^ 2 and i <- i ^ 1.
+constexpr int kDppRowRor8 = 0x128, kDppRowHalfMirror = 0x141, kDppQuadXor2 = 0x4E, kDppQuadXor1 = 0xB1;
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 // SiLU(v) = v / (1 + e^-v) with the hardware exponential and reciprocal
 // (v_exp_f32, v_rcp_f32: about 1 ulp each) instead of a correctly rounded
 // divide.  v -> -inf gives -0 (the reciprocal of inf is 0).
