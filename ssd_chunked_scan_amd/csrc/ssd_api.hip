@@ -410,7 +410,7 @@ ssd_status run_conv(const ssd_conv_args *a, hipStream_t st)
 // backward
 // ---------------------------------------------------------------------------
 struct BwdWorkspace {
-    size_t delta, cs, cb, states, gstates, cbr, dyr, br, cr, csr, dlr, ypr, yo, zo, xyp, rpart, cpart, bnd, dyx,
+    size_t delta, cs, cb, states, gstates, cbr, br, cr, csr, dlr, ypr, yo, zo, xyp, rpart, cpart, bnd, dyx,
         mrow, mcol, dA_part, dD_part, total;
 };
 
@@ -433,7 +433,6 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     w.states = take(sts);
     w.gstates = take(sts);
     w.cbr = take(cbs);
-    w.dyr = take(xs);
     w.br = take(bcs);
     w.cr = take(bcs);
     w.csr = take(dcs);
@@ -495,7 +494,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     float *delta = F32(w.delta), *cs = F32(w.cs), *csr = F32(w.csr), *dlr = F32(w.dlr);
     float *yo = F32(w.yo), *zo = F32(w.zo), *xyp = F32(w.xyp), *rpart = F32(w.rpart), *cpart = F32(w.cpart);
     float *bnd = F32(w.bnd), *dyx = F32(w.dyx), *dA_part = F32(w.dA_part), *dD_part = F32(w.dD_part);
-    E *cb = EP(w.cb), *states = EP(w.states), *gstates = EP(w.gstates), *cbr = EP(w.cbr), *dyr = EP(w.dyr);
+    E *cb = EP(w.cb), *states = EP(w.states), *gstates = EP(w.gstates), *cbr = EP(w.cbr);
     E *br = EP(w.br), *cr = EP(w.cr), *ypr = EP(w.ypr), *mrow = EP(w.mrow), *mcol = EP(w.mcol);
     ssd_status r;
     // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
@@ -504,11 +503,10 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     if ((r = run_cb<E>(s, &f, cb, st)) != SSD_OK) return r;
     if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st)) != SSD_OK) return r;
     if ((r = run_passing<E>(s, &f, cs, states, nullptr, st)) != SSD_OK) return r;
-    // 2. every chunk's tokens in reversed order: dy, B, C, and the reversed cs / delta
+    // 2. every chunk's tokens in reversed order: B, C, and the reversed cs / delta
+    //    (dy is read reversed by the kernels themselves)
     constexpr int V = kVec16<E>;
-    const int64_t vx = s.b * s.T * s.H * s.P / V, vbc = s.b * s.T * s.G * s.N / V;
-    hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vx, 256)), dim3(256), 0, st, (const E *)g->dy, dyr,
-                       (int)s.T, (int)s.Q, s.H * s.P, vx);
+    const int64_t vbc = s.b * s.T * s.G * s.N / V;
     hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vbc, 256)), dim3(256), 0, st, (const E *)a->B, br,
                        (int)s.T, (int)s.Q, s.G * s.N, vbc);
     hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vbc, 256)), dim3(256), 0, st, (const E *)a->C, cr,
@@ -519,7 +517,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     if ((r = launched()) != SSD_OK) return r;
     // 3. reversed-order problem: x <- dy, B <- C, C <- B, unit step size, no skip term
     ssd_fwd_args rv = *a;
-    rv.x = dyr;
+    rv.x = g->dy;
     rv.B = cr;
     rv.C = br;
     rv.D = nullptr;

@@ -396,6 +396,17 @@ struct KTile<bf16, KR, COLS, TH> {
             voff[i] = (v < NV && c * 8 < ncols) ? (uint32_t)(r * ld * 2 + c * 16) : kOffNone;
         }
     }
+    // The first `len` rows in reversed order (tile row r = source row len - 1 - r),
+    // rows from len on zero.
+    __device__ __forceinline__ void init_rev(int64_t ld, int ncols, int len)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * TH;
+            const int r = v / VPR, c = v % VPR;
+            voff[i] = (v < NV && c * 8 < ncols && r < len) ? (uint32_t)((len - 1 - r) * ld * 2 + c * 16) : kOffNone;
+        }
+    }
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs)
     {
@@ -471,14 +482,31 @@ struct KTile<float, KR, COLS, TH> {
     }
 
     int64_t ldb;
+    bool rev;
+    int rtop[PER];   // reversed tiles: the source row of each block's first tile row
     __device__ __forceinline__ void init(int64_t ld, int ncols)
     {
         ldb = ld * 4;
+        rev = false;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int blk = threadIdx.x + i * TH;
             const int cbk = blk % CBK, sb = blk / CBK;
             voff[i] = (blk < NB && cbk * 4 < ncols) ? (uint32_t)(sb * 4 * ldb + cbk * 16) : kOffNone;
+        }
+    }
+    // The first `len` rows in reversed order (tile row r = source row len - 1 - r),
+    // rows from len on zero.
+    __device__ __forceinline__ void init_rev(int64_t ld, int ncols, int len)
+    {
+        ldb = ld * 4;
+        rev = true;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int blk = threadIdx.x + i * TH;
+            const int cbk = blk % CBK, sb = blk / CBK;
+            rtop[i] = len - 1 - sb * 4;
+            voff[i] = (blk < NB && cbk * 4 < ncols) ? (uint32_t)(cbk * 16) : kOffNone;
         }
     }
 
@@ -487,8 +515,14 @@ struct KTile<float, KR, COLS, TH> {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                raw[i][r] = bload16(rs, voff[i] == kOffNone ? kOffNone : voff[i] + (uint32_t)(r * ldb));
+            for (int r = 0; r < 4; ++r) {
+                if (rev) {
+                    const int gr = rtop[i] - r;
+                    raw[i][r] = bload16(rs, voff[i] == kOffNone || gr < 0 ? kOffNone : voff[i] + (uint32_t)(gr * ldb));
+                } else {
+                    raw[i][r] = bload16(rs, voff[i] == kOffNone ? kOffNone : voff[i] + (uint32_t)(r * ldb));
+                }
+            }
     }
 
     template <bool SCALE, bool SEL>
@@ -681,10 +715,11 @@ __device__ __forceinline__ void seg_end_mark(const int32_t *__restrict__ seq_idx
 // owns n rows w*NT/4 .. +NT/4 of D[n][p] (A = B^T, B = (w x)^T):
 //   acc[i][j][r]  <->  n = w*NT/4 + i*16 + 4*(lane/16) + r,  p = j*16 + lane%16.
 // GRAD = true is the same product for the backward pass's per-chunk gradient
-// states U_c = sum_t exp(cs_t) dy_t C_t^T, fed with the chunk's tokens in
-// reversed order (x = dy reversed, B^T = C^T reversed): the weight of reversed
-// position s is exp(cs[len-1-s]) from the given cs, no cumsum step runs, and
-// delta and cs are only read.
+// states U_c = sum_t exp(cs_t) dy_t C_t^T, run on the chunk's tokens in reversed
+// order: x = dy is passed in its own order and its rows are read reversed here,
+// B^T = C^T comes reversed from the caller; the weight of reversed position s
+// is exp(cs[len-1-s]) from the given cs, no cumsum step runs, and delta and cs
+// are only read.
 template <typename E, int Q, int NT, bool PACKED, bool GRAD = false>
 __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const E *__restrict__ x, const E *__restrict__ cbuf, const E *__restrict__ dt, const float *__restrict__ A,
@@ -721,7 +756,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     if (!GRAD && wave == 0) chunk_cumsum_load<E>(dt, seq_idx, b, c, h, T, H, Q, dv, sv);
     const int64_t ldx = (int64_t)H * P;
     XT xs;
-    xs.init(ldx, P - p0);
+    if constexpr (GRAD) xs.init_rev(ldx, P - p0, len);   // the chunk's tokens in reversed order
+    else xs.init(ldx, P - p0);
     xs.load(XT::rsrc(x + (((int64_t)b * T + t0) * H + h) * P + p0, ldx, len));
 
     // B^T fragments of this chunk and group; K steps past the sequence end are skipped
@@ -1045,7 +1081,9 @@ template <int Q> constexpr int scan_threads() { return Q * 2; }
 // fragment offset is an immediate); columns N..NT-1 are masked.
 // Dot modes (used by the backward pass; DOT = 0 is the forward): with v = `vec`
 // at each token's position (DOT = 1) or at the mirrored position len-1-t of a
-// chunk whose tokens were reversed (DOT = 2), the kernel also writes, per token,
+// chunk whose tokens were reversed (DOT = 2: x is passed in its own order and its
+// rows are read reversed here; every other input comes reversed from the
+// caller), the kernel also writes, per token,
 // fp32 dot products over this workgroup's 64 p (one [b,H,nc,Q] slice per p tile,
 // indexed by the token's original position):
 //   dot1 = v . (the entering-state term alone),  dot2 (DOT = 2) = v . (the whole
@@ -1118,7 +1156,8 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
     for (int i = 0; i < HG; ++i) hraw[i] = bload16(hrs, hoff(i));
     XT xs;
-    xs.init((int64_t)H * P, P - p0);
+    if constexpr (DOT == 2) xs.init_rev((int64_t)H * P, P - p0, len);   // the chunk's tokens in reversed order
+    else xs.init((int64_t)H * P, P - p0);
     if constexpr (!P1ONLY) xs.load(XT::rsrc(x + (((int64_t)b * T + t0) * H + h) * P + p0, (int64_t)H * P, len));
     float c_i = 0.f, d_i = 0.f;
     int s_i = 0;
