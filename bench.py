@@ -192,9 +192,11 @@ def run_cpu_baseline(inp, budget_s=20.0):
 
 
 def run_backward(dev, inp, g, reps, warmup):
-    """Time ssd_bwd (every input gradient; the chunk intermediates recomputed
-    inside) on the workload's inputs with a seeded dy and dfinal, between HIP
-    events on the launch stream; outputs and workspace preallocated."""
+    """Time ssd_bwd (every input gradient) on the workload's inputs with a seeded
+    dy and dfinal, between HIP events on the launch stream; outputs and workspaces
+    preallocated.  Two ways: reading the forward's chunk intermediates from the
+    workspace of the forward that produced y (a training step's order), and
+    recomputing them inside."""
     import numpy as np
     import torch
     from ssd_chunked_scan_amd import ssd
@@ -202,36 +204,28 @@ def run_backward(dev, inp, g, reps, warmup):
     nseq = inp.nseq if inp.seq_idx is not None else None
     if nseq is not None:
         return None   # the backward takes no packed streams
-    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states)
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states)
+    fws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states, workspace=fws)
     rng = np.random.default_rng(7)
     dy = torch.from_numpy(rng.standard_normal(tuple(inp.x.shape)).astype(np.float32)).to(dev).to(g.x.dtype)
     b, T, H, P = inp.x.shape
     N = inp.B.shape[3]
     dfin = torch.from_numpy(rng.standard_normal((b, H, P, N)).astype(np.float32)).to(dev)
-    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states)
     ws = torch.empty(ssd.bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    grads = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, D=g.D, initial_states=g.initial_states,
-                    dfinal_states=dfin, workspace=ws)
+    kw = dict(D=g.D, initial_states=g.initial_states, dfinal_states=dfin, workspace=ws)
+    grads = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, **kw)
     stream = torch.cuda.current_stream(dev)
-
-    def one():
-        ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, D=g.D, initial_states=g.initial_states,
-                dfinal_states=dfin, grads=grads, workspace=ws)
-
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b_ in ev:
-        a.record(stream)
-        one()
-        b_.record(stream)
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b_) for a, b_ in ev]
-    avg = sum(ms) / len(ms)
-    return {"ms": round(avg, 5), "step_ms": percentiles(ms), "tokens_per_s": round(inp.real_tokens / (avg / 1e3), 1),
+    saved = _event_ms(lambda: ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, grads=grads, fwd_workspace=fws,
+                                      **kw), reps, warmup, stream)
+    recomp = _event_ms(lambda: ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, grads=grads, **kw),
+                       reps, warmup, stream)
+    avg, avg_r = sum(saved) / len(saved), sum(recomp) / len(recomp)
+    return {"ms": round(avg, 5), "step_ms": percentiles(saved), "tokens_per_s": round(inp.real_tokens / (avg / 1e3), 1),
+            "ms_recompute": round(avg_r, 5), "step_ms_recompute": percentiles(recomp),
             "workspace_bytes": int(ws.numel()),
-            "note": "all input gradients; the forward's chunk intermediates are recomputed inside"}
+            "note": "all input gradients; ms reads the forward's chunk intermediates from that forward's "
+                    "workspace, ms_recompute recomputes them inside"}
 
 
 def run_decode(dev, reps, warmup):

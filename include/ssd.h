@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
     SSD_OK = 0,
@@ -220,8 +220,13 @@ ssd_status ssd_step(const ssd_step_args *args, void *stream);
  * `args` describes the forward exactly as it was run (shape, dtype, x, dt, A, B,
  * C, D, initial_states; seq_idx NULL) and args->y must hold its output y (an
  * input here).  Its final_states, workspace and workspace_bytes fields are
- * ignored: the chunk intermediates are recomputed in the backward's own
- * workspace.
+ * ignored.  The forward's chunk intermediates (Delta, cs, CB and the states
+ * entering each chunk) are recomputed in the backward's own workspace, unless
+ * fwd_workspace passes the workspace of the ssd_fwd call that produced y: that
+ * call must have been on exactly these inputs, and the workspace left untouched
+ * since.  The backward then reads them from there (it never writes to it), and
+ * its own workspace's slots for them go unused.  Nothing checks that the
+ * workspace really holds them.
  */
 typedef struct {
     const void *dy;                /* [b,T,H,P] dtype */
@@ -235,6 +240,8 @@ typedef struct {
     float *dinitial_states;        /* [b,H,P,N] fp32, out, or NULL */
     void *workspace;               /* device scratch, >= ssd_bwd_workspace_size */
     size_t workspace_bytes;
+    const void *fwd_workspace;     /* the forward's workspace (see above), or NULL to recompute */
+    size_t fwd_workspace_bytes;    /* >= ssd_fwd_workspace_size when fwd_workspace is given */
 } ssd_bwd_args;
 
 /* Workspace bytes ssd_bwd needs for the forward problem `args` (shape and dtype

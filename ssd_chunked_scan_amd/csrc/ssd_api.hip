@@ -497,12 +497,22 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     E *cb = EP(w.cb), *states = EP(w.states), *gstates = EP(w.gstates), *cbr = EP(w.cbr);
     E *br = EP(w.br), *cr = EP(w.cr), *ypr = EP(w.ypr), *mrow = EP(w.mrow), *mcol = EP(w.mcol);
     ssd_status r;
-    // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
     ssd_fwd_args f = *a;
     f.final_states = nullptr;
-    if ((r = run_cb<E>(s, &f, cb, st)) != SSD_OK) return r;
-    if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st)) != SSD_OK) return r;
-    if ((r = run_passing<E>(s, &f, cs, states, nullptr, st)) != SSD_OK) return r;
+    if (g->fwd_workspace) {
+        // 1. the forward's chunk intermediates, as its own call left them (read only)
+        const Workspace fw = workspace_layout(s);
+        char *fws = const_cast<char *>(static_cast<const char *>(g->fwd_workspace));
+        delta = reinterpret_cast<float *>(fws + fw.delta);
+        cs = reinterpret_cast<float *>(fws + fw.cs);
+        cb = reinterpret_cast<E *>(fws + fw.cb);
+        states = reinterpret_cast<E *>(fws + fw.states);
+    } else {
+        // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
+        if ((r = run_cb<E>(s, &f, cb, st)) != SSD_OK) return r;
+        if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st)) != SSD_OK) return r;
+        if ((r = run_passing<E>(s, &f, cs, states, nullptr, st)) != SSD_OK) return r;
+    }
     // 2. every chunk's tokens in reversed order: B, C, and the reversed cs / delta
     //    (dy is read reversed by the kernels themselves)
     constexpr int V = kVec16<E>;
@@ -792,19 +802,21 @@ ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream
     if (!g->dA) return SSD_ERR_NULL_POINTER;
     if (!empty && (!args->y || !g->dy || !g->dx || !g->ddt || !g->dB || !g->dC)) return SSD_ERR_NULL_POINTER;
     const void *ptrs[] = {args->y, g->dy, g->dfinal_states, g->dx, g->ddt, g->dA, g->dB, g->dC, g->dD,
-                          g->dinitial_states, g->workspace};
+                          g->dinitial_states, g->workspace, g->fwd_workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
     const Sizes z = tensor_sizes(s);
     const size_t st = (size_t)(s.b * s.H * s.P * s.N) * 4;
     const BwdWorkspace w = bwd_workspace_layout(s);
+    const size_t fws = workspace_layout(s).total;
     if (!empty) {
         if (!g->workspace) return SSD_ERR_NULL_POINTER;
         if (g->workspace_bytes < w.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+        if (g->fwd_workspace && g->fwd_workspace_bytes < fws) return SSD_ERR_WORKSPACE_TOO_SMALL;
     }
     const Range ins[] = {{args->x, z.x}, {args->dt, z.dt}, {args->A, z.A}, {args->B, z.bc}, {args->C, z.bc},
                          {args->D, z.D}, {args->initial_states, z.init}, {args->y, z.y}, {g->dy, z.x},
-                         {g->dfinal_states, st}};
+                         {g->dfinal_states, st}, {g->fwd_workspace, fws}};
     const Range outs[] = {{g->dx, z.x}, {g->ddt, z.dt}, {g->dA, z.A}, {g->dB, z.bc}, {g->dC, z.bc},
                           {g->dD, z.D}, {g->dinitial_states, st}, {empty ? nullptr : g->workspace, w.total}};
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {

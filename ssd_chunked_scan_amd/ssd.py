@@ -64,6 +64,7 @@ class BwdArgs(ctypes.Structure):
         ("ddt", ctypes.c_void_p), ("dA", ctypes.c_void_p), ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p),
         ("dD", ctypes.c_void_p), ("dinitial_states", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("fwd_workspace", ctypes.c_void_p), ("fwd_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -429,11 +430,14 @@ def bwd_workspace_bytes(p: Problem) -> int:
 
 
 def bwd(x, dt, A, B, C, chunk, y, dy, D=None, initial_states=None, dfinal_states=None, dt_softplus=True,
-        grads=None, workspace=None, stream=None, want_dinit=True):
+        grads=None, workspace=None, stream=None, want_dinit=True, fwd_workspace=None):
     """Gradients of sum(y * dy) + sum(final_states * dfinal_states) (see ``ssd_bwd``
     in ``include/ssd.h``).  ``y`` is the forward output.  Returns a dict with dx,
     ddt, dA, dB, dC, dD (None without D) and dinitial_states (None unless
-    ``want_dinit``); ``grads`` may pass those tensors pre-allocated."""
+    ``want_dinit``); ``grads`` may pass those tensors pre-allocated.
+    ``fwd_workspace``: the workspace of the ``fwd`` call that produced ``y`` (on
+    these same inputs, untouched since), whose chunk intermediates are then read
+    instead of recomputed."""
     p = Problem(x, dt, A, B, C, chunk, D, initial_states, None, None, dt_softplus)
     _check(y, "y", x.dtype, x.shape, p.device)
     _check(dy, "dy", x.dtype, x.shape, p.device)
@@ -457,11 +461,13 @@ def bwd(x, dt, A, B, C, chunk, y, dy, D=None, initial_states=None, dfinal_states
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=p.device)
     _check(workspace, "workspace", torch.uint8, None, p.device)
+    _check(fwd_workspace, "fwd_workspace", torch.uint8, None, p.device)
     p.args.y = _ptr(y)
     ga = BwdArgs(dy=_ptr(dy), dfinal_states=_ptr(dfinal_states), dx=_ptr(g["dx"]), ddt=_ptr(g["ddt"]),
                  dA=_ptr(g["dA"]), dB=_ptr(g["dB"]), dC=_ptr(g["dC"]), dD=_ptr(g["dD"]),
                  dinitial_states=_ptr(g["dinitial_states"]), workspace=_ptr(workspace),
-                 workspace_bytes=workspace.numel())
+                 workspace_bytes=workspace.numel(), fwd_workspace=_ptr(fwd_workspace),
+                 fwd_workspace_bytes=0 if fwd_workspace is None else fwd_workspace.numel())
     st = stream if stream is not None else torch.cuda.current_stream(p.device).cuda_stream
     rc = load_library().ssd_bwd(ctypes.byref(p.args), ctypes.byref(ga), ctypes.c_void_p(st))
     if rc != 0:

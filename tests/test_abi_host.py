@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(ssd.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ssd_abi_version() == 1
+    assert lib.ssd_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -164,6 +164,8 @@ def _bwd_args(**kw):
         setattr(g, name, kw.get(name, addr))
         addr += 0x10000000
     g.workspace_bytes = kw.get("workspace_bytes", 1 << 40)
+    g.fwd_workspace = kw.get("fwd_workspace", 0)
+    g.fwd_workspace_bytes = kw.get("fwd_workspace_bytes", 1 << 40)
     return g
 
 
@@ -178,6 +180,10 @@ def _bwd_args(**kw):
     (dict(), dict(dx=0x10000000), ALIAS),                       # dx == x
     (dict(), dict(dC=0xa0000000 + 256), ALIAS),                 # dC inside dy
     (dict(), dict(dB=0xa0000000 + 0x20000000), ALIAS),          # dB == dx
+    (dict(), dict(fwd_workspace=0x1a0000008), MISAL),
+    (dict(), dict(fwd_workspace=0x1a0000000, fwd_workspace_bytes=256), WS),
+    (dict(), dict(fwd_workspace=0xa0000000 + 0x20000000), ALIAS),   # the forward's workspace == dx
+    (dict(), dict(fwd_workspace=0xa0000000 + 0x90000000), ALIAS),   # ... == the backward's workspace
 ])
 def test_bwd_rejects_invalid_arguments(lib, fkw, gkw, code):
     a = _args(**fkw)

@@ -180,3 +180,27 @@ def test_bwd_reads_nothing_past_the_last_row(dtype, T):
     assert worst(f64(gr["dB"]), ref.dB, [0, 2]) <= tol
     assert worst(f64(gr["dC"]), ref.dC, [0, 2]) <= tol
     assert worst(f64(gr["dinitial_states"]), ref.dinit, [0, 1]) <= tol
+
+
+@pytest.mark.parametrize("Q", [64, 128, 256])
+def test_bwd_with_the_forwards_workspace(Q):
+    """Reading the forward's chunk intermediates from its workspace gives the very
+    gradients of recomputing them (bit for bit), and leaves that workspace as it
+    was."""
+    inp = wl.make_inputs(2, 2 * Q + 37, 4, 64, 64, 2, Q, "bf16", 200 + Q, init_std=0.3)
+    g = inp.to("cuda:0")
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, Q, g.D, g.initial_states)
+    fws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device="cuda:0")
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, Q, D=g.D, initial_states=g.initial_states, workspace=fws)
+    torch.cuda.synchronize()
+    keep = fws.clone()
+    dy = torch.randn(tuple(inp.x.shape), generator=torch.Generator().manual_seed(Q)).to(torch.bfloat16).cuda()
+    dfin = torch.randn((2, 4, 64, 64), generator=torch.Generator().manual_seed(Q + 1)).cuda()
+    kw = dict(D=g.D, initial_states=g.initial_states, dfinal_states=dfin)
+    a = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, Q, y, dy, **kw)
+    b = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, Q, y, dy, fwd_workspace=fws, **kw)
+    torch.cuda.synchronize()
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+    assert torch.equal(fws, keep)
