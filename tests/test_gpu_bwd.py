@@ -204,3 +204,32 @@ def test_bwd_with_the_forwards_workspace(Q):
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), k
     assert torch.equal(fws, keep)
+
+
+def test_bwd_long_workload_full_size():
+    """The benchmark's backward configuration: the long workload (16384 tokens,
+    32 heads of 64, N = 256, chunk 256, bf16) at full size, the forward's
+    intermediates read from its workspace as the benchmark times it, every
+    gradient against the oracle."""
+    inp = wl.workload(3)
+    _log(f"[bwd] {inp.name} full size")
+    g = inp.to("cuda:0")
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states)
+    fws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device="cuda:0")
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states, workspace=fws)
+    rng = np.random.default_rng(7)
+    b, T, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    dy = torch.from_numpy(rng.standard_normal((b, T, H, P)).astype(np.float32)).to(torch.bfloat16)
+    dfin = torch.from_numpy(rng.standard_normal((b, H, P, N)).astype(np.float32))
+    gr = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy.to("cuda:0"), D=g.D, initial_states=g.initial_states,
+                 dfinal_states=dfin.to("cuda:0"), fwd_workspace=fws)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp.x, inp.dt, inp.A, inp.B, inp.C, dy, inp.D, inp.initial_states, dfin)
+    errs = {"dx": worst(f64(gr["dx"]), ref.dx, [0, 2]), "ddt": worst(f64(gr["ddt"]), ref.ddt, [0, 2]),
+            "dB": worst(f64(gr["dB"]), ref.dB, [0, 2]), "dC": worst(f64(gr["dC"]), ref.dC, [0, 2]),
+            "dinit": worst(f64(gr["dinitial_states"]), ref.dinit, [0, 1]), "dA": rel(f64(gr["dA"]), ref.dA),
+            "dD": rel(f64(gr["dD"]), ref.dD)}
+    _log("    " + "  ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f"  (tol {TOL['bf16']:.0e})")
+    for k, v in errs.items():
+        assert v <= TOL["bf16"], (k, v)
