@@ -443,7 +443,7 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     w.xyp = take(ntp * dcs);
     w.rpart = take(qt * dcs);
     w.cpart = take(qt * dcs);
-    w.bnd = take((size_t)(s.b * s.H * s.nc) * 4);
+    w.bnd = take((size_t)(s.b * s.H * s.nc) * (size_t)(s.P * s.N / 256) * 4);   // per (b, h, c): PN / 256 partials
     w.dyx = take(dcs);
     w.mrow = take(ms);
     w.mcol = take(ms);
@@ -473,14 +473,14 @@ ssd_status run_state_grad(const Shape &s, const ssd_fwd_args *ar, const float *c
 
 template <typename E>
 ssd_status run_passing_rev(const Shape &s, const float *cs, E *gstates, const float *dfinal, float *dinit,
-                           hipStream_t st)
+                           const E *hin, float *bnd_part, hipStream_t st)
 {
     const int64_t PN = s.P * s.N;
-    constexpr int VE = 4;
+    constexpr int VE = 4;   // so PN / (64 VE) = PN / 256 boundary partials per (b, h, c)
     const int64_t vecs = s.b * s.H * PN / VE;
     hipLaunchKernelGGL((k_state_passing<E, VE, true>), dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, gstates,
                        cs, dfinal, dinit, (const int32_t *)nullptr, (int)s.T, (int)s.H, PN, (int)s.nc, (int)s.Q,
-                       vecs);
+                       vecs, hin, bnd_part);
     return launched();
 }
 
@@ -537,7 +537,9 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     if ((r = run_cb<E>(s, &rv, cbr, st)) != SSD_OK) return r;
     // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
     if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st)) != SSD_OK) return r;
-    if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, st)) != SSD_OK) return r;
+    //    (with the boundary terms e^{cs_last} <G_c, Hin_c> of dl, as partial sums)
+    if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, states, bnd, st)) != SSD_OK)
+        return r;
     // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y'
     if ((r = run_scan_dot<E, 2, false>(s, &rv, dlr, csr, cbr, gstates, (const E *)a->x, zo, xyp, st)) != SSD_OK)
         return r;
@@ -562,7 +564,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         else r = tok(std::integral_constant<int, 64>{});
         if (r != SSD_OK) return r;
     }
-    // 8. M (summed over the group's heads) with the row / column sums of S; the boundary terms
+    // 8. M (summed over the group's heads) with the row / column sums of S
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     const int nnt = (int)((s.N + 63) / 64);
     if ((r = with_q(s.Q, [&](auto q) {
@@ -575,13 +577,12 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
              });
          })) != SSD_OK)
         return r;
-    hipLaunchKernelGGL(k_bwd_bnd<E>, dim3((unsigned)(s.b * s.nc * s.H)), dim3(kThreads), 0, st, (const E *)gstates,
-                       (const E *)states, cs, bnd, (int)s.H, (int)s.nc, (int)s.Q, s.P * s.N);
     // 9. dl, ddt, dA, dD
     const int64_t dlrows = s.b * s.H * s.nc;
     hipLaunchKernelGGL(k_bwd_dl<E>, dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart, yo, zo,
                        xyp, bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T,
-                       (int)s.H, (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), dlrows, (int)a->dt_softplus);
+                       (int)s.H, (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), dlrows, (int)a->dt_softplus,
+                       s.P * s.N / 256);
     hipLaunchKernelGGL(k_bwd_sum_heads, dim3((unsigned)s.H), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
                        (int)s.b, (int)s.H, (int)s.nc);
     if ((r = launched()) != SSD_OK) return r;

@@ -123,35 +123,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_token(
     if (sl == 0 && h < H) dyx[srow] = sdx;
 }
 
-// e^{cs_last(c)} <G_c, Hin_c> for every (b, c, h): one workgroup each.
-template <typename E>
-__global__ __launch_bounds__(kThreads) void k_bwd_bnd(const E *__restrict__ gst, const E *__restrict__ hin,
-                                                      const float *__restrict__ cs, float *__restrict__ bnd, int H,
-                                                      int nc, int Q, int64_t PN)
-{
-    __shared__ float red[kThreads / 64];
-    const int u = blockIdx.x;   // (b * nc + c) * H + h
-    const int h = u % H, c = (u / H) % nc, b = u / (H * nc);
-    const E *g = gst + (int64_t)u * PN, *s = hin + (int64_t)u * PN;
-    float acc = 0.f;
-    for (int64_t i = 4 * threadIdx.x; i < PN; i += 4 * kThreads) {
-        float a[4], v[4];
-        load4_f32(g + i, a);
-        load4_f32(s + i, v);
-        acc += a[0] * v[0] + a[1] * v[1] + a[2] * v[2] + a[3] * v[3];
-    }
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float t = 0.f;
-        for (int w = 0; w < kThreads / 64; ++w) t += red[w];
-        const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-        bnd[((int64_t)b * H + h) * nc + c] = __builtin_amdgcn_exp2f(cs[row + Q - 1] * kLog2e) * t;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // per (b, h): dl, ddt, and the dA / dD partial sums
 // ---------------------------------------------------------------------------
@@ -160,7 +131,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bnd(const E *__restrict__ gst,
 //   dl_k = sum_{j >= k} (r_j - c_j + yo_j) + sum_{s < k} Delta_s zo_s + bnd_c
 // with r_j / c_j the row / column sums of S (k_bwd_m), yo_j = dy_j . (entering-
 // state term of y_j), zo_s = x_s . (the G_c term of y'_s), bnd_c = e^{cs_last}
-// <G_c, Hin_c>.  Then dDelta = A dl + x . y' and ddt = dDelta * sigmoid(dt).
+// <G_c, Hin_c> (summed here from the nbp partials the reverse state scan left in
+// bnd_part).  Then dDelta = A dl + x . y' and ddt = dDelta * sigmoid(dt).
 // One wave per (b, h, c); lane l holds the tokens l*per .. l*per + per - 1 (per =
 // Q/64); the scans run in fp64; dA and dD partials go to [b,H,nc].
 __device__ __forceinline__ double wave_incl_scan(double v)
@@ -177,10 +149,10 @@ __device__ __forceinline__ double wave_incl_scan(double v)
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     const float *__restrict__ rpart, const float *__restrict__ cpart, const float *__restrict__ yo,
-    const float *__restrict__ zo, const float *__restrict__ xyp, const float *__restrict__ bnd,
+    const float *__restrict__ zo, const float *__restrict__ xyp, const float *__restrict__ bnd_part,
     const float *__restrict__ dyx, const float *__restrict__ delta, const E *__restrict__ dt,
     const float *__restrict__ A, E *__restrict__ ddt, float *__restrict__ dA_part, float *__restrict__ dD_part, int T,
-    int H, int Q, int nc, int ntp, int64_t rows, int softplus)
+    int H, int Q, int nc, int ntp, int64_t rows, int softplus, int64_t nbp)
 {
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // (b * H + h) * nc + c
     if (wid >= rows) return;   // whole wave
@@ -214,11 +186,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
         zsum += zv[e];
     }
     // suffix sums of a (inclusive) and prefix sums of z (exclusive) over the chunk
-    const double ain = wave_incl_scan(asum), zin = wave_incl_scan(zsum);
+    double bsum = 0.0;
+    for (int64_t i = lane; i < nbp; i += 64) bsum += bnd_part[wid * nbp + i];
+    const double ain = wave_incl_scan(asum), zin = wave_incl_scan(zsum), bin = wave_incl_scan(bsum);
     const double atot = __shfl(ain, 63);
     double asuf = atot - ain + asum;   // sum of a over this lane's tokens and all later lanes
     double zpre = zin - zsum;          // sum of z over earlier lanes
-    const double b0 = bnd[wid];
+    const double b0 = __shfl(bin, 63);
     double sa = 0.0, sd = 0.0;
     for (int e = 0; e < per; ++e) {
         const int j = lane * per + e;

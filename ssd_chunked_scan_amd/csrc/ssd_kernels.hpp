@@ -897,12 +897,17 @@ template <int VE> __device__ __forceinline__ void store_final(float *p, const fl
 // backward pass's gradient-state scan: with U_c in `states` and dL/d(final
 // state) in `init`, slot c receives G_c = dL/d(state after chunk c) and
 // `final_states` receives dL/d(initial state); G_{c-1} = exp(cs_last(c)) G_c +
-// U_c has the same form as the forward step.  (REV takes no seq_idx.)
+// U_c has the same form as the forward step.  (REV takes no seq_idx.)  With
+// `hin` (the states entering each chunk, laid out like `states`) it also forms
+// the boundary term exp(cs_last(c)) <G_c, Hin_c> of the log-decay gradient:
+// each wave's share of the dot product goes to bnd_part[(b, h, c), wave of the
+// (b, h)], PN / (64 VE) partials per (b, h, c), in a fixed order.
 template <typename E, int VE, bool REV = false>
 __global__ __launch_bounds__(kThreads) void k_state_passing(
     E *__restrict__ states, const float *__restrict__ cs, const float *__restrict__ init,
     float *__restrict__ final_states, const int32_t *__restrict__ seq_idx,
-    int T, int H, int64_t PN, int nc, int Q, int64_t total_vecs)
+    int T, int H, int64_t PN, int nc, int Q, int64_t total_vecs,
+    const E *__restrict__ hin = nullptr, float *__restrict__ bnd_part = nullptr)
 {
     using R = typename RawVec<E, VE>::type;
     constexpr int D = kPrefetch;   // divides 64
@@ -926,6 +931,21 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
 #pragma unroll
     for (int k = 0; k < D; ++k)
         if (k < nc) buf[k] = *reinterpret_cast<const R *>(lane_base + (int64_t)chunk(k) * cstride);
+    // the boundary term (REV with hin): Hin of the visited chunks, in a ring of
+    // DH loads in flight (shallower than the states' ring, to keep registers)
+    constexpr bool BND = REV;
+    constexpr int DH = BND ? (sizeof(E) == 2 ? D / 2 : D / 4) : 1;   // divides D
+    const bool bnd_on = BND && hin != nullptr;   // uniform
+    const E *hin_base = BND && hin ? hin + ((int64_t)b * nc * H + h) * PN + e0 : nullptr;
+    const int64_t nwv = PN / (64 * VE), wv = e0 / (64 * VE);
+    R hbuf[DH];
+    if constexpr (BND) {
+        if (bnd_on) {
+#pragma unroll
+            for (int k = 0; k < DH; ++k)
+                if (k < nc) hbuf[k] = *reinterpret_cast<const R *>(hin_base + (int64_t)chunk(k) * cstride);
+        }
+    }
     int sprev = seq_idx ? seq_idx[0] : 0;
     for (int cb = 0; cb < nc; cb += 64) {
         // the per-chunk scalars of 64 visited chunks: lane i holds visit cb + i
@@ -946,6 +966,27 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
                     const bool keep = REV || !seq_idx || sc == sprev;
                     sprev = sc;
                     const float d = exp_neg(lm);
+                    if constexpr (BND) {
+                        if (bnd_on) {
+                            // hs is G_c here: its dot with Hin_c over this wave's elements
+                            float hv[VE];
+                            unpack_vec<E, VE>(hbuf[j % DH], hv);
+                            if (k + DH < nc)
+                                hbuf[j % DH] = *reinterpret_cast<const R *>(hin_base + (int64_t)chunk(k + DH) * cstride);
+                            float dot = 0.f;
+#pragma unroll
+                            for (int v = 0; v < VE; ++v) dot += hs[v] * hv[v];
+                            dot += dpp_mov<kDppQuadXor1>(dot);
+                            dot += dpp_mov<kDppQuadXor2>(dot);
+                            dot += dpp_mov<kDppRowHalfMirror>(dot);   // the other quad of the half row
+                            dot += dpp_mov<kDppRowRor8>(dot);         // the other half row
+                            const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dot), 0)) +
+                                              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dot), 16)) +
+                                              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dot), 32)) +
+                                              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dot), 48));
+                            if (lane == 0) bnd_part[((int64_t)bh * nc + chunk(k)) * nwv + wv] = d * tot;
+                        }
+                    }
 #pragma unroll
                     for (int v = 0; v < VE; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
                 }
