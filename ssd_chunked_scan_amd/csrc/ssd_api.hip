@@ -276,22 +276,26 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, true>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
-                                   (float *)nullptr, (float *)nullptr, (const E *)nullptr);
+                                   (float *)nullptr, (float *)nullptr, (const E *)nullptr, (const float *)nullptr,
+                                   (const float *)nullptr);
             else
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
-                                   (float *)nullptr, (float *)nullptr, (const E *)nullptr);
+                                   (float *)nullptr, (float *)nullptr, (const E *)nullptr, (const float *)nullptr,
+                                   (const float *)nullptr);
             return launched();
         });
     });
 }
 
 // chunk_scan in a dot mode (non-packed): DOT = 1 with P1ONLY (entering-state dot
-// only, no y), or DOT = 2 (y written, both dots) on a chunk-reversed problem.
+// only, no y), or DOT = 2 (both dots) on a chunk-reversed problem, writing
+// dx = dx_delta y' + dx_D x to a->y at the original token order.
 template <typename E, int DOT, bool P1ONLY>
 ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
-                        const E *hin, const E *vec, float *dot1, float *dot2, hipStream_t st)
+                        const E *hin, const E *vec, float *dot1, float *dot2, hipStream_t st,
+                        const float *dx_delta = nullptr, const float *dx_D = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -301,7 +305,7 @@ ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delt
             hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false, DOT, P1ONLY>), grid, dim3(scan_threads<Q>()), 0, st,
                                (const E *)a->x, delta, cs, cb, hin, a->D, (const int32_t *)nullptr, (E *)a->y,
                                (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, vec, dot1, dot2,
-                               (const E *)nullptr);
+                               (const E *)nullptr, dx_delta, dx_D);
             return launched();
         });
     });
@@ -320,7 +324,8 @@ ssd_status run_scan_gated(const Shape &s, const ssd_fwd_args *a, const float *de
             auto launch = [&](auto kern) {
                 hipLaunchKernelGGL(kern, grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x, delta, cs, cb, hin,
                                    a->D, a->seq_idx, (E *)a->y, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
-                                   (int)s.nc, ntp, (const E *)nullptr, (float *)nullptr, (float *)nullptr, z);
+                                   (int)s.nc, ntp, (const E *)nullptr, (float *)nullptr, (float *)nullptr, z,
+                                   (const float *)nullptr, (const float *)nullptr);
             };
             if (s.packed) launch(k_chunk_scan<E, Q, NT, true, 0, false, true>);
             else launch(k_chunk_scan<E, Q, NT, false, 0, false, true>);
@@ -410,7 +415,7 @@ ssd_status run_conv(const ssd_conv_args *a, hipStream_t st)
 // backward
 // ---------------------------------------------------------------------------
 struct BwdWorkspace {
-    size_t delta, cs, cb, states, gstates, cbr, br, cr, csr, dlr, ypr, yo, zo, xyp, rpart, cpart, bnd, dyx,
+    size_t delta, cs, cb, states, gstates, cbr, br, cr, csr, dlr, yo, zo, xyp, rpart, cpart, bnd, dyx,
         mrow, mcol, dA_part, dD_part, total;
 };
 
@@ -420,7 +425,6 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     const size_t dcs = (size_t)(s.b * s.H * s.nc * s.Q) * 4;
     const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * (s.Q + 2 * nt_of(s.N))) * s.esz;
     const size_t sts = (size_t)(s.b * s.nc * s.H * s.P * s.N) * s.esz;
-    const size_t xs = (size_t)(s.b * s.T * s.H * s.P) * s.esz;
     const size_t bcs = (size_t)(s.b * s.T * s.G * s.N) * s.esz;
     const size_t ms = (size_t)(s.b * s.nc * s.G * s.Q * s.Q) * s.esz;
     const size_t bh = (size_t)(s.b * s.H) * 4;
@@ -437,7 +441,6 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     w.cr = take(bcs);
     w.csr = take(dcs);
     w.dlr = take(dcs);
-    w.ypr = take(xs);
     w.yo = take(ntp * dcs);
     w.zo = take(ntp * dcs);
     w.xyp = take(ntp * dcs);
@@ -495,7 +498,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     float *yo = F32(w.yo), *zo = F32(w.zo), *xyp = F32(w.xyp), *rpart = F32(w.rpart), *cpart = F32(w.cpart);
     float *bnd = F32(w.bnd), *dyx = F32(w.dyx), *dA_part = F32(w.dA_part), *dD_part = F32(w.dD_part);
     E *cb = EP(w.cb), *states = EP(w.states), *gstates = EP(w.gstates), *cbr = EP(w.cbr);
-    E *br = EP(w.br), *cr = EP(w.cr), *ypr = EP(w.ypr), *mrow = EP(w.mrow), *mcol = EP(w.mcol);
+    E *br = EP(w.br), *cr = EP(w.cr), *mrow = EP(w.mrow), *mcol = EP(w.mcol);
     ssd_status r;
     ssd_fwd_args f = *a;
     f.final_states = nullptr;
@@ -525,13 +528,14 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     hipLaunchKernelGGL(k_bwd_reverse_cs, dim3(grid1(ncs, 256)), dim3(256), 0, st, cs, csr, dlr, (int)s.T, (int)s.Q,
                        (int)s.nc, ncs);
     if ((r = launched()) != SSD_OK) return r;
-    // 3. reversed-order problem: x <- dy, B <- C, C <- B, unit step size, no skip term
+    // 3. reversed-order problem: x <- dy, B <- C, C <- B, unit step size, no skip
+    //    term; its output is turned into dx = Delta y' + D dy in original order
     ssd_fwd_args rv = *a;
     rv.x = g->dy;
     rv.B = cr;
     rv.C = br;
     rv.D = nullptr;
-    rv.y = ypr;
+    rv.y = g->dx;
     rv.initial_states = nullptr;
     rv.final_states = nullptr;
     if ((r = run_cb<E>(s, &rv, cbr, st)) != SSD_OK) return r;
@@ -540,31 +544,16 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     //    (with the boundary terms e^{cs_last} <G_c, Hin_c> of dl, as partial sums)
     if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, states, bnd, st)) != SSD_OK)
         return r;
-    // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y'
-    if ((r = run_scan_dot<E, 2, false>(s, &rv, dlr, csr, cbr, gstates, (const E *)a->x, zo, xyp, st)) != SSD_OK)
+    // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y';
+    //    it writes dx = Delta y' + D dy
+    if ((r = run_scan_dot<E, 2, false>(s, &rv, dlr, csr, cbr, gstates, (const E *)a->x, zo, xyp, st, delta,
+                                       a->D)) != SSD_OK)
         return r;
     // 6. dy . (entering-state term of y), from the forward's entering states
     if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st)) != SSD_OK)
         return r;
-    // 7. dx, dy . x
-    {
-        auto tok = [&](auto lw) {
-            constexpr int L = decltype(lw)::value;
-            const int64_t waves = s.b * s.T * ((s.H + 64 / L - 1) / (64 / L));
-            hipLaunchKernelGGL((k_bwd_token<E, L>), dim3(grid1(waves, kThreads / 64)), dim3(kThreads), 0, st,
-                               (const E *)a->x, (const E *)g->dy, (const E *)ypr, delta, a->D, (E *)g->dx, dyx,
-                               (int)s.T, (int)s.H, (int)s.P, (int)s.Q, (int)s.nc, waves);
-            return launched();
-        };
-        const int64_t need = s.P / 4;   // lanes per head
-        if (need <= 4) r = tok(std::integral_constant<int, 4>{});
-        else if (need <= 8) r = tok(std::integral_constant<int, 8>{});
-        else if (need <= 16) r = tok(std::integral_constant<int, 16>{});
-        else if (need <= 32) r = tok(std::integral_constant<int, 32>{});
-        else r = tok(std::integral_constant<int, 64>{});
-        if (r != SSD_OK) return r;
-    }
-    // 8. M (summed over the group's heads) with the row / column sums of S
+    // 7. M (summed over the group's heads) with the row / column sums of S, and
+    //    dy . x of every (token, head) from its diagonal
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     const int nnt = (int)((s.N + 63) / 64);
     if ((r = with_q(s.Q, [&](auto q) {
@@ -572,12 +561,12 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
                  constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
                  hipLaunchKernelGGL((k_bwd_m<E, Q, NT>), dim3((unsigned)(ntri * s.nc * s.G), (unsigned)s.b),
                                     dim3(kThreads), 0, st, (const E *)g->dy, (const E *)a->x, delta, cs, (const E *)cb,
-                                    mrow, mcol, rpart, cpart, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc);
+                                    mrow, mcol, rpart, cpart, dyx, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc);
                  return launched();
              });
          })) != SSD_OK)
         return r;
-    // 9. dl, ddt, dA, dD
+    // 8. dl, ddt, dA, dD
     const int64_t dlrows = s.b * s.H * s.nc;
     hipLaunchKernelGGL(k_bwd_dl<E>, dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart, yo, zo,
                        xyp, bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T,
@@ -586,7 +575,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     hipLaunchKernelGGL(k_bwd_sum_heads, dim3((unsigned)s.H), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
                        (int)s.b, (int)s.H, (int)s.nc);
     if ((r = launched()) != SSD_OK) return r;
-    // 10. dC and dB
+    // 9. dC and dB
     return with_q(s.Q, [&](auto q) {
         constexpr int Q = decltype(q)::value;
         const dim3 grid((unsigned)(s.nc * s.G * qt * nnt), (unsigned)s.b);

@@ -74,56 +74,6 @@ __global__ void k_bwd_reverse_cs(const float *__restrict__ cs, float *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// per token: dx = Delta y' + D dy, and dy . x
-// ---------------------------------------------------------------------------
-// Lanes work on four consecutive p (8- or 16-byte accesses); a wave covers
-// 64 / L heads of one token, L = the power of two >= P/4 lanes per head (for P
-// above 256, L = 64 and each lane takes several four-element groups).  y'_s
-// comes from the reversed scan, so it is read at the mirrored position.  dy . x
-// of each (token, head) goes to a [b,H,nc,Q] row.
-template <typename E, int L>
-__global__ __launch_bounds__(kThreads) void k_bwd_token(
-    const E *__restrict__ x, const E *__restrict__ dy, const E *__restrict__ yrev, const float *__restrict__ delta,
-    const float *__restrict__ D, E *__restrict__ dx, float *__restrict__ dyx, int T, int H, int P, int Q, int nc,
-    int64_t total_waves)
-{
-    constexpr int HPW = 64 / L;   // heads per wave
-    const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (wid >= total_waves) return;   // whole wave
-    const int lane = threadIdx.x & 63, seg = lane / L, sl = lane % L;
-    const int hgroups = (H + HPW - 1) / HPW;
-    const int hg = (int)(wid % hgroups);
-    const int64_t bt = wid / hgroups;
-    const int h = hg * HPW + seg;
-    const int b = (int)(bt / T), t = (int)(bt % T);
-    const int c = t / Q, k = t % Q, len = min(Q, T - c * Q);
-    const int tr = c * Q + (len - 1 - k);
-    float sdx = 0.f;
-    int64_t srow = 0;
-    if (h < H) {
-        srow = (((int64_t)b * H + h) * nc + c) * Q + k;
-        const float dl = delta[srow];
-        const float Dh = D ? D[h] : 0.f;
-        const int64_t o = (bt * H + h) * P, orv = (((int64_t)b * T + tr) * H + h) * P;
-        for (int p = 4 * sl; p < P; p += 4 * L) {
-            float xv[4], dv[4], yv[4], ov[4];
-            load4_f32(x + o + p, xv);
-            load4_f32(dy + o + p, dv);
-            load4_f32(yrev + orv + p, yv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                ov[q] = dl * yv[q] + Dh * dv[q];
-                sdx += dv[q] * xv[q];
-            }
-            store4_f32(dx + o + p, ov);
-        }
-    }
-#pragma unroll
-    for (int m = L / 2; m > 0; m >>= 1) sdx += __shfl_xor(sdx, m, L);
-    if (sl == 0 && h < H) dyx[srow] = sdx;
-}
-
-// ---------------------------------------------------------------------------
 // per (b, h): dl, ddt, and the dA / dD partial sums
 // ---------------------------------------------------------------------------
 // Inside chunk c (l_k enters through cs_j for j >= k in the chunk, and through
@@ -265,11 +215,13 @@ __global__ void k_bwd_sum_heads(const float *__restrict__ dA_part, const float *
 // rpart[si][t] = sum_{s in tile si} S[t][s] and column sums cpart[ti][s] = sum_{t
 // in tile ti} S[t][s] are written per tile ([QT][b,H,nc,Q] fp32 each); rows and
 // columns come from one S, so their difference cancels exactly where it should.
+// The diagonal tiles also write each head's dy_t . x_t (the product at s = t)
+// to dyx [b,H,nc,Q] fp32.
 template <typename E, int Q, int NT>
 __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const E *__restrict__ dy, const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
     const E *__restrict__ cbuf, E *__restrict__ mrow, E *__restrict__ mcol, float *__restrict__ rpart,
-    float *__restrict__ cpart, int T, int H, int G, int P, int nc)
+    float *__restrict__ cpart, float *__restrict__ dyx, int T, int H, int G, int P, int nc)
 {
     using F = frag_t<E>;
     constexpr int V = kVec16<E>, ES = (int)sizeof(E);
@@ -415,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
             } else {
                 // the diagonal tile or the ragged last one: the exact per-element
                 // decay, and only s <= t < len
+                const int64_t hrow = (((int64_t)b * H + g * hpg + k / PC) * nc + c) * Q;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int s = si * 64 + s_w + 16 * j + li;
@@ -424,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int t = ti * 64 + t_w + 16 * i + 4 * lg + r;
+                            if (si == ti && s == t && t < len) dyx[hrow + t] = acc[i][j][r];
                             if (s <= t && t < len) {
                                 const float w =
                                     __builtin_amdgcn_exp2f((hcs[0][t_w + 16 * i + 4 * lg + r] - css) * kLog2e) * ds;

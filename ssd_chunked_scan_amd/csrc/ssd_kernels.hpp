@@ -1130,6 +1130,10 @@ template <int Q> constexpr int scan_threads() { return Q * 2; }
 //   dot1 = v . (the entering-state term alone),  dot2 (DOT = 2) = v . (the whole
 //   output before the D skip term).
 // P1ONLY computes dot1 only: no x tile, no intra-chunk terms, no y.
+// DOT = 2 writes, instead of the reversed problem's output y'_t, the gradient
+// dx = dx_delta[t'] y'_t + dx_D[h] x_t at the token's original position t' =
+// len-1-t (x = the reversed problem's input, here dy; dx_delta = the forward's
+// step sizes in their own order; dx_D may be null).
 // GATE multiplies every output by SiLU(z) (z = `gate`, laid out like y) before
 // its one rounding to E: the gate of the Mamba-2 block ("SSM 家族全景图（下）",
 // the block data flow of section five: the gated path passes a SiLU and the two
@@ -1140,7 +1144,8 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const E *__restrict__ cbuf, const E *__restrict__ hin,
     const float *__restrict__ D, const int32_t *__restrict__ seq_idx, E *__restrict__ y,
     int T, int H, int G, int P, int N, int nc, int ntp, const E *__restrict__ vec = nullptr,
-    float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr, const E *__restrict__ gate = nullptr)
+    float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr, const E *__restrict__ gate = nullptr,
+    const float *__restrict__ dx_delta = nullptr, const float *__restrict__ dx_D = nullptr)
 {
     using F = frag_t<E>;
     constexpr int TH = scan_threads<Q>();
@@ -1563,7 +1568,20 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
         }
     }
 
-    // ---- epilogue: store y ----
+    // ---- epilogue: store y (DOT = 2: dx at the mirrored rows) ----
+    const float dxD = DOT == 2 && dx_D ? dx_D[h] : 0.f;
+    if constexpr (DOT == 2) {
+        // Delta y' in fp32 here; the D dy term joins in the row phase below
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+            const int t = 16 * jb[k] + li;
+            const float dl = t < len ? dx_delta[cso + len - 1 - t] : 0.f;
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[k][pb][q] *= dl;
+        }
+    }
     if constexpr (sizeof(E) == 2) {
         // Each wave turns its own 32 rows around in the entering-state region (free
         // since the barrier after step 4) so that y leaves as whole 128-byte rows
@@ -1585,9 +1603,23 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int t = 16 * jb[k] + 8 * half + rsel;
-                const uint4 v = *reinterpret_cast<const uint4 *>(hs + yoff(t, chunk));
+                uint4 v = *reinterpret_cast<const uint4 *>(hs + yoff(t, chunk));
+                if constexpr (DOT == 2) {
+                    // + D dy, with dy's row t (p0 + 8 chunk ..) from the x tile
+                    if (dx_D) {
+                        const floatx8 d = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), floatx8);
+                        const floatx8 xv = __builtin_convertvector(
+                            *reinterpret_cast<const bf16x8 *>(xt + t * 64 + 4 * ((2 * chunk) ^ XT::swz(t))), floatx8);
+                        float o[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) o[e] = d[e] + dxD * xv[e];
+                        v = uint4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                  pack_bf16x2(o[6], o[7])};
+                    }
+                }
+                const int tw = DOT == 2 ? len - 1 - t : t;   // the row written
                 if (t < len && pin)
-                    *reinterpret_cast<uint4 *>(y + (((int64_t)b * T + t0 + t) * H + h) * P + p0 + 8 * chunk) = v;
+                    *reinterpret_cast<uint4 *>(y + (((int64_t)b * T + t0 + tw) * H + h) * P + p0 + 8 * chunk) = v;
             }
         }
     } else {
@@ -1601,7 +1633,16 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
                 const int p = p0 + pb * 16 + 4 * lg;
                 if (p >= P) continue;
                 float o[4] = {acc[k][pb][0], acc[k][pb][1], acc[k][pb][2], acc[k][pb][3]};
-                store4_f32(y + (((int64_t)b * T + t0 + t) * H + h) * P + p, o);
+                const int tw = DOT == 2 ? len - 1 - t : t;   // the row written
+                if constexpr (DOT == 2) {
+                    if (dx_D) {
+                        float xv[4];
+                        load4_f32(x + (((int64_t)b * T + t0 + tw) * H + h) * P + p, xv);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) o[q] += dxD * xv[q];
+                    }
+                }
+                store4_f32(y + (((int64_t)b * T + t0 + tw) * H + h) * P + p, o);
             }
         }
     }
