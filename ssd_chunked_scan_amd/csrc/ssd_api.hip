@@ -277,13 +277,13 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
                                    (float *)nullptr, (float *)nullptr, (const E *)nullptr, (const float *)nullptr,
-                                   (const float *)nullptr);
+                                   (const float *)nullptr, (float *)nullptr);
             else
                 hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false>), grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x,
                                    delta, cs, cb, hin, a->D, a->seq_idx, (E *)a->y, (int)s.T,
                                    (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (const E *)nullptr,
                                    (float *)nullptr, (float *)nullptr, (const E *)nullptr, (const float *)nullptr,
-                                   (const float *)nullptr);
+                                   (const float *)nullptr, (float *)nullptr);
             return launched();
         });
     });
@@ -295,7 +295,7 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
 template <typename E, int DOT, bool P1ONLY>
 ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
                         const E *hin, const E *vec, float *dot1, float *dot2, hipStream_t st,
-                        const float *dx_delta = nullptr, const float *dx_D = nullptr)
+                        const float *dx_delta = nullptr, const float *dx_D = nullptr, float *dxv = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -305,7 +305,7 @@ ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delt
             hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false, DOT, P1ONLY>), grid, dim3(scan_threads<Q>()), 0, st,
                                (const E *)a->x, delta, cs, cb, hin, a->D, (const int32_t *)nullptr, (E *)a->y,
                                (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, vec, dot1, dot2,
-                               (const E *)nullptr, dx_delta, dx_D);
+                               (const E *)nullptr, dx_delta, dx_D, dxv);
             return launched();
         });
     });
@@ -325,7 +325,7 @@ ssd_status run_scan_gated(const Shape &s, const ssd_fwd_args *a, const float *de
                 hipLaunchKernelGGL(kern, grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x, delta, cs, cb, hin,
                                    a->D, a->seq_idx, (E *)a->y, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
                                    (int)s.nc, ntp, (const E *)nullptr, (float *)nullptr, (float *)nullptr, z,
-                                   (const float *)nullptr, (const float *)nullptr);
+                                   (const float *)nullptr, (const float *)nullptr, (float *)nullptr);
             };
             if (s.packed) launch(k_chunk_scan<E, Q, NT, true, 0, false, true>);
             else launch(k_chunk_scan<E, Q, NT, false, 0, false, true>);
@@ -447,7 +447,7 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     w.rpart = take(qt * dcs);
     w.cpart = take(qt * dcs);
     w.bnd = take((size_t)(s.b * s.H * s.nc) * (size_t)(s.P * s.N / 256) * 4);   // per (b, h, c): PN / 256 partials
-    w.dyx = take(dcs);
+    w.dyx = take(dcs * ntp);   // one slice per 64-wide p tile
     w.mrow = take(ms);
     w.mcol = take(ms);
     w.dA_part = take(bh * (size_t)s.nc);
@@ -545,15 +545,14 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, states, bnd, st)) != SSD_OK)
         return r;
     // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y';
-    //    it writes dx = Delta y' + D dy
+    //    it writes dx = Delta y' + D dy, and dy . x per (token, head)
     if ((r = run_scan_dot<E, 2, false>(s, &rv, dlr, csr, cbr, gstates, (const E *)a->x, zo, xyp, st, delta,
-                                       a->D)) != SSD_OK)
+                                       a->D, dyx)) != SSD_OK)
         return r;
     // 6. dy . (entering-state term of y), from the forward's entering states
     if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st)) != SSD_OK)
         return r;
-    // 7. M (summed over the group's heads) with the row / column sums of S, and
-    //    dy . x of every (token, head) from its diagonal
+    // 7. M (summed over the group's heads) with the row / column sums of S
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     const int nnt = (int)((s.N + 63) / 64);
     if ((r = with_q(s.Q, [&](auto q) {
@@ -561,7 +560,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
                  constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
                  hipLaunchKernelGGL((k_bwd_m<E, Q, NT>), dim3((unsigned)(ntri * s.nc * s.G), (unsigned)s.b),
                                     dim3(kThreads), 0, st, (const E *)g->dy, (const E *)a->x, delta, cs, (const E *)cb,
-                                    mrow, mcol, rpart, cpart, dyx, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc);
+                                    mrow, mcol, rpart, cpart, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc);
                  return launched();
              });
          })) != SSD_OK)

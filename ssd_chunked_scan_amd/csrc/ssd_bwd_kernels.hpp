@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
             }
             ddt[((int64_t)b * T + t) * H + h] = from_float<E>(gr);
             sa += (double)delta[row + j] * dl;
-            sd += dyx[row + j];
+            for (int tp = 0; tp < ntp; ++tp) sd += dyx[tp * slice + row + j];
         }
         asuf -= av[e];
         zpre += zv[e];
@@ -215,13 +215,11 @@ __global__ void k_bwd_sum_heads(const float *__restrict__ dA_part, const float *
 // rpart[si][t] = sum_{s in tile si} S[t][s] and column sums cpart[ti][s] = sum_{t
 // in tile ti} S[t][s] are written per tile ([QT][b,H,nc,Q] fp32 each); rows and
 // columns come from one S, so their difference cancels exactly where it should.
-// The diagonal tiles also write each head's dy_t . x_t (the product at s = t)
-// to dyx [b,H,nc,Q] fp32.
 template <typename E, int Q, int NT>
 __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const E *__restrict__ dy, const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
     const E *__restrict__ cbuf, E *__restrict__ mrow, E *__restrict__ mcol, float *__restrict__ rpart,
-    float *__restrict__ cpart, float *__restrict__ dyx, int T, int H, int G, int P, int nc)
+    float *__restrict__ cpart, int T, int H, int G, int P, int nc)
 {
     using F = frag_t<E>;
     constexpr int V = kVec16<E>, ES = (int)sizeof(E);
@@ -367,7 +365,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
             } else {
                 // the diagonal tile or the ragged last one: the exact per-element
                 // decay, and only s <= t < len
-                const int64_t hrow = (((int64_t)b * H + g * hpg + k / PC) * nc + c) * Q;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int s = si * 64 + s_w + 16 * j + li;
@@ -377,7 +374,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int t = ti * 64 + t_w + 16 * i + 4 * lg + r;
-                            if (si == ti && s == t && t < len) dyx[hrow + t] = acc[i][j][r];
                             if (s <= t && t < len) {
                                 const float w =
                                     __builtin_amdgcn_exp2f((hcs[0][t_w + 16 * i + 4 * lg + r] - css) * kLog2e) * ds;

@@ -1133,7 +1133,8 @@ template <int Q> constexpr int scan_threads() { return Q * 2; }
 // DOT = 2 writes, instead of the reversed problem's output y'_t, the gradient
 // dx = dx_delta[t'] y'_t + dx_D[h] x_t at the token's original position t' =
 // len-1-t (x = the reversed problem's input, here dy; dx_delta = the forward's
-// step sizes in their own order; dx_D may be null).
+// step sizes in their own order; dx_D may be null), and x . v per token over
+// this workgroup's 64 p to dxv (laid out like dot1).
 // GATE multiplies every output by SiLU(z) (z = `gate`, laid out like y) before
 // its one rounding to E: the gate of the Mamba-2 block ("SSM 家族全景图（下）",
 // the block data flow of section five: the gated path passes a SiLU and the two
@@ -1145,7 +1146,8 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const float *__restrict__ D, const int32_t *__restrict__ seq_idx, E *__restrict__ y,
     int T, int H, int G, int P, int N, int nc, int ntp, const E *__restrict__ vec = nullptr,
     float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr, const E *__restrict__ gate = nullptr,
-    const float *__restrict__ dx_delta = nullptr, const float *__restrict__ dx_D = nullptr)
+    const float *__restrict__ dx_delta = nullptr, const float *__restrict__ dx_D = nullptr,
+    float *__restrict__ dxv = nullptr)
 {
     using F = frag_t<E>;
     constexpr int TH = scan_threads<Q>();
@@ -1605,11 +1607,22 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
                 const int t = 16 * jb[k] + 8 * half + rsel;
                 uint4 v = *reinterpret_cast<const uint4 *>(hs + yoff(t, chunk));
                 if constexpr (DOT == 2) {
-                    // + D dy, with dy's row t (p0 + 8 chunk ..) from the x tile
+                    // dy's row t (p0 + 8 chunk ..) from the x tile: + D dy, and dy . v
+                    // with v's same row and columns (still in registers), summed
+                    // over the octet of lanes that holds the row
+                    const floatx8 xv = __builtin_convertvector(
+                        *reinterpret_cast<const bf16x8 *>(xt + t * 64 + 4 * ((2 * chunk) ^ XT::swz(t))), floatx8);
+                    const floatx8 vr = __builtin_convertvector(__builtin_bit_cast(bf16x8, vrow[k][half]), floatx8);
+                    float dv = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dv += xv[e] * vr[e];
+                    dv += dpp_mov<kDppQuadXor1>(dv);
+                    dv += dpp_mov<kDppQuadXor2>(dv);
+                    dv += dpp_mov<kDppRowHalfMirror>(dv);   // the octet's other quad
+                    if (chunk == 0 && t < len)
+                        dxv[((((int64_t)tp * gridDim.y + b) * H + h) * nc + c) * Q + len - 1 - t] = dv;
                     if (dx_D) {
                         const floatx8 d = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), floatx8);
-                        const floatx8 xv = __builtin_convertvector(
-                            *reinterpret_cast<const bf16x8 *>(xt + t * 64 + 4 * ((2 * chunk) ^ XT::swz(t))), floatx8);
                         float o[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) o[e] = d[e] + dxD * xv[e];
@@ -1627,22 +1640,30 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
         for (int k = 0; k < NSB; ++k) {
             const int t = 16 * jb[k] + li;
-            if (t >= len) continue;
+            const int tw = DOT == 2 ? len - 1 - t : t;   // the row written
+            float dpart = 0.f;
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) {
                 const int p = p0 + pb * 16 + 4 * lg;
-                if (p >= P) continue;
+                if (t >= len || p >= P) continue;
                 float o[4] = {acc[k][pb][0], acc[k][pb][1], acc[k][pb][2], acc[k][pb][3]};
-                const int tw = DOT == 2 ? len - 1 - t : t;   // the row written
                 if constexpr (DOT == 2) {
-                    if (dx_D) {
-                        float xv[4];
-                        load4_f32(x + (((int64_t)b * T + t0 + tw) * H + h) * P + p, xv);
+                    float xv[4], vv[4];
+                    load4_f32(x + (((int64_t)b * T + t0 + tw) * H + h) * P + p, xv);
+                    load4_f32(vec + (((int64_t)b * T + t0 + tw) * H + h) * P + p, vv);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) o[q] += dxD * xv[q];
+                    for (int q = 0; q < 4; ++q) {
+                        dpart += xv[q] * vv[q];
+                        o[q] += dxD * xv[q];
                     }
                 }
                 store4_f32(y + (((int64_t)b * T + t0 + tw) * H + h) * P + p, o);
+            }
+            if constexpr (DOT == 2) {
+                // dy . v of token t over the four lane groups (all lanes take part)
+                dpart += __shfl_xor(dpart, 16);
+                dpart += __shfl_xor(dpart, 32);
+                if (lg == 0 && t < len) dxv[((((int64_t)tp * gridDim.y + b) * H + h) * nc + c) * Q + tw] = dpart;
             }
         }
     }
