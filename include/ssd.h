@@ -160,9 +160,16 @@ ssd_status ssd_chunk_state(const ssd_fwd_args *args, float *delta, float *cs, co
 ssd_status ssd_state_passing(const ssd_fwd_args *args, const float *cs, void *states,
                              void *stream);
 
-/* With seq_idx only: final_states[s] = the state after segment s's last token,
- * from that token's chunk inputs and the state entering the chunk (`states` as
- * left by ssd_state_passing).  `seg_end` is caller scratch of nseq int32. */
+/* With seq_idx only: final_states[s] = the state after segment s's last token.
+ * Packing several sequences into one stream and cutting the state carry between
+ * them (A_t = 0 at each boundary) is the variable-length mechanism of section
+ * 4.2 of "Transformers与SSMs的隐藏联系" (jsqmd.com); each packed sequence's own
+ * final state is then the recurrence's h at its last token (section 3.1 of
+ * "Mamba 2 -- Transformers are SSMs").  It is formed from that token's chunk
+ * inputs and the state entering the chunk (`states` as left by
+ * ssd_state_passing).  `seg_end` is caller scratch of nseq int32 (device); ids
+ * that never occur get a zero state.  Errors: SSD_ERR_SEQ_IDX without seq_idx,
+ * SSD_ERR_NULL_POINTER without final_states. */
 ssd_status ssd_seq_final_states(const ssd_fwd_args *args, const float *delta, const float *cs,
                                 const void *states, int32_t *seg_end, void *stream);
 

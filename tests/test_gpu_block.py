@@ -217,7 +217,8 @@ def test_block_small_workload_full_size():
 def test_block_long_workload_full_size():
     """The block measured by the benchmark: the long workload's shape (16384 tokens,
     32 heads of 64, N = 256, chunk 256, bf16; xBC of 2560 channels, 4 taps), the
-    convolution checked on every element, the gated forward on sampled heads."""
+    convolution checked on every element, the gated forward on every (batch,
+    head) slice."""
     inp = wl.workload(3)
     blk = wl.block_inputs(inp, seed=4000)
     x, B, C = check_conv(inp, blk, "bf16", label=inp.name)
@@ -225,18 +226,13 @@ def test_block_long_workload_full_size():
     y, _ = ssd.fwd_gated(x, g.dt, g.A, B, C, inp.chunk, blk.z.to("cuda:0"), D=g.D, initial_states=g.initial_states)
     torch.cuda.synchronize()
     b, T, H, P = inp.x.shape
-    mask = np.zeros((b, H), bool)
-    rng = np.random.default_rng(3)
-    for _ in range(5):
-        mask[rng.integers(b), rng.integers(H)] = True
-    mask[b - 1, H - 1] = True
     # the oracle's chain starts from its own convolution, rounded to bf16 once
     H_, P_, G_, N_ = H, P, inp.B.shape[2], inp.B.shape[3]
     rx, rB, rC = (torch.from_numpy(a).to(torch.bfloat16)
                   for a in oracle.conv1d_silu(blk.xbc, blk.weight, H_, P_, G_, N_, blk.bias))
-    r = oracle.forward(rx, inp.dt, inp.A, rB, rC, inp.D, inp.initial_states, unit_mask=mask)
+    r = oracle.forward(rx, inp.dt, inp.A, rB, rC, inp.D, inp.initial_states)
     ref = oracle.gated(r.y, blk.z)
     got = f64(y)
-    e = max(rel(got[i, :, h], ref[i, :, h]) for i, h in zip(*np.nonzero(mask)))
-    _log(f"    sampled heads {int(mask.sum())}: max rel-L2 gated y={e:.3e}")
+    e = max(rel(got[i, :, h], ref[i, :, h]) for i in range(b) for h in range(H))
+    _log(f"    all {b * H} (batch, head) slices: max rel-L2 gated y={e:.3e}")
     assert e <= TOL["bf16"]
