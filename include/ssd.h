@@ -63,7 +63,9 @@ typedef enum {
     SSD_ERR_WORKSPACE_TOO_SMALL = 7, /* workspace_bytes below ssd_fwd_workspace_size */
     SSD_ERR_MISALIGNED = 8,          /* a tensor pointer is not 16-byte aligned */
     SSD_ERR_ALIASING = 9,            /* an output overlaps an input or another output */
-    SSD_ERR_HIP = 10                 /* a kernel launch failed */
+    SSD_ERR_HIP = 10,                /* a kernel launch failed */
+    SSD_ERR_SCRATCH_TOO_SMALL = 11   /* ssd_fwd_noalloc: the problem's workspace exceeds
+                                        SSD_NOALLOC_SCRATCH_BYTES */
 } ssd_status;
 
 typedef enum {
@@ -110,6 +112,29 @@ ssd_status ssd_fwd_workspace_size(const ssd_fwd_args *args, size_t *bytes);
 
 /* The whole forward pass: y and final_states from the inputs in `args`. */
 ssd_status ssd_fwd(const ssd_fwd_args *args, void *stream);
+
+/*
+ * ssd_fwd_noalloc: ssd_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It runs the very kernels of ssd_fwd, with the workspace taken
+ * from a static device array inside the library instead of args->workspace
+ * (ignored).  The caller still passes the inputs and outputs.
+ *   - Limit: the problem's ssd_fwd_workspace_size must be at most
+ *     SSD_NOALLOC_SCRATCH_BYTES (128 MiB: e.g. 16384 tokens x 32 heads x P = 64
+ *     x N = 256 in bf16 needs about 92 MiB); larger problems return
+ *     SSD_ERR_SCRATCH_TOO_SMALL before anything is enqueued.
+ *   - Every GPU the library runs on holds its own copy of the array until the
+ *     process ends.  The first call on a device looks up the array's address
+ *     on that device (once, no allocation); nothing here calls hipMalloc or
+ *     hipFree.
+ *   - All calls on one GPU share that GPU's array: calls that may overlap in
+ *     time on one GPU (several streams, several host threads) race and must be
+ *     ordered by the caller.  Calls on one stream are ordered by the stream.
+ *     No state is carried from one call to the next: every byte a call reads
+ *     from the array it has written first.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+ssd_status ssd_fwd_noalloc(const ssd_fwd_args *args, void *stream);
 
 /*
  * Per-step entry points.  Each runs one step of the chunked algorithm with

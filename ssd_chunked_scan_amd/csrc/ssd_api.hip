@@ -9,6 +9,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "ssd_kernels.hpp"
@@ -588,6 +589,35 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     });
 }
 
+// ---------------------------------------------------------------------------
+// static scratch for ssd_fwd_noalloc
+// ---------------------------------------------------------------------------
+// The forward's workspace for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy of this array from module load until the
+// process ends.  In host code `scratch` only names the symbol: its device
+// address on the current device comes from hipGetSymbolAddress, taken once per
+// device and cached, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = SSD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (nullptr on failure).
+void *scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 const char *const kStatusText[] = {
     "ok",
     "a required pointer is NULL",
@@ -600,6 +630,7 @@ const char *const kStatusText[] = {
     "a tensor pointer is not 16-byte aligned",
     "an output overlaps an input or another output",
     "a HIP kernel launch failed",
+    "the problem needs more scratch than the library's static buffer holds (ssd_fwd_noalloc)",
 };
 
 }  // namespace
@@ -644,6 +675,28 @@ ssd_status ssd_fwd(const ssd_fwd_args *args, void *stream)
     for (const Range &o : others)
         if (overlaps(ws, o)) return SSD_ERR_ALIASING;
     return s.dtype == SSD_DTYPE_BF16 ? fwd_typed<bf16>(s, args, w, st) : fwd_typed<float>(s, args, w, st);
+}
+
+ssd_status ssd_fwd_noalloc(const ssd_fwd_args *args, void *stream)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB | kNeedC | kNeedY | kCheckFinal)) != SSD_OK)
+        return r;
+    const Workspace w = workspace_layout(s);
+    if (w.total > kScratchBytes) return SSD_ERR_SCRATCH_TOO_SMALL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.T == 0) return fill_final(s, args, st);
+    void *ws = scratch_address();
+    if (!ws) return SSD_ERR_HIP;
+    // The forward writes every workspace byte it later reads (delta, cs, the
+    // chunk_cb buffer's lower tiles, the states, the segment ends), so nothing in
+    // the static buffer has to be cleared between calls.
+    ssd_fwd_args a = *args;
+    a.workspace = ws;
+    a.workspace_bytes = kScratchBytes;
+    return s.dtype == SSD_DTYPE_BF16 ? fwd_typed<bf16>(s, &a, w, st) : fwd_typed<float>(s, &a, w, st);
 }
 
 ssd_status ssd_chunk_cumsum(const ssd_fwd_args *args, float *delta, float *cs, void *stream)

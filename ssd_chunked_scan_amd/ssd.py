@@ -27,7 +27,10 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 EXPORTED = ["ssd_abi_version", "ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd",
             "ssd_chunk_cumsum", "ssd_chunk_cb", "ssd_chunk_state", "ssd_state_passing",
             "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step", "ssd_bwd_workspace_size", "ssd_bwd",
-            "ssd_fwd_gated", "ssd_conv1d_silu"]
+            "ssd_fwd_gated", "ssd_conv1d_silu", "ssd_fwd_noalloc"]
+
+# The static scratch of ssd_fwd_noalloc (SSD_NOALLOC_SCRATCH_BYTES in include/ssd.h).
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class FwdArgs(ctypes.Structure):
@@ -115,6 +118,7 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_bwd.argtypes = [P, ctypes.POINTER(BwdArgs), vp]
     lib.ssd_fwd_gated.argtypes = [P, vp, vp]
     lib.ssd_conv1d_silu.argtypes = [ctypes.POINTER(ConvArgs), vp]
+    lib.ssd_fwd_noalloc.argtypes = [P, vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -232,6 +236,25 @@ def fwd_gated(x, dt, A, B, C, chunk, z, D=None, initial_states=None, seq_idx=Non
     gate fused into its last kernel; z is [b,T,H,P] like x."""
     return _fwd(z, x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus, y,
                 final_states, workspace, stream, want_final)
+
+
+def fwd_noalloc(x, dt, A, B, C, chunk, D=None, initial_states=None, seq_idx=None, nseq=None,
+                dt_softplus=True, y=None, final_states=None, stream=None, want_final=True):
+    """y, final_states = SSD forward through ``ssd_fwd_noalloc``: the library's
+    static device scratch replaces the workspace (the problem's workspace must fit
+    ``NOALLOC_SCRATCH_BYTES``).  Pass ``y`` and ``final_states`` pre-allocated for
+    a call that allocates nothing at all."""
+    p = Problem(x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus)
+    if y is None:
+        y = p.empty(x.shape)
+    _check(y, "y", x.dtype, x.shape, p.device)
+    if want_final and final_states is None:
+        final_states = p.empty(p.final_shape(), torch.float32)
+    _check(final_states, "final_states", torch.float32, p.final_shape(), p.device)
+    p.args.y = _ptr(y)
+    p.args.final_states = _ptr(final_states)
+    p.call("ssd_fwd_noalloc", stream=stream)
+    return y, final_states
 
 
 def _fwd(z, x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus, y, final_states,

@@ -13,7 +13,7 @@ from ssd_chunked_scan_amd import ssd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssd.h")
 
-OK, NULLP, SHAPE, DTYPE, CHUNK, GROUPS, SEQ, WS, MISAL, ALIAS, HIP = range(11)
+OK, NULLP, SHAPE, DTYPE, CHUNK, GROUPS, SEQ, WS, MISAL, ALIAS, HIP, SCRATCH = range(12)
 
 
 def declared_functions():
@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(11):
+    for code in range(12):
         s = ssd.status_string(code)
         assert s and s != "unknown status"
     assert ssd.status_string(99) == "unknown status"
@@ -95,6 +95,25 @@ def test_workspace_size(lib):
     assert n.value == want
     bad = _args(chunk=48)
     assert lib.ssd_fwd_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == CHUNK
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """ssd_fwd_noalloc validates like ssd_fwd and refuses, before any HIP call, a
+    problem whose workspace exceeds the static scratch (the 2.7B-shaped workload
+    needs about 190 MiB; the long 16K-token one about 92 MiB fits)."""
+    big = _args(batch=8, seqlen=2048, nheads=80, headdim=64, dstate=128, chunk=128, workspace=0)
+    n = ctypes.c_size_t()
+    assert lib.ssd_fwd_workspace_size(ctypes.byref(big), ctypes.byref(n)) == OK
+    assert n.value > ssd.NOALLOC_SCRATCH_BYTES
+    assert lib.ssd_fwd_noalloc(ctypes.byref(big), None) == SCRATCH
+    fits = _args(batch=1, seqlen=16384, nheads=32, headdim=64, dstate=256, chunk=256)
+    assert lib.ssd_fwd_workspace_size(ctypes.byref(fits), ctypes.byref(n)) == OK
+    assert n.value <= ssd.NOALLOC_SCRATCH_BYTES
+    # the ordinary argument checks come first
+    assert lib.ssd_fwd_noalloc(ctypes.byref(_args(chunk=32)), None) == CHUNK
+    assert lib.ssd_fwd_noalloc(ctypes.byref(_args(x=0)), None) == NULLP
+    assert lib.ssd_fwd_noalloc(ctypes.byref(_args(y=0x10000000)), None) == ALIAS
+    assert lib.ssd_fwd_noalloc(None, None) == NULLP
 
 
 def test_step_entry_points_validate(lib):
