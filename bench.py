@@ -5,18 +5,26 @@ One step = one full forward pass (chunk_cb, chunk_state with the cumsum step
 inside, state_passing, [seq_final], chunk_scan) over one batch of seeded synthetic
 input already resident in HBM.  Prints ONE JSON line:
 
-  value        whole-job tokens/s over the K timed steps (wall clock, synchronised)
-  roofline     the dominant kernel's achieved algorithmic FLOP/s (or bytes/s) per
+  value        tokens/s of the headline workload over the K timed steps, each
+               step cold: a 1 GiB write before it (outside its HIP events)
+               evicts L2 and the 256 MB MALL, so every input comes from HBM;
+               ms_per_step is the mean cold step
+  warm         the same K steps back to back (wall clock between synchronisations)
+  roofline     the dominant kernel's achieved algorithmic bytes/s (or FLOP/s) per
                launch, from HIP events recorded on the launch stream, against
                MI355X's published peak
-  step_ms      p10/p50/p90 of single steps between HIP events, warm (back to back)
-               and cold (L2 and MALL evicted by a 1 GiB write before each step)
+  step_ms      p10/p50/p90 of single steps between HIP events, cold and warm
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same workload
-  kernels      per-kernel breakdown (average ms per launch, achieved rate, fraction,
-               counter-measured MFMA busy % where a record for these sources exists)
+  kernels      per-kernel breakdown of the headline workload (average ms per
+               launch, achieved rate, fraction, counter-measured MFMA busy %
+               where a record for these sources exists); chunk_cumsum is the
+               standalone cumsum step, which ssd_fwd runs inside chunk_state
+  workloads    the same forward measurements (cold and warm rates, TFLOP/s,
+               per-kernel fractions) for every one of the five workloads
   backward     ssd_bwd on the same workload (all input gradients): time per call
   decode       the decode step (one token per sequence, state carried) on its own
                seeded workload: time per launch, tokens/s and its HBM roofline
+  block        the convolution prologue and the gated forward
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
 """
@@ -149,9 +157,35 @@ def algorithmic_work(shape, esz, packed):
         "chunk_scan": dict(flops=2.0 * b * T * H * P * Q * causal + 2.0 * b * T * H * N * P,
                            bytes=2 * b * T * H * P * esz + b * T * G * N * esz + dcs + st + cbb),
     }
-    if packed:
-        w["seq_final"] = dict(flops=0.0, bytes=0)
+    if packed is not None and packed is not False:
+        w["seq_final"] = seq_final_work(shape, esz, packed)
     return w
+
+
+def seq_final_work(shape, esz, seq_idx):
+    """Algorithmic FLOPs and bytes of seq_final on a packed stream (seq_idx: the
+    host copy of the int32 ids, nseq taken from shape["nseq"]).  Per sequence
+    whose last token t_e lies in chunk c: the rows of c from the later of the
+    chunk start and the sequence start through t_e (x, B, and their delta and
+    cs), the state entering c when the sequence was already open there, and the
+    fp32 final state; every id without a token still gets its zero state
+    written."""
+    import numpy as np
+    ids = np.asarray(seq_idx)
+    H, P, N, G, Q = (shape[k] for k in ("nheads", "headdim", "dstate", "ngroups", "chunk"))
+    nseq = shape["nseq"]
+    flops, nbytes = 0.0, nseq * H * P * N * 4 + len(ids) * 4
+    change = np.flatnonzero(np.diff(ids)) + 1
+    starts = np.concatenate([[0], change])
+    ends = np.concatenate([change - 1, [len(ids) - 1]])
+    for st, te in zip(starts, ends):
+        t0 = (te // Q) * Q
+        rows = te - max(t0, st) + 1
+        flops += 2.0 * rows * H * P * N
+        nbytes += rows * (H * P * esz + G * N * esz + 2 * H * 4)
+        if st < t0:
+            nbytes += H * P * N * esz
+    return dict(flops=flops, bytes=int(nbytes))
 
 
 def run_cpu_baseline(inp, budget_s=20.0):
@@ -338,6 +372,130 @@ def run_block(dev, inp, g, reps, warmup):
                     "y * silu(z) on the plain forward's y, for comparison only"}
 
 
+def progress(msg):
+    """One line on stderr per finished phase (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def measure_forward(idx, dev, steps, warmup, kreps, flush):
+    """The forward on workload `idx`: K cold steps (each after a cache-evicting
+    write, outside its HIP events), K warm steps back to back (wall clock), and
+    the per-kernel breakdown through the per-step entry points (HIP events on
+    the launch stream around each launch, kernels in ssd_fwd's order so that the
+    caches between them are as in a real forward)."""
+    import numpy as np
+    import torch
+    from ssd_chunked_scan_amd import ssd
+    from ssd_chunked_scan_amd import workloads as wl
+
+    cfg = wl.WORKLOADS[idx]
+    t_start = time.perf_counter()
+    inp = wl.workload(idx)
+    g = inp.to(dev)
+    progress(f"workload {idx} inputs ready ({time.perf_counter() - t_start:.1f} s)")
+    nseq = inp.nseq if inp.seq_idx is not None else None
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states, g.seq_idx, nseq)
+    ws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(g.x)
+    fin = torch.empty(p.final_shape(), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states,
+                seq_idx=g.seq_idx, nseq=nseq, y=y, final_states=fin, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # cold: K steps, each after a 1 GiB write that evicts L2 and the MALL
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for r in range(steps):
+        flush.fill_(float(r))
+        pairs[r][0].record(stream)
+        step()
+        pairs[r][1].record(stream)
+    torch.cuda.synchronize()
+    cold = [a.elapsed_time(b_) for a, b_ in pairs]
+    # warm: K steps back to back, wall clock between synchronisations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t0
+    # warm single steps between events
+    wreps = min(steps, 100)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wreps)]
+    for a, b_ in pairs:
+        a.record(stream)
+        step()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    warm_ev = [a.elapsed_time(b_) for a, b_ in pairs]
+
+    # per-kernel breakdown
+    names = ["chunk_cumsum", "chunk_cb", "chunk_state", "state_passing"]
+    if inp.seq_idx is not None:
+        names.append("seq_final")
+    names.append("chunk_scan")
+    delta = torch.empty((p.b, p.H, p.nc, p.Q), dtype=torch.float32, device=dev)
+    cs = torch.empty_like(delta)
+    cb = torch.empty(p.cb_shape(), dtype=g.x.dtype, device=dev)
+    states = torch.empty((p.b, p.nc, p.H, p.P, p.N), dtype=g.x.dtype, device=dev)
+    seg_end = torch.empty((max(p.nseq, 1),), dtype=torch.int32, device=dev)
+    ybuf = torch.empty_like(g.x)
+    calls = {
+        "chunk_cumsum": lambda: ssd.chunk_cumsum(p, delta, cs),
+        "chunk_cb": lambda: ssd.chunk_cb(p, cb),
+        "chunk_state": lambda: ssd.chunk_state(p, delta, cs, cb, states),
+        "state_passing": lambda: ssd.state_passing(p, cs, states, None if inp.seq_idx is not None else fin),
+        "seq_final": lambda: ssd.seq_final_states(p, delta, cs, states, fin, seg_end),
+        "chunk_scan": lambda: ssd.chunk_scan(p, delta, cs, cb, states, ybuf),
+    }
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(kreps)] for n in names}
+    for _ in range(2):
+        for n in names:
+            calls[n]()
+    torch.cuda.synchronize()
+    for r in range(kreps):
+        for n in names:
+            ev[n][r][0].record(stream)
+            calls[n]()
+            ev[n][r][1].record(stream)
+    torch.cuda.synchronize()
+    kms = {n: sum(a.elapsed_time(b_) for a, b_ in ev[n]) / kreps for n in names}
+
+    esz = 2 if g.x.dtype == torch.bfloat16 else 4
+    shape = dict(inp.shape, nseq=nseq or 0)
+    work = algorithmic_work(shape, esz, None if inp.seq_idx is None else inp.seq_idx.numpy())
+    kernels = {}
+    for n in names:
+        kernels[n] = dict(ms=round(kms[n], 5), **roofline_point(work[n], kms[n] / 1e3, esz))
+        if work[n].get("flops"):
+            kernels[n]["mfma_busy_pct"] = measured_mfma(n, cfg["name"])
+    kernels["chunk_cumsum"]["note"] = "standalone; ssd_fwd runs this step inside chunk_state"
+    fwd_names = [n for n in names if n != "chunk_cumsum"]
+    total_flops = sum(work[n].get("flops", 0.0) for n in fwd_names)
+    cold_ms = sum(cold) / len(cold)
+    progress(f"workload {idx} forward measured ({time.perf_counter() - t_start:.1f} s)")
+    return {
+        "inp": inp, "g": g, "work": work, "names": fwd_names, "kms": kms, "esz": esz,
+        "summary": {
+            "workload": cfg["name"], "batch": inp.x.shape[0], "seqlen": inp.x.shape[1],
+            "real_tokens": inp.real_tokens,
+            "cold": {"ms": round(cold_ms, 5), **percentiles(cold),
+                     "tokens_per_s": round(inp.real_tokens * len(cold) / (sum(cold) / 1e3), 1),
+                     "tflops": round(total_flops / (cold_ms / 1e3) / 1e12, 2)},
+            "warm": {"ms": round(warm_s * 1e3 / steps, 5), **percentiles(warm_ev),
+                     "tokens_per_s": round(inp.real_tokens * steps / warm_s, 1),
+                     "tflops": round(total_flops / (warm_s / steps) / 1e12, 2)},
+            "kernels": kernels,
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +503,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
+    ap.add_argument("--only-headline", action="store_true", help="skip the other four workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
@@ -374,126 +533,69 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    kreps = max(5, min(args.steps, 50))
+    head = measure_forward(args.workload, dev, args.steps, args.warmup, kreps, flush)
+    inp, g = head["inp"], head["g"]
     cfg = wl.WORKLOADS[args.workload]
-    inp = wl.workload(args.workload)
-    g = inp.to(dev)
-    nseq = inp.nseq if inp.seq_idx is not None else None
-    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states, g.seq_idx, nseq)
-    ws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device=dev)
-    y = torch.empty_like(g.x)
-    fin = torch.empty(p.final_shape(), dtype=torch.float32, device=dev)
-
-    def step():
-        ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states,
-                seq_idx=g.seq_idx, nseq=nseq, y=y, final_states=fin, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = inp.real_tokens * args.steps / elapsed
-
-    # per-step latency: HIP events around single steps on the launch stream, warm
-    # (back to back) and cold (a 1 GiB write before each step, outside the events,
-    # evicts L2 and the 256 MB MALL)
-    stream = torch.cuda.current_stream(dev)
-    reps = max(5, min(args.steps, 100))
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    lat = {}
-    for mode in ("warm", "cold"):
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(reps)]
-        for r in range(reps):
-            if mode == "cold":
-                flush.fill_(float(r))
-            pairs[r][0].record(stream)
-            step()
-            pairs[r][1].record(stream)
-        torch.cuda.synchronize()
-        lat[mode] = [a.elapsed_time(b_) for a, b_ in pairs]
-    del flush
-    step_ms = {m: percentiles(v) for m, v in lat.items()}
-    step_ms["cold_tokens_per_s"] = round(inp.real_tokens / (step_ms["cold"]["p50"] / 1e3), 1)
-    step_ms["reps"] = reps
-
-    # per-kernel breakdown: the same kernels through the per-step entry points,
-    # bracketed by HIP events on the stream they are launched on
-    names = ["chunk_cb", "chunk_state", "state_passing"]   # the kernels ssd_fwd launches
-    if inp.seq_idx is not None:
-        names.append("seq_final")
-    names.append("chunk_scan")
-    delta = torch.empty((p.b, p.H, p.nc, p.Q), dtype=torch.float32, device=dev)
-    cs = torch.empty_like(delta)
-    cb = torch.empty(p.cb_shape(), dtype=g.x.dtype, device=dev)
-    states = torch.empty((p.b, p.nc, p.H, p.P, p.N), dtype=g.x.dtype, device=dev)
-    seg_end = torch.empty((max(p.nseq, 1),), dtype=torch.int32, device=dev)
-    ybuf = torch.empty_like(g.x)
-    calls = {
-        "chunk_cumsum": lambda: ssd.chunk_cumsum(p, delta, cs),
-        "chunk_cb": lambda: ssd.chunk_cb(p, cb),
-        "chunk_state": lambda: ssd.chunk_state(p, delta, cs, cb, states),
-        "state_passing": lambda: ssd.state_passing(p, cs, states, None if inp.seq_idx is not None else fin),
-        "seq_final": lambda: ssd.seq_final_states(p, delta, cs, states, fin, seg_end),
-        "chunk_scan": lambda: ssd.chunk_scan(p, delta, cs, cb, states, ybuf),
-    }
-    reps = max(5, min(args.steps, 50))
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)] for n in names}
-    for _ in range(2):
-        for n in names:
-            calls[n]()
-    torch.cuda.synchronize()
-    for r in range(reps):
-        for n in names:
-            ev[n][r][0].record(stream)
-            calls[n]()
-            ev[n][r][1].record(stream)
-    torch.cuda.synchronize()
-    kms = {n: sum(a.elapsed_time(b_) for a, b_ in ev[n]) / reps for n in names}
-
-    esz = 2 if g.x.dtype == torch.bfloat16 else 4
-    work = algorithmic_work(inp.shape, esz, inp.seq_idx is not None)
-    kernels = {}
-    for n in names:
-        kernels[n] = dict(ms=round(kms[n], 5), **roofline_point(work[n], kms[n] / 1e3, esz))
-        if work[n].get("flops"):
-            kernels[n]["mfma_busy_pct"] = measured_mfma(n, cfg["name"])
+    summ = head["summary"]
+    kernels = summ["kernels"]
+    names = head["names"]
+    kms = head["kms"]
     dom = max(names, key=lambda n: kms[n])
     kd = kernels[dom]
+    work = head["work"]
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
                 "unit": kd["unit"], "frac": kd["frac"], "mfma_frac": kd.get("mfma_frac"),
                 "hbm_frac": kd["hbm_frac"], "flop_per_byte": kd.get("flop_per_byte"),
                 "traffic": measured_traffic(dom, cfg["name"]), "traffic_unit": "HBM bytes per launch",
                 "algorithmic_bytes": int(work[dom]["bytes"]),
                 "mfma_busy_pct": measured_mfma(dom, cfg["name"])}
-    total_flops = sum(w.get("flops", 0.0) for w in work.values())
-    decode = None if args.no_decode else run_decode(dev, reps, 5)
-    backward = None if args.no_backward else run_backward(dev, inp, g, max(5, min(reps, 20)), 3)
-    block = None if args.no_block else run_block(dev, inp, g, max(5, min(reps, 50)), 3)
+    workloads = {}
+    for idx in sorted(wl.WORKLOADS):
+        if idx == args.workload:
+            workloads[str(idx)] = summ
+        elif not args.only_headline:
+            other = measure_forward(idx, dev, args.steps, args.warmup, kreps, flush)
+            workloads[str(idx)] = other["summary"]
+            del other
+            torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
+
+    decode = None if args.no_decode else run_decode(dev, kreps * 2, 5)
+    progress("decode measured")
+    backward = None if args.no_backward else run_backward(dev, inp, g, max(5, min(kreps, 20)), 3)
+    progress("backward measured")
+    block = None if args.no_block else run_block(dev, inp, g, kreps, 3)
+    progress("block measured")
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(inp, args.cpu_budget)
+        progress("cpu baseline measured")
 
     b, T, H, P = inp.x.shape
+    esz = head["esz"]
+    cold = summ["cold"]
     line = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": cold["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": cold["ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if esz == 2 else "f32", "data": "synthetic (seeded, see workloads.py)",
         "config": {"workload": cfg["name"], "batch": b, "seqlen": T, "nheads": H, "headdim": P,
                    "dstate": inp.B.shape[3], "ngroups": inp.B.shape[2], "chunk": inp.chunk,
                    "real_tokens": inp.real_tokens},
-        "tflops": round(total_flops / (ms_per_step / 1e3) / 1e12, 2),
+        "timing": "value and ms_per_step: the K timed steps, each cold (a 1 GiB write before it, "
+                  "outside its HIP events, evicts L2 and MALL); warm: the same K steps back to back",
+        "tflops": cold["tflops"],
+        "warm": summ["warm"],
         "roofline": roofline,
-        "step_ms": step_ms,
+        "step_ms": {"cold": {k: cold[k] for k in ("p10", "p50", "p90")},
+                    "warm": {k: summ["warm"][k] for k in ("p10", "p50", "p90")}},
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "workloads": workloads,
         "backward": backward,
         "decode": decode,
         "block": block,

@@ -75,3 +75,18 @@ def test_roofline_point_picks_the_binding_roof():
     assert bench.roofline_point({"flops": 100e9, "bytes": 1e9}, 1e-3, 4)["bound"] == "mfma"
     copy = bench.roofline_point({"bytes": 4e9}, 1e-3, 2)
     assert copy["bound"] == "hbm" and copy["frac"] == pytest.approx(0.5) and "mfma_frac" not in copy
+
+
+def test_seq_final_work_counts_each_sequences_tail_rows():
+    # chunk 4; ids 0 0 0 | 0 0 1 1 | 1 2 2 2 (nseq 4: id 3 never occurs)
+    ids = [0, 0, 0, 0, 0, 1, 1, 1, 2, 2, 2]
+    shape = dict(nheads=2, headdim=16, dstate=16, ngroups=1, chunk=4, nseq=4)
+    w = bench.seq_final_work(shape, 2, ids)
+    H, P, N, G = 2, 16, 16, 1
+    # id 0 ends at t=4 (chunk 1, open since t=0): 1 row + the entering state
+    # id 1 ends at t=7 (chunk 1, starts at t=5 inside it): 3 rows, no entering state
+    # id 2 ends at t=10 (chunk 2, starts at t=8 = chunk start): 3 rows, no entering state
+    rows = 1 + 3 + 3
+    assert w["flops"] == 2.0 * rows * H * P * N
+    want = 4 * H * P * N * 4 + len(ids) * 4 + rows * (H * P * 2 + G * N * 2 + 2 * H * 4) + H * P * N * 2
+    assert w["bytes"] == want
