@@ -86,6 +86,26 @@ __device__ __forceinline__ void store_frag(float *p, const floatx8 &v)
     *reinterpret_cast<floatx4 *>(p + 4) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
 }
 
+// A fragment with the K slots whose flag is off replaced by zero (a select, so
+// a non-finite value in a dropped slot cannot reach the product).
+__device__ __forceinline__ bf16x8 mask_frag(const bf16x8 &v, const bool (&keep)[8])
+{
+    const uint4 u = __builtin_bit_cast(uint4, v);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = w[i] & ((keep[2 * i] ? 0x0000ffffu : 0u) | (keep[2 * i + 1] ? 0xffff0000u : 0u));
+    return __builtin_bit_cast(bf16x8, uint4{o[0], o[1], o[2], o[3]});
+}
+__device__ __forceinline__ floatx8 mask_frag(const floatx8 &v, const bool (&keep)[8])
+{
+    floatx8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = keep[e] ? v[e] : 0.f;
+    return o;
+}
+
 __device__ __forceinline__ floatx8 to_f32(const bf16x8 &v) { return __builtin_convertvector(v, floatx8); }
 __device__ __forceinline__ floatx8 to_f32(const floatx8 &v) { return v; }
 

@@ -434,6 +434,8 @@ struct KTile<bf16, KR, COLS, TH> {
                     q[e] = keep ? pack_bf16x2(lo, hi) : 0u;
                 }
                 o = uint4{q[0], q[1], q[2], q[3]};
+            } else if constexpr (SEL) {
+                if (m[r] == 0) o = uint4{0u, 0u, 0u, 0u};
             }
             *reinterpret_cast<uint4 *>(dst + r * PITCH + 4 * ((2 * c) ^ swz(r))) = o;
         }
@@ -609,7 +611,7 @@ __device__ __forceinline__ void state_product(StateSmem<E, NT> &sm, const E *xsr
     for (int j = 0; j < 4; ++j) xoff[j] = XT::frag_off(j * 16);
     for (int kb = 0; kb < slen; kb += 64) {
         xs.template store<true, SEL>(sm.x, w + kb, m + kb);
-        bs.template store<false, false>(sm.b, nullptr, nullptr);
+        bs.template store<false, SEL>(sm.b, nullptr, m + kb);
         __syncthreads();
         if (kb + 64 < slen) {
             xs.load(XT::rsrc(xsrc + (int64_t)(kb + 64) * ldx, ldx, slen - kb - 64));
@@ -818,6 +820,23 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     }
     __syncthreads();
     xs.template store<true, PACKED>(xt, w, m);
+    // A chunk that holds a segment boundary keeps only its tokens a .. len-1 (ids
+    // never decrease, so the kept tokens are one run ending at the chunk's last
+    // token): the x rows before a are already zero (a select); the K steps wholly
+    // before a are skipped and the one that straddles a drops its B^T columns
+    // before a by a select, so a non-finite B of another sequence cannot reach
+    // this state.
+    int first_kept = 0;
+    if (PACKED && !GRAD) {
+        for (int s = lane; s < Q; s += 64) {   // every wave finds it on its own
+            const uint64_t kept = __ballot(m[s] != 0);
+            if (kept) {
+                first_kept = s - lane + __builtin_ctzll(kept);
+                break;
+            }
+        }
+        first_kept = __builtin_amdgcn_readfirstlane(first_kept);
+    }
     __syncthreads();
 
     floatx4 acc[NI][4];
@@ -831,13 +850,23 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         if (ks < kend) {   // wave-uniform
-            F bx[4];
+            if (PACKED && ks * 32 < first_kept) {   // wave-uniform; only in a chunk with a boundary
+                const int sb = ks * 32 + 8 * (lane >> 4);
+                bool kp[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bx[j] = XT::frag_at(xt, xoff[j], ks * 32);
+                for (int e = 0; e < 8; ++e) kp[e] = sb + e >= first_kept;
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
+                for (int i = 0; i < NI; ++i) ra[ks % RING][i] = mask_frag(ra[ks % RING][i], kp);
+            }
+            if (!PACKED || ks * 32 + 32 > first_kept) {
+                F bx[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mma(acc[i][j], ra[ks % RING][i], bx[j]);
+                for (int j = 0; j < 4; ++j) bx[j] = XT::frag_at(xt, xoff[j], ks * 32);
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mma(acc[i][j], ra[ks % RING][i], bx[j]);
+            }
         }
         if (ks + RING < NKS) {
 #pragma unroll
@@ -1467,7 +1496,36 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) xoff[pb] = XT::frag_off(pb * 16);
 
+    // Packed streams: a chunk that holds a segment boundary (block-uniform) takes
+    // selects wherever the common path relies on a zero weight, so that a
+    // non-finite x or B of one sequence cannot reach another's outputs: in step 1
+    // the x rows and CB columns of tokens outside the sub-block's segment are
+    // dropped, and the diagonal step runs once per segment among the sub-block's
+    // rows, each pass kept only for that segment's rows.
+    const bool bnd = PACKED && sq[0] != sq[max(len, 1) - 1];
+    // first_row[k]: the first row of the chunk in the segment of sub-block k's
+    // first row (boundary chunks only; 0 otherwise)
+    int first_row[NSB];
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) {
+        first_row[k] = 0;
+        if (PACKED && bnd) {   // binary search: ids never decrease along the chunk
+            const int tj = 16 * jb[k], sj = sq[tj];
+            int lo = 0, hi = tj;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (__builtin_amdgcn_readfirstlane(sq[mid]) < sj) lo = mid + 1;
+                else hi = mid;
+            }
+            first_row[k] = lo;
+        }
+    }
+
     // ---- step 1, the K steps strictly below each sub-block's diagonal step ----
+    // In a chunk with a segment boundary, the K steps before the start of the
+    // segment of the sub-block's first row (first_row) contribute nothing: the
+    // ones wholly before it are skipped, and the one that straddles it is done
+    // after the loop with selects.
 #pragma unroll
     for (int ks = 0; ks < KSB; ++ks) {
         F a[4];
@@ -1477,6 +1535,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
         for (int k = 0; k < NSB; ++k) {
             const int j = jb[k];
             if (ks >= (j >> 1) || !live[k]) continue;
+            if (PACKED && ks * 32 < first_row[k]) continue;   // wave-uniform; 0 without a boundary
             const float *vrow = vt + vt_offset(j) + ks * 32 + 8 * lg;
             const floatx4 v0 = *reinterpret_cast<const floatx4 *>(vrow);
             const floatx4 v1 = *reinterpret_cast<const floatx4 *>(vrow + 4);
@@ -1488,6 +1547,32 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
         if (ks + RING < KSB) {
 #pragma unroll
             for (int k = 0; k < NSB; ++k) bload_frag(cbrs, cb_off(k, ks + RING), cr[ks % RING][k]);
+        }
+    }
+    if (PACKED && bnd) {
+        // The straddling K step: the x rows and CB columns before first_row are
+        // dropped by selects (its CB fragment is fetched again here).
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+            const int j = jb[k], ks = first_row[k] >> 5;
+            if (!live[k] || ks * 32 == first_row[k] || ks >= (j >> 1)) continue;   // wave-uniform
+            F cbf;
+            bload_frag(cbrs, cb_off(k, ks), cbf);
+            const float *vrow = vt + vt_offset(j) + ks * 32 + 8 * lg;
+            const floatx4 v0 = *reinterpret_cast<const floatx4 *>(vrow);
+            const floatx4 v1 = *reinterpret_cast<const floatx4 *>(vrow + 4);
+            const int sb = ks * 32 + 8 * lg;
+            bool kp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kp[e] = sb + e >= first_row[k];
+            const floatx8 cf = to_f32(cbf);
+            floatx8 wf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wf[e] = kp[e] ? cf[e] * (e < 4 ? v0[e] : v1[e - 4]) : 0.f;
+            const F wfr = from_f32<F>(wf);
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+                mma(acc[k][pb], mask_frag(XT::frag_at(xt, xoff[pb], ks * 32), kp), wfr);
         }
     }
 
@@ -1530,6 +1615,39 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
             wf[e] = (ok ? cf[e] * exp2_(cst - csv[e]) * dv[e] : 0.f) + (e == rel ? Dh : 0.f);
         }
         const F wfr = from_f32<F>(wf);
+        if (PACKED && bnd && sq[ks * 32] != sq[ks * 32 + 31]) {   // wave-uniform
+            // The K step holds a segment boundary: one pass per segment id sig among
+            // rows tj .. tj+15 (ids never decrease along the chunk; rows past the end
+            // repeat the last id), with the x slots of other segments dropped, each
+            // pass kept for the rows of sig only (one p block at a time)
+            // Each pass covers the rows lo .. hi of one id (a contiguous run, found
+            // from the per-lane ids by ballots; everything here is wave-uniform).
+            const int sid = sq[t];
+            int lo = tj;
+            while (lo < tj + 16) {
+                const int sig = __builtin_amdgcn_readfirstlane(sq[lo]);
+                const uint64_t later = __ballot(sid > sig) & 0xffffull;
+                const int hi = later ? tj + __builtin_ctzll(later) - 1 : tj + 15;
+                // the K slots of this id: rows of sig before tj lie in the same K
+                // step only when tj is its second half, and the id may run on past
+                // hi into the K step's second half
+                const uint64_t ks_in = __ballot(lane < 32 && sq[ks * 32 + (lane & 31)] == sig);
+                const int slo = ks * 32 + __builtin_ctzll(ks_in), shi = ks * 32 + 63 - __builtin_clzll(ks_in);
+                bool kp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kp[e] = sb + e >= slo && sb + e <= shi;
+                const bool mine = t >= lo && t <= hi;
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    floatx4 tmp = floatx4{0.f, 0.f, 0.f, 0.f};
+                    mma(tmp, mask_frag(XT::frag_at(xt, xoff[pb], ks * 32), kp), wfr);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[k][pb][q] += mine ? tmp[q] : 0.f;
+                }
+                lo = hi + 1;
+            }
+            continue;
+        }
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) mma(acc[k][pb], XT::frag_at(xt, xoff[pb], ks * 32), wfr);
     }

@@ -293,6 +293,60 @@ def test_nan_isolation_across_chunk_aligned_sequences():
     assert not torch.isfinite(y1[0, ~keep]).all()
 
 
+def _poisoned_run(dtype, Q, what, lengths, seq, pos, seed=14):
+    """A packed stream whose boundaries mostly fall inside chunks, run clean and
+    with one non-finite input (x, B or dt) at token `pos` of sequence `seq`."""
+    T = sum(lengths)
+    H, P, N, G = 4, 32, 32, 2
+    ids = np.concatenate([np.full(L, i) for i, L in enumerate(lengths)]).astype(np.int32)
+    base = small(dtype, T, H=H, P=P, N=N, G=G, b=1, seed=seed, init_std=0.3)
+    inp = wl.Inputs(base.x, base.dt, base.A, base.B, base.C, base.D, base.initial_states,
+                    torch.from_numpy(ids), len(lengths), Q, lengths=lengths)
+    y0, f0 = run_gpu(inp)
+    t = int(np.cumsum([0] + lengths)[seq]) + pos
+    x, B, dt = inp.x.clone(), inp.B.clone(), inp.dt.clone()
+    if what == "x":
+        x[0, t, 1, 3] = float("nan")
+    elif what == "x_inf":
+        x[0, t, 2, 0] = float("inf")
+    elif what == "B":
+        B[0, t, 1, 5] = float("nan")
+    else:
+        dt[0, t, 0] = float("nan")
+    bad = wl.Inputs(x, dt, inp.A, B, inp.C, inp.D, inp.initial_states, inp.seq_idx, inp.nseq, Q,
+                    lengths=lengths)
+    y1, f1 = run_gpu(bad)
+    return ids, t, y0, f0, y1, f1
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("Q", [64, 128, 256])
+@pytest.mark.parametrize("what", ["x", "x_inf", "B", "dt"])
+def test_nan_isolation_mid_chunk_boundaries(dtype, Q, what):
+    """A NaN or Inf in x, B or dt inside one packed sequence, with sequence
+    boundaries inside chunks (several sequences share a chunk, some shorter than a
+    K step): every other sequence's outputs and final state are bit-identical to
+    the clean run, and the poisoned sequence's final state is not finite.  (The
+    state reset at a boundary is a select, and the GPU path drops the tokens of
+    other sequences by selects wherever it would otherwise multiply them by a zero
+    weight.)"""
+    lengths = [37, 90, 5, 61, 140, 23, 9, 200]
+    for seq, pos in ((3, 10), (4, 0), (3, 60), (2, 2), (7, 150)):
+        _log(f"[nan mid-chunk] dtype={dtype} Q={Q} {what} in sequence {seq} at +{pos}")
+        ids, t, y0, f0, y1, f1 = _poisoned_run(dtype, Q, what, lengths, seq, pos)
+        keep = torch.from_numpy(ids != seq).cuda()
+        assert torch.equal(y1[0, keep], y0[0, keep]), (seq, pos)
+        for k in range(len(lengths)):
+            if k != seq:
+                assert torch.equal(f1[k], f0[k]), (seq, pos, k)
+        assert not torch.isfinite(f1[seq]).all()
+        # the poisoned sequence before the poisoned token's 32-token block (chunks
+        # start at multiples of 32) is untouched too
+        start = int(np.cumsum([0] + lengths)[seq])
+        clean_to = max(start, (t // 32) * 32)
+        assert torch.equal(y1[0, start:clean_to], y0[0, start:clean_to])
+
+
 # ---------------------------------------------------------------------------
 # per-step pins against oracle intermediates
 # ---------------------------------------------------------------------------
