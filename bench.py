@@ -21,7 +21,8 @@ input already resident in HBM.  Prints ONE JSON line:
                standalone cumsum step, which ssd_fwd runs inside chunk_state
   workloads    the same forward measurements (cold and warm rates, TFLOP/s,
                per-kernel fractions) for every one of the five workloads
-  backward     ssd_bwd on the same workload (all input gradients): time per call
+  backward     ssd_bwd on the same workload (all input gradients): time per call;
+               backward_packed the same on the packed workload
   decode       the decode step (one token per sequence, state carried) on its own
                seeded workload: time per launch, tokens/s and its HBM roofline
   block        the convolution prologue and the gated forward
@@ -236,30 +237,36 @@ def run_backward(dev, inp, g, reps, warmup):
     from ssd_chunked_scan_amd import ssd
 
     nseq = inp.nseq if inp.seq_idx is not None else None
-    if nseq is not None:
-        return None   # the backward takes no packed streams
-    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states)
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, inp.chunk, g.D, g.initial_states, g.seq_idx, nseq)
     fws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device=dev)
-    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states, workspace=fws)
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states, seq_idx=g.seq_idx,
+                   nseq=nseq, workspace=fws)
     rng = np.random.default_rng(7)
     dy = torch.from_numpy(rng.standard_normal(tuple(inp.x.shape)).astype(np.float32)).to(dev).to(g.x.dtype)
-    b, T, H, P = inp.x.shape
-    N = inp.B.shape[3]
-    dfin = torch.from_numpy(rng.standard_normal((b, H, P, N)).astype(np.float32)).to(dev)
+    dfin = torch.from_numpy(rng.standard_normal(p.final_shape()).astype(np.float32)).to(dev)
     ws = torch.empty(ssd.bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    kw = dict(D=g.D, initial_states=g.initial_states, dfinal_states=dfin, workspace=ws)
+    kw = dict(D=g.D, initial_states=g.initial_states, dfinal_states=dfin, workspace=ws, seq_idx=g.seq_idx,
+              nseq=nseq)
     grads = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, **kw)
     stream = torch.cuda.current_stream(dev)
-    saved = _event_ms(lambda: ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, grads=grads, fwd_workspace=fws,
-                                      **kw), reps, warmup, stream)
     recomp = _event_ms(lambda: ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, grads=grads, **kw),
                        reps, warmup, stream)
-    avg, avg_r = sum(saved) / len(saved), sum(recomp) / len(recomp)
-    return {"ms": round(avg, 5), "step_ms": percentiles(saved), "tokens_per_s": round(inp.real_tokens / (avg / 1e3), 1),
-            "ms_recompute": round(avg_r, 5), "step_ms_recompute": percentiles(recomp),
-            "workspace_bytes": int(ws.numel()),
-            "note": "all input gradients; ms reads the forward's chunk intermediates from that forward's "
-                    "workspace, ms_recompute recomputes them inside"}
+    avg_r = sum(recomp) / len(recomp)
+    out = {"workload": inp.name, "real_tokens": inp.real_tokens, "ms_recompute": round(avg_r, 5),
+           "step_ms_recompute": percentiles(recomp), "workspace_bytes": int(ws.numel())}
+    if nseq is None:
+        saved = _event_ms(lambda: ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, grads=grads,
+                                          fwd_workspace=fws, **kw), reps, warmup, stream)
+        avg = sum(saved) / len(saved)
+        out.update(ms=round(avg, 5), step_ms=percentiles(saved),
+                   tokens_per_s=round(inp.real_tokens / (avg / 1e3), 1),
+                   note="all input gradients; ms reads the forward's chunk intermediates from that forward's "
+                        "workspace, ms_recompute recomputes them inside")
+    else:
+        out.update(ms=round(avg_r, 5), tokens_per_s=round(inp.real_tokens / (avg_r / 1e3), 1),
+                   note="all input gradients of a packed stream: the stream is laid out again with every "
+                        "sequence starting at a chunk start, and the chunk intermediates recomputed there")
+    return out
 
 
 def run_decode(dev, reps, warmup):
@@ -566,6 +573,11 @@ def main():
     decode = None if args.no_decode else run_decode(dev, kreps * 2, 5)
     progress("decode measured")
     backward = None if args.no_backward else run_backward(dev, inp, g, max(5, min(kreps, 20)), 3)
+    backward_packed = None
+    if not args.no_backward and not args.only_headline and wl.WORKLOADS[args.workload].get("packed") is None:
+        pk = wl.workload(4)
+        backward_packed = run_backward(dev, pk, pk.to(dev), max(5, min(kreps, 20)), 3)
+        del pk
     progress("backward measured")
     block = None if args.no_block else run_block(dev, inp, g, kreps, 3)
     progress("block measured")
@@ -597,6 +609,7 @@ def main():
         "kernels": kernels,
         "workloads": workloads,
         "backward": backward,
+        "backward_packed": backward_packed,
         "decode": decode,
         "block": block,
     }

@@ -239,10 +239,9 @@ ssd_status ssd_step(const ssd_step_args *args, void *stream);
 
 /*
  * Backward: the gradients of L = sum(y * dy) + sum(final_states * dfinal) with
- * respect to every input of ssd_fwd, for a forward WITHOUT seq_idx (packed
- * streams return SSD_ERR_SEQ_IDX).  The pages give no backward equations; these
- * are the chain rule applied to the recurrence at the top of this header,
- * organised by chunks like the forward:
+ * respect to every input of ssd_fwd, with or without seq_idx.  The pages give no
+ * backward equations; these are the chain rule applied to the recurrence at the
+ * top of this header, organised by chunks like the forward:
  *
  *   g_t = dL/dh_t,  dx_t = Delta_t g_t B_t + D dy_t,  dB_t = sum_heads Delta_t g_t^T x_t,
  *   dC_t = sum_heads h_t^T dy_t,  dDelta_t = x_t.(g_t B_t) + A dl_t with
@@ -250,7 +249,7 @@ ssd_status ssd_step(const ssd_step_args *args, void *stream);
  *   dA = sum Delta dl,  dD = sum dy.x,  dinit = a_0 g_0.
  *
  * `args` describes the forward exactly as it was run (shape, dtype, x, dt, A, B,
- * C, D, initial_states; seq_idx NULL) and args->y must hold its output y (an
+ * C, D, initial_states, seq_idx and nseq) and args->y must hold its output y (an
  * input here).  Its final_states, workspace and workspace_bytes fields are
  * ignored.  The forward's chunk intermediates (Delta, cs, CB and the states
  * entering each chunk) are recomputed in the backward's own workspace, unless
@@ -259,10 +258,20 @@ ssd_status ssd_step(const ssd_step_args *args, void *stream);
  * since.  The backward then reads them from there (it never writes to it), and
  * its own workspace's slots for them go unused.  Nothing checks that the
  * workspace really holds them.
+ *
+ * Packed streams (seq_idx, batch 1; the state reset at every boundary of
+ * section 4.2 of "Transformers与SSMs的隐藏联系"): dfinal_states is [nseq,H,P,N],
+ * the gradient of each segment's final state (rows of ids that never occur are
+ * not read as anything but zero gradients).  The backward copies the stream
+ * into its workspace laid out so that every segment starts at a chunk start
+ * (each segment followed by padding tokens with x = B = C = dy = 0 and a zero
+ * step size, up to the next multiple of the chunk), runs the chunked backward
+ * there with the carry cut between segments and each segment's dfinal entering
+ * at its last chunk, and copies the gradients back; fwd_workspace is not read.
  */
 typedef struct {
     const void *dy;                /* [b,T,H,P] dtype */
-    const float *dfinal_states;    /* [b,H,P,N] fp32, or NULL for zero */
+    const float *dfinal_states;    /* [b,H,P,N] fp32 (with seq_idx [nseq,H,P,N]), or NULL for zero */
     void *dx;                      /* [b,T,H,P] dtype, out */
     void *ddt;                     /* [b,T,H]   dtype, out (gradient with respect to dt as passed) */
     float *dA;                     /* [H] fp32, out */
@@ -272,12 +281,13 @@ typedef struct {
     float *dinitial_states;        /* [b,H,P,N] fp32, out, or NULL */
     void *workspace;               /* device scratch, >= ssd_bwd_workspace_size */
     size_t workspace_bytes;
-    const void *fwd_workspace;     /* the forward's workspace (see above), or NULL to recompute */
+    const void *fwd_workspace;     /* the forward's workspace (see above), or NULL to recompute;
+                                      not read with seq_idx */
     size_t fwd_workspace_bytes;    /* >= ssd_fwd_workspace_size when fwd_workspace is given */
 } ssd_bwd_args;
 
 /* Workspace bytes ssd_bwd needs for the forward problem `args` (shape and dtype
- * fields only). */
+ * fields, and seq_idx != NULL with nseq). */
 ssd_status ssd_bwd_workspace_size(const ssd_fwd_args *args, size_t *bytes);
 
 /* The backward pass.  All outputs are overwritten; gradients summed over heads

@@ -227,16 +227,18 @@ ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float 
     });
 }
 
+// cseg: the per-chunk segment ids of a stream whose segments start at chunk
+// starts (the packed backward's layout; seq_idx is then not read), or NULL.
 template <typename E>
 ssd_status run_passing(const Shape &s, const ssd_fwd_args *a, const float *cs, E *states, float *final_states,
-                       hipStream_t st)
+                       hipStream_t st, const int32_t *cseg = nullptr)
 {
     const int64_t PN = s.P * s.N;   // a multiple of 256
     constexpr int VE = 4;            // elements per thread
     const int64_t vecs = s.b * s.H * PN / VE;
     hipLaunchKernelGGL((k_state_passing<E, VE>), dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, states, cs,
-                       a->initial_states, final_states, a->seq_idx, (int)s.T, (int)s.H, PN, (int)s.nc, (int)s.Q,
-                       vecs);
+                       a->initial_states, final_states, cseg ? nullptr : a->seq_idx, (int)s.T, (int)s.H, PN,
+                       (int)s.nc, (int)s.Q, vecs, (const E *)nullptr, (float *)nullptr, cseg);
     return launched();
 }
 
@@ -477,20 +479,23 @@ ssd_status run_state_grad(const Shape &s, const ssd_fwd_args *ar, const float *c
 
 template <typename E>
 ssd_status run_passing_rev(const Shape &s, const float *cs, E *gstates, const float *dfinal, float *dinit,
-                           const E *hin, float *bnd_part, hipStream_t st)
+                           const E *hin, float *bnd_part, hipStream_t st, const int32_t *cseg = nullptr)
 {
     const int64_t PN = s.P * s.N;
     constexpr int VE = 4;   // so PN / (64 VE) = PN / 256 boundary partials per (b, h, c)
     const int64_t vecs = s.b * s.H * PN / VE;
     hipLaunchKernelGGL((k_state_passing<E, VE, true>), dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, gstates,
                        cs, dfinal, dinit, (const int32_t *)nullptr, (int)s.T, (int)s.H, PN, (int)s.nc, (int)s.Q,
-                       vecs, hin, bnd_part);
+                       vecs, hin, bnd_part, cseg);
     return launched();
 }
 
+// cseg (packed streams, on the layout in which every segment starts at a chunk
+// start): the per-chunk segment ids; g->dfinal_states is then [nseq,H,P,N] and
+// g->fwd_workspace is not used.
 template <typename E>
 ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *g, const BwdWorkspace &w,
-                     hipStream_t st)
+                     hipStream_t st, const int32_t *cseg = nullptr)
 {
     char *ws = static_cast<char *>(g->workspace);
     auto F32 = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
@@ -503,7 +508,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     ssd_status r;
     ssd_fwd_args f = *a;
     f.final_states = nullptr;
-    if (g->fwd_workspace) {
+    if (g->fwd_workspace && !cseg) {
         // 1. the forward's chunk intermediates, as its own call left them (read only)
         const Workspace fw = workspace_layout(s);
         char *fws = const_cast<char *>(static_cast<const char *>(g->fwd_workspace));
@@ -515,7 +520,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
         if ((r = run_cb<E>(s, &f, cb, st)) != SSD_OK) return r;
         if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st)) != SSD_OK) return r;
-        if ((r = run_passing<E>(s, &f, cs, states, nullptr, st)) != SSD_OK) return r;
+        if ((r = run_passing<E>(s, &f, cs, states, nullptr, st, cseg)) != SSD_OK) return r;
     }
     // 2. every chunk's tokens in reversed order: B, C, and the reversed cs / delta
     //    (dy is read reversed by the kernels themselves)
@@ -543,7 +548,8 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
     if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st)) != SSD_OK) return r;
     //    (with the boundary terms e^{cs_last} <G_c, Hin_c> of dl, as partial sums)
-    if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, states, bnd, st)) != SSD_OK)
+    if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, states, bnd, st, cseg)) !=
+        SSD_OK)
         return r;
     // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y';
     //    it writes dx = Delta y' + D dy, and dy . x per (token, head)
@@ -587,6 +593,121 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
                            (int)s.G, (int)s.P, (int)s.N, (int)s.nc, nnt);
         return launched();
     });
+}
+
+// ---------------------------------------------------------------------------
+// backward of a packed stream
+// ---------------------------------------------------------------------------
+// The stream is copied to a layout in which every segment starts at a chunk
+// start (k_bwd_seg_ranges, k_bwd_pad_map), the chunked backward runs there with
+// the state carry cut between segments and each segment's final-state gradient
+// entering at its last chunk, and the gradients are copied back.  Tp bounds the
+// padded length from the host side: each of at most nseq segments adds fewer
+// than Q tokens of padding.
+struct PackedBwd {
+    Shape sp;   // the padded problem (batch 1, no seq_idx)
+    size_t seg_end, ostart, len, pstart, pos_src, cseg, ppos, xp, dyp, dtp, bp, cp, dxp, ddtp, dbp, dcp, inner, total;
+    BwdWorkspace w;
+};
+
+PackedBwd packed_bwd_layout(const Shape &s)
+{
+    PackedBwd k;
+    k.sp = s;
+    k.sp.packed = false;
+    k.sp.nseq = 0;
+    const int64_t tp = ((s.T + s.nseq * (s.Q - 1)) + s.Q - 1) / s.Q * s.Q;
+    k.sp.T = tp;
+    k.sp.nc = tp / s.Q;
+    const size_t xs = (size_t)(tp * s.H * s.P) * s.esz, ds = (size_t)(tp * s.H) * s.esz,
+                 bs = (size_t)(tp * s.G * s.N) * s.esz, ids = (size_t)s.nseq * 4;
+    size_t o = 0;
+    auto take = [&](size_t n) { const size_t at = o; o = align256(o + n); return at; };
+    k.seg_end = take(ids);
+    k.ostart = take(ids);
+    k.len = take(ids);
+    k.pstart = take(ids);
+    k.pos_src = take((size_t)tp * 4);
+    k.cseg = take((size_t)k.sp.nc * 4);
+    k.ppos = take((size_t)s.T * 4);
+    k.xp = take(xs);
+    k.dyp = take(xs);
+    k.dtp = take(ds);
+    k.bp = take(bs);
+    k.cp = take(bs);
+    k.dxp = take(xs);
+    k.ddtp = take(ds);
+    k.dbp = take(bs);
+    k.dcp = take(bs);
+    k.inner = o;
+    k.w = bwd_workspace_layout(k.sp);
+    k.total = align256(o + k.w.total);
+    return k;
+}
+
+template <typename E>
+ssd_status bwd_packed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *g, const PackedBwd &k,
+                      hipStream_t st)
+{
+    char *ws = static_cast<char *>(g->workspace);
+    auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
+    auto EP = [&](size_t off) { return reinterpret_cast<E *>(ws + off); };
+    const int T = (int)s.T, Q = (int)s.Q, nseq = (int)s.nseq, Tp = (int)k.sp.T;
+    int32_t *seg_end = I32(k.seg_end), *ostart = I32(k.ostart), *len = I32(k.len), *pstart = I32(k.pstart);
+    int32_t *pos_src = I32(k.pos_src), *cseg = I32(k.cseg), *ppos = I32(k.ppos);
+    // the padded layout
+    hipLaunchKernelGGL(k_seg_end, dim3(grid1(T, 256)), dim3(256), 0, st, a->seq_idx, seg_end, T, nseq);
+    hipLaunchKernelGGL(k_bwd_seg_ranges, dim3(1), dim3(64), 0, st, seg_end, ostart, len, pstart, nseq, Q);
+    hipLaunchKernelGGL(k_bwd_pad_map, dim3(grid1(Tp, 256)), dim3(256), 0, st, ostart, len, pstart, pos_src, cseg,
+                       nseq, Q, Tp);
+    hipLaunchKernelGGL(k_bwd_unpad_map, dim3(grid1(T, 256)), dim3(256), 0, st, a->seq_idx, ostart, pstart, ppos, T,
+                       nseq);
+    if (launched() != SSD_OK) return SSD_ERR_HIP;
+    const int64_t HP = s.H * s.P, GN = s.G * s.N;
+    constexpr int V = kVec16<E>;
+    auto rows = [&](const void *src, void *dst, const int32_t *map, int64_t R, int64_t nrows) {
+        const int64_t nv = nrows * R / V;
+        hipLaunchKernelGGL(k_gather_rows<E>, dim3(grid1(nv, 256)), dim3(256), 0, st, (const E *)src, (E *)dst, map,
+                           R, nv);
+    };
+    auto elems = [&](const void *src, void *dst, const int32_t *map, int64_t R, int64_t nrows, float fill) {
+        hipLaunchKernelGGL(k_gather_elems<E>, dim3(grid1(nrows * R, 256)), dim3(256), 0, st, (const E *)src,
+                           (E *)dst, map, R, nrows * R, fill);
+    };
+    rows(a->x, EP(k.xp), pos_src, HP, Tp);
+    rows(g->dy, EP(k.dyp), pos_src, HP, Tp);
+    rows(a->B, EP(k.bp), pos_src, GN, Tp);
+    rows(a->C, EP(k.cp), pos_src, GN, Tp);
+    // padding takes a zero step size: softplus(-inf) = 0
+    elems(a->dt, EP(k.dtp), pos_src, s.H, Tp, a->dt_softplus ? -__builtin_huge_valf() : 0.f);
+    if (launched() != SSD_OK) return SSD_ERR_HIP;
+    // the chunked backward on the padded stream
+    ssd_fwd_args fp = *a;
+    fp.seqlen = Tp;
+    fp.x = EP(k.xp);
+    fp.dt = EP(k.dtp);
+    fp.B = EP(k.bp);
+    fp.C = EP(k.cp);
+    fp.seq_idx = nullptr;
+    fp.nseq = 0;
+    fp.y = nullptr;
+    ssd_bwd_args gp = *g;
+    gp.dy = EP(k.dyp);
+    gp.dx = EP(k.dxp);
+    gp.ddt = EP(k.ddtp);
+    gp.dB = EP(k.dbp);
+    gp.dC = EP(k.dcp);
+    gp.workspace = ws + k.inner;
+    gp.workspace_bytes = k.w.total;
+    gp.fwd_workspace = nullptr;
+    ssd_status r = bwd_typed<E>(k.sp, &fp, &gp, k.w, st, cseg);
+    if (r != SSD_OK) return r;
+    // back to the original positions
+    rows(EP(k.dxp), g->dx, ppos, HP, T);
+    rows(EP(k.dbp), g->dB, ppos, GN, T);
+    rows(EP(k.dcp), g->dC, ppos, GN, T);
+    elems(EP(k.ddtp), g->ddt, ppos, s.H, T, 0.f);
+    return launched();
 }
 
 // ---------------------------------------------------------------------------
@@ -826,9 +947,8 @@ ssd_status ssd_bwd_workspace_size(const ssd_fwd_args *args, size_t *bytes)
     Shape s;
     ssd_status r = parse_shape(args, &s);
     if (r != SSD_OK) return r;
-    if (s.packed) return SSD_ERR_SEQ_IDX;
     if (!bytes) return SSD_ERR_NULL_POINTER;
-    *bytes = bwd_workspace_layout(s).total;
+    *bytes = s.packed ? packed_bwd_layout(s).total : bwd_workspace_layout(s).total;
     return SSD_OK;
 }
 
@@ -837,7 +957,6 @@ ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream
     Shape s;
     ssd_status r = parse_shape(args, &s);
     if (r != SSD_OK) return r;
-    if (s.packed) return SSD_ERR_SEQ_IDX;
     if (!g) return SSD_ERR_NULL_POINTER;
     if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB | kNeedC)) != SSD_OK) return r;
     const bool empty = s.T == 0;
@@ -848,19 +967,22 @@ ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
     const Sizes z = tensor_sizes(s);
-    const size_t st = (size_t)(s.b * s.H * s.P * s.N) * 4;
-    const BwdWorkspace w = bwd_workspace_layout(s);
+    const size_t st = (size_t)(s.b * s.H * s.P * s.N) * 4;   // dinitial_states
+    // packed streams: the backward always recomputes on its own layout, so a
+    // forward workspace is not read
+    const void *fwd_ws = s.packed ? nullptr : g->fwd_workspace;
+    const size_t wtotal = s.packed ? packed_bwd_layout(s).total : bwd_workspace_layout(s).total;
     const size_t fws = workspace_layout(s).total;
     if (!empty) {
         if (!g->workspace) return SSD_ERR_NULL_POINTER;
-        if (g->workspace_bytes < w.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
-        if (g->fwd_workspace && g->fwd_workspace_bytes < fws) return SSD_ERR_WORKSPACE_TOO_SMALL;
+        if (g->workspace_bytes < wtotal) return SSD_ERR_WORKSPACE_TOO_SMALL;
+        if (fwd_ws && g->fwd_workspace_bytes < fws) return SSD_ERR_WORKSPACE_TOO_SMALL;
     }
     const Range ins[] = {{args->x, z.x}, {args->dt, z.dt}, {args->A, z.A}, {args->B, z.bc}, {args->C, z.bc},
-                         {args->D, z.D}, {args->initial_states, z.init}, {args->y, z.y}, {g->dy, z.x},
-                         {g->dfinal_states, st}, {g->fwd_workspace, fws}};
+                         {args->D, z.D}, {args->initial_states, z.init}, {args->seq_idx, z.seq}, {args->y, z.y},
+                         {g->dy, z.x}, {g->dfinal_states, z.fin}, {fwd_ws, fws}};
     const Range outs[] = {{g->dx, z.x}, {g->ddt, z.dt}, {g->dA, z.A}, {g->dB, z.bc}, {g->dC, z.bc},
-                          {g->dD, z.D}, {g->dinitial_states, st}, {empty ? nullptr : g->workspace, w.total}};
+                          {g->dD, z.D}, {g->dinitial_states, st}, {empty ? nullptr : g->workspace, wtotal}};
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
         for (const Range &in : ins)
             if (overlaps(outs[i], in)) return SSD_ERR_ALIASING;
@@ -873,11 +995,17 @@ ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream
         hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dA, (const float *)nullptr, s.H);
         if (g->dD)
             hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dD, (const float *)nullptr, s.H);
+        // (an empty packed stream has no segment that could receive the initial state)
         if (g->dinitial_states)
             hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.b * s.H * s.P * s.N, 256)), dim3(256), 0, hs,
-                               g->dinitial_states, g->dfinal_states, s.b * s.H * s.P * s.N);
+                               g->dinitial_states, s.packed ? nullptr : g->dfinal_states, s.b * s.H * s.P * s.N);
         return launched();
     }
+    if (s.packed) {
+        const PackedBwd k = packed_bwd_layout(s);
+        return s.dtype == SSD_DTYPE_BF16 ? bwd_packed<bf16>(s, args, g, k, hs) : bwd_packed<float>(s, args, g, k, hs);
+    }
+    const BwdWorkspace w = bwd_workspace_layout(s);
     return s.dtype == SSD_DTYPE_BF16 ? bwd_typed<bf16>(s, args, g, w, hs) : bwd_typed<float>(s, args, g, w, hs);
 }
 

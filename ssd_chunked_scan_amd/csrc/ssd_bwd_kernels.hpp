@@ -74,6 +74,117 @@ __global__ void k_bwd_reverse_cs(const float *__restrict__ cs, float *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// packed streams: a layout in which every segment starts at a chunk start
+// ---------------------------------------------------------------------------
+// The backward of a packed stream runs on a copy of the stream laid out so that
+// every segment occupies whole chunks: segment s (in id order) starts at padded
+// position pstart[s], a multiple of Q, and is followed by padding up to the next
+// multiple of Q.  Padding tokens have x = B = C = dy = 0 and a step size of zero,
+// so they leave the state unchanged and contribute nothing; the state carry is
+// cut where a chunk starts a new segment.  Positions past the last segment form
+// chunks of no segment (id -1).
+
+// From seg_end (the last position of every id, -1 for an id that never occurs;
+// ids never decrease along the stream): ostart[s] = the first position of s,
+// len[s] its token count, pstart[s] its start in the padded layout.  One wave,
+// ids in blocks of 64 with running carries.
+__global__ void k_bwd_seg_ranges(const int32_t *__restrict__ seg_end, int32_t *__restrict__ ostart,
+                                 int32_t *__restrict__ len, int32_t *__restrict__ pstart, int nseq, int Q)
+{
+    const int lane = threadIdx.x;
+    int end_before = -1;   // the largest last position of the ids below the block
+    int64_t pad_before = 0;
+    for (int base = 0; base < nseq; base += 64) {
+        const int s = base + lane;
+        const int e = s < nseq ? seg_end[s] : -1;
+        // inclusive max-scan of e and sum-scan of the padded lengths over the block
+        int mx = e;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(mx, o);
+            if (lane >= o) mx = max(mx, u);
+        }
+        const int up = __shfl_up(mx, 1);
+        const int first = 1 + max(end_before, lane > 0 ? up : -1);   // one past every earlier id's end
+        const int n = e >= 0 ? e - first + 1 : 0;
+        int64_t pad = (int64_t)((n + Q - 1) / Q) * Q;
+        int64_t ps = pad;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t u = __shfl_up(ps, o);
+            if (lane >= o) ps += u;
+        }
+        if (s < nseq) {
+            ostart[s] = first;
+            len[s] = n;
+            pstart[s] = (int32_t)(pad_before + ps - pad);
+        }
+        end_before = max(end_before, __shfl(mx, 63));
+        pad_before += __shfl(ps, 63);
+    }
+}
+
+// pos_src[pp] = the original position at padded position pp (-1 for padding), and
+// cseg[pp / Q] = the segment of every padded chunk (-1 past the last segment).
+// The segment of pp is the last id whose padded start is <= pp (a binary search;
+// an id without tokens has the same start as the next one).
+__global__ void k_bwd_pad_map(const int32_t *__restrict__ ostart, const int32_t *__restrict__ len,
+                              const int32_t *__restrict__ pstart, int32_t *__restrict__ pos_src,
+                              int32_t *__restrict__ cseg, int nseq, int Q, int Tp)
+{
+    const int pp = blockIdx.x * blockDim.x + threadIdx.x;
+    if (pp >= Tp) return;
+    int lo = 0, hi = nseq - 1;   // the last s with pstart[s] <= pp (pstart[0] = 0)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pstart[mid] <= pp) lo = mid;
+        else hi = mid - 1;
+    }
+    const int off = pp - pstart[lo], n = len[lo];
+    const int padded = (n + Q - 1) / Q * Q;
+    pos_src[pp] = off < n ? ostart[lo] + off : -1;
+    if (pp % Q == 0) cseg[pp / Q] = off < padded ? lo : -1;
+}
+
+// ppos[t] = the padded position of original position t.
+__global__ void k_bwd_unpad_map(const int32_t *__restrict__ seq_idx, const int32_t *__restrict__ ostart,
+                                const int32_t *__restrict__ pstart, int32_t *__restrict__ ppos, int T, int nseq)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    const int s = min(max(seq_idx[t], 0), nseq - 1);
+    ppos[t] = pstart[s] + t - ostart[s];
+}
+
+// dst row r = src row map[r] (rows of R elements, R * sizeof(E) a multiple of 16
+// bytes), or zero where map[r] < 0.
+template <typename E>
+__global__ void k_gather_rows(const E *__restrict__ src, E *__restrict__ dst, const int32_t *__restrict__ map,
+                              int64_t R, int64_t total_vecs)
+{
+    constexpr int V = kVec16<E>;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total_vecs) return;
+    const int64_t vpr = R / V, r = i / vpr, v = i % vpr;
+    const int m = map[r];
+    uint4 val{0u, 0u, 0u, 0u};
+    if (m >= 0) val = *reinterpret_cast<const uint4 *>(src + (int64_t)m * R + v * V);
+    *reinterpret_cast<uint4 *>(dst + r * R + v * V) = val;
+}
+
+// The same one element at a time, with `fill` where map[r] < 0.
+template <typename E>
+__global__ void k_gather_elems(const E *__restrict__ src, E *__restrict__ dst, const int32_t *__restrict__ map,
+                               int64_t R, int64_t total, float fill)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t r = i / R, e = i % R;
+    const int m = map[r];
+    dst[i] = m >= 0 ? src[(int64_t)m * R + e] : from_float<E>(fill);
+}
+
+// ---------------------------------------------------------------------------
 // per (b, h): dl, ddt, and the dA / dD partial sums
 // ---------------------------------------------------------------------------
 // Inside chunk c (l_k enters through cs_j for j >= k in the chunk, and through

@@ -931,12 +931,21 @@ template <int VE> __device__ __forceinline__ void store_final(float *p, const fl
 // the boundary term exp(cs_last(c)) <G_c, Hin_c> of the log-decay gradient:
 // each wave's share of the dot product goes to bnd_part[(b, h, c), wave of the
 // (b, h)], PN / (64 VE) partials per (b, h, c), in a fixed order.
+//
+// cseg (instead of seq_idx; batch 1): the segment id of every chunk, for a
+// stream laid out so that every segment starts at a chunk start (-1 for chunks
+// past the last segment).  Forward: the carry is cut where the id changes, and
+// the state stored as entering such a chunk is zero.  REV: where the id changes
+// between chunk c-1 and c, G_{c-1} restarts from segment cseg[c-1]'s own
+// gradient, `init` + cseg[c-1] * H * PN (init is then [nseq, H, PN], and an id
+// of -1 or a NULL init means zero).
 template <typename E, int VE, bool REV = false>
 __global__ __launch_bounds__(kThreads) void k_state_passing(
     E *__restrict__ states, const float *__restrict__ cs, const float *__restrict__ init,
     float *__restrict__ final_states, const int32_t *__restrict__ seq_idx,
     int T, int H, int64_t PN, int nc, int Q, int64_t total_vecs,
-    const E *__restrict__ hin = nullptr, float *__restrict__ bnd_part = nullptr)
+    const E *__restrict__ hin = nullptr, float *__restrict__ bnd_part = nullptr,
+    const int32_t *__restrict__ cseg = nullptr)
 {
     using R = typename RawVec<E, VE>::type;
     constexpr int D = kPrefetch;   // divides 64
@@ -952,7 +961,14 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
     float hs[VE];
 #pragma unroll
     for (int v = 0; v < VE; ++v) hs[v] = 0.f;
-    if (init) load_init<VE>(init + (int64_t)bh * PN + e0, hs);
+    // the gradient of segment sg (REV with cseg), or zero
+    auto seg_init = [&](int sg) {
+#pragma unroll
+        for (int v = 0; v < VE; ++v) hs[v] = 0.f;
+        if (init && sg >= 0) load_init<VE>(init + ((int64_t)sg * H + h) * PN + e0, hs);
+    };
+    if (REV && cseg) seg_init(cseg[nc - 1]);
+    else if (init) load_init<VE>(init + (int64_t)bh * PN + e0, hs);
     const float *lamp = cs + (int64_t)bh * nc * Q + (Q - 1);   // cs at each chunk's last position
     const int64_t cstride = (int64_t)H * PN;
     E *lane_base = states + ((int64_t)b * nc * H + h) * PN + e0;
@@ -981,6 +997,17 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
         const int cl = cb + lane;
         const float lamv = cl < nc ? lamp[(int64_t)chunk(cl) * Q] : 0.f;
         const int slv = (!REV && seq_idx && cl < nc) ? seq_idx[min(cl * Q + Q, T) - 1] : 0;
+        // with cseg: whether the visited chunk's neighbour on the far side (c-1 for
+        // REV, c for the forward, where the carry from c-1 enters) is in another
+        // segment, and that neighbour's id (REV)
+        int cut = 0, nseg = -1;
+        if (cseg && cl < nc) {
+            const int c = chunk(cl);
+            if (c > 0) {
+                nseg = cseg[c - 1];
+                cut = cseg[c] != nseg;
+            }
+        }
         for (int k0 = 0; k0 < 64 && cb + k0 < nc; k0 += D) {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
@@ -989,10 +1016,19 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
                     float sv[VE];
                     unpack_vec<E, VE>(buf[j], sv);
                     if (k + D < nc) buf[j] = *reinterpret_cast<const R *>(lane_base + (int64_t)chunk(k + D) * cstride);
-                    store_vec<VE>(lane_base + (int64_t)chunk(k) * cstride, hs);
+                    const int kcut = cseg ? __builtin_amdgcn_readlane(cut, k0 + j) : 0;   // uniform
+                    if (!REV && kcut) {
+                        // a chunk that starts a segment: nothing enters it
+                        float zero[VE];
+#pragma unroll
+                        for (int v = 0; v < VE; ++v) zero[v] = 0.f;
+                        store_vec<VE>(lane_base + (int64_t)chunk(k) * cstride, zero);
+                    } else {
+                        store_vec<VE>(lane_base + (int64_t)chunk(k) * cstride, hs);
+                    }
                     const float lm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lamv), k0 + j));
                     const int sc = __builtin_amdgcn_readlane(slv, k0 + j);
-                    const bool keep = REV || !seq_idx || sc == sprev;
+                    const bool keep = (REV || !seq_idx || sc == sprev) && !(!REV && kcut);
                     sprev = sc;
                     const float d = exp_neg(lm);
                     if constexpr (BND) {
@@ -1016,8 +1052,12 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
                             if (lane == 0) bnd_part[((int64_t)bh * nc + chunk(k)) * nwv + wv] = d * tot;
                         }
                     }
+                    if (REV && kcut) {
+                        seg_init(__builtin_amdgcn_readlane(nseg, k0 + j));   // G of chunk c-1 restarts
+                    } else {
 #pragma unroll
-                    for (int v = 0; v < VE; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
+                        for (int v = 0; v < VE; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
+                    }
                 }
             }
         }

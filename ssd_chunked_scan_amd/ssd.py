@@ -453,18 +453,19 @@ def bwd_workspace_bytes(p: Problem) -> int:
 
 
 def bwd(x, dt, A, B, C, chunk, y, dy, D=None, initial_states=None, dfinal_states=None, dt_softplus=True,
-        grads=None, workspace=None, stream=None, want_dinit=True, fwd_workspace=None):
+        grads=None, workspace=None, stream=None, want_dinit=True, fwd_workspace=None, seq_idx=None, nseq=None):
     """Gradients of sum(y * dy) + sum(final_states * dfinal_states) (see ``ssd_bwd``
     in ``include/ssd.h``).  ``y`` is the forward output.  Returns a dict with dx,
     ddt, dA, dB, dC, dD (None without D) and dinitial_states (None unless
     ``want_dinit``); ``grads`` may pass those tensors pre-allocated.
     ``fwd_workspace``: the workspace of the ``fwd`` call that produced ``y`` (on
     these same inputs, untouched since), whose chunk intermediates are then read
-    instead of recomputed."""
-    p = Problem(x, dt, A, B, C, chunk, D, initial_states, None, None, dt_softplus)
+    instead of recomputed (not for packed streams).  With ``seq_idx`` (packed
+    streams, batch 1) ``dfinal_states`` is [nseq, H, P, N], one per segment."""
+    p = Problem(x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus)
     _check(y, "y", x.dtype, x.shape, p.device)
     _check(dy, "dy", x.dtype, x.shape, p.device)
-    _check(dfinal_states, "dfinal_states", torch.float32, (p.b, p.H, p.P, p.N), p.device)
+    _check(dfinal_states, "dfinal_states", torch.float32, p.final_shape(), p.device)
     g = dict(grads or {})
     g.setdefault("dx", p.empty(x.shape))
     g.setdefault("ddt", p.empty(dt.shape))

@@ -189,7 +189,7 @@ def _bwd_args(**kw):
 
 
 @pytest.mark.parametrize("fkw,gkw,code", [
-    (dict(seq_idx=0x90000000, nseq=1), dict(), SEQ),            # packed streams have no backward
+    (dict(seq_idx=0x90000000, nseq=1, batch=2), dict(), SEQ),   # packed streams need batch 1
     (dict(chunk=96), dict(), CHUNK),
     (dict(y=0), dict(), NULLP),                                 # the forward output is an input here
     (dict(), dict(dy=0), NULLP), (dict(), dict(dx=0), NULLP), (dict(), dict(dA=0), NULLP),
@@ -218,8 +218,14 @@ def test_bwd_workspace_size(lib):
     m = ctypes.c_size_t()
     assert lib.ssd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(m)) == OK
     assert n.value > m.value
-    packed = _args(seq_idx=0x90000000, nseq=2)
-    assert lib.ssd_bwd_workspace_size(ctypes.byref(packed), ctypes.byref(n)) == SEQ
+    # a packed stream also holds its copy laid out with every segment starting at a
+    # chunk start (each of the nseq segments padded by fewer than `chunk` tokens)
+    plain = _args(seqlen=4096, nheads=8, chunk=128)
+    packed = _args(seqlen=4096, nheads=8, chunk=128, seq_idx=0x90000000, nseq=5)
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(plain), ctypes.byref(n)) == OK
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(packed), ctypes.byref(m)) == OK
+    assert m.value > n.value
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(_args(seq_idx=0x90000000, nseq=0)), ctypes.byref(n)) == SEQ
 
 
 @pytest.mark.parametrize("z,code", [

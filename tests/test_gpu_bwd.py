@@ -233,3 +233,108 @@ def test_bwd_long_workload_full_size():
     _log("    " + "  ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f"  (tol {TOL['bf16']:.0e})")
     for k, v in errs.items():
         assert v <= TOL["bf16"], (k, v)
+
+
+# ---------------------------------------------------------------------------
+# packed streams
+# ---------------------------------------------------------------------------
+
+def check_bwd_packed(inp, dtype, label="", seed=0):
+    """The backward of a packed stream against the oracle's, per (segment, head)
+    slice of dx and ddt, per (segment, group) slice of dB and dC, per head of
+    dinit, and over the heads for dA and dD; dfinal holds one gradient per
+    segment id."""
+    _log(f"[bwd packed] {label} T={inp.x.shape[1]} lengths={inp.lengths} Q={inp.chunk} {dtype}")
+    g = inp.to("cuda:0")
+    nseq = inp.nseq
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states,
+                   seq_idx=g.seq_idx, nseq=nseq, dt_softplus=inp.dt_softplus)
+    rng = np.random.default_rng(300 + seed)
+    b, T, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    dy = torch.from_numpy(rng.standard_normal((b, T, H, P)).astype(np.float32))
+    dy = dy.to(torch.bfloat16) if dtype == "bf16" else dy
+    dfin = torch.from_numpy(rng.standard_normal((nseq, H, P, N)).astype(np.float32))
+    gr = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy.to("cuda:0"), D=g.D,
+                 initial_states=g.initial_states, dfinal_states=dfin.to("cuda:0"),
+                 dt_softplus=inp.dt_softplus, seq_idx=g.seq_idx, nseq=nseq)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp.x, inp.dt, inp.A, inp.B, inp.C, dy, inp.D, inp.initial_states, dfin,
+                          seq_idx=inp.seq_idx, nseq=nseq, dt_softplus=inp.dt_softplus)
+    ids = inp.seq_idx.numpy()
+    segs = [np.flatnonzero(ids == s) for s in np.unique(ids)]
+
+    def seg_worst(got, want):
+        # got / want [1, T, K, ...]: slices (segment, k) over (tokens of the segment, ...)
+        return max(rel(got[0, sl, k], want[0, sl, k]) for sl in segs for k in range(got.shape[2]))
+
+    errs = {
+        "dx": seg_worst(f64(gr["dx"]), ref.dx),
+        "ddt": seg_worst(f64(gr["ddt"])[..., None], ref.ddt[..., None]),
+        "dB": seg_worst(f64(gr["dB"]), ref.dB),
+        "dC": seg_worst(f64(gr["dC"]), ref.dC),
+        "dA": rel(f64(gr["dA"]), ref.dA),
+    }
+    if inp.initial_states is not None:
+        errs["dinit"] = worst(f64(gr["dinitial_states"]), ref.dinit, [0, 1])
+    if ref.dD is not None:
+        errs["dD"] = rel(f64(gr["dD"]), ref.dD)
+    _log("    " + "  ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f"  (tol {TOL[dtype]:.0e})")
+    for k, v in errs.items():
+        assert v <= TOL[dtype], (k, v)
+    for k, t in gr.items():
+        if t is not None:
+            assert torch.isfinite(t).all(), k
+    return gr
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("Q", [64, 128, 256])
+def test_bwd_packed(dtype, Q):
+    """Packed sequences with boundaries inside chunks, an initial state (the first
+    sequence's), several sequences sharing a chunk, groups."""
+    inp = wl.make_inputs(1, None, 4, 64, 64, 2, Q, dtype, 400 + Q, init_std=0.3,
+                         packed=dict(nseqs=7, lo=20, hi=300))
+    check_bwd_packed(inp, dtype, label="mid-chunk boundaries")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_bwd_packed_slow_decay_sparse_ids(dtype):
+    """Slow decay (the carried state and dfinal matter far back), segment ids with
+    gaps that start above 0, and sequences that end exactly on a chunk boundary
+    (64, 128) as well as inside one."""
+    import math
+    Q = 64
+    lengths, sids, nseq = [64, 70, 128, 5, 93], [1, 2, 4, 5, 7], 9
+    T = sum(lengths)
+    ids = np.concatenate([np.full(L, s) for s, L in zip(sids, lengths)]).astype(np.int32)
+    base = wl.make_inputs(1, T, 3, 32, 48, 1, Q, dtype, 77, init_std=0.4,
+                          a_log_range=(math.log(0.01), math.log(0.1)))
+    inp = wl.Inputs(base.x, base.dt, base.A, base.B, base.C, base.D, base.initial_states,
+                    torch.from_numpy(ids), nseq, Q, lengths=lengths)
+    check_bwd_packed(inp, dtype, label="slow decay, sparse ids")
+
+
+def test_bwd_packed_raw_dt_no_D():
+    inp = wl.make_inputs(1, None, 2, 32, 64, 1, 128, "fp32", 91, with_d=False,
+                         packed=dict(nseqs=4, lo=50, hi=400))
+    inp.dt_softplus = False
+    inp.dt = inp.dt.float().abs() * 0.3
+    check_bwd_packed(inp, "fp32", label="raw dt, no D")
+
+
+def test_bwd_packed_deterministic():
+    inp = wl.make_inputs(1, None, 4, 64, 64, 2, 128, "bf16", 92, packed=dict(nseqs=5, lo=30, hi=500))
+    a = check_bwd_packed(inp, "bf16", label="determinism 1")
+    b = check_bwd_packed(inp, "bf16", label="determinism 2")
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+
+
+def test_bwd_packed_workload_full_size():
+    """The packed workload (16 sequences of 128-2048 tokens plus the padding
+    segment, 64 heads, N = 128, 8 groups, chunk 128, bf16) at full size, every
+    (segment, head) slice against the oracle."""
+    inp = wl.workload(4)
+    check_bwd_packed(inp, "bf16", label=inp.name)
