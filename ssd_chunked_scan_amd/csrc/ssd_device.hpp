@@ -165,6 +165,19 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// A load of data read for the last time (the non-temporal cache policy), so it
+// does not displace data that later loads will hit in L2 or the MALL.
+constexpr int kCpolNonTemporal = 2;
+__device__ __forceinline__ uint4 bload16_last(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNonTemporal));
+}
+// 16-byte stores of results nothing in this pass reads again (non-temporal).
+__device__ __forceinline__ void store16_stream(void *p, uint4 v)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
 // The same with a wave-uniform extra offset in the scalar offset field (only for
 // accesses known to be in range: the scalar part is not range-checked).
 __device__ __forceinline__ uint4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff)
