@@ -547,6 +547,13 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     if ((r = run_cb<E>(s, &rv, cbr, st)) != SSD_OK) return r;
     // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
     if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st)) != SSD_OK) return r;
+    if (cseg) {
+        // packed layout: each segment's dfinal into the U slot of the chunk after its last
+        const int64_t PN = s.P * s.N;
+        hipLaunchKernelGGL(k_bwd_inject_dfinal<E>, dim3(grid1(s.H * PN / 4, 256), (unsigned)s.nc), dim3(256), 0, st,
+                           gstates, g->dfinal_states, cseg, (int)s.H, PN, (int)s.nc);
+        if ((r = launched()) != SSD_OK) return r;
+    }
     //    (with the boundary terms e^{cs_last} <G_c, Hin_c> of dl, as partial sums)
     if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, states, bnd, st, cseg)) !=
         SSD_OK)

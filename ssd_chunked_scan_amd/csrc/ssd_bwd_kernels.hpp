@@ -146,6 +146,25 @@ __global__ void k_bwd_pad_map(const int32_t *__restrict__ ostart, const int32_t 
     if (pp % Q == 0) cseg[pp / Q] = off < padded ? lo : -1;
 }
 
+// Where chunk c starts a segment of the padded stream, its gradient state slot
+// (U_c, which the reverse scan does not read there) takes the final-state
+// gradient of the segment before it, cseg[c-1] (zero for -1 or without dfinal):
+// the reverse scan restarts from that slot.  Grid (ceil(H*PN/4/256), nc), four
+// elements per thread.
+template <typename E>
+__global__ void k_bwd_inject_dfinal(E *__restrict__ gstates, const float *__restrict__ dfinal,
+                                    const int32_t *__restrict__ cseg, int H, int64_t PN, int nc)
+{
+    const int c = blockIdx.y;
+    if (c == 0 || cseg[c] == cseg[c - 1]) return;   // uniform
+    const int sg = cseg[c - 1];
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= (int64_t)H * PN) return;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (dfinal && sg >= 0) load4_f32(dfinal + (int64_t)sg * H * PN + i, v);
+    store4_f32(gstates + (int64_t)c * H * PN + i, v);
+}
+
 // ppos[t] = the padded position of original position t.
 __global__ void k_bwd_unpad_map(const int32_t *__restrict__ seq_idx, const int32_t *__restrict__ ostart,
                                 const int32_t *__restrict__ pstart, int32_t *__restrict__ ppos, int T, int nseq)

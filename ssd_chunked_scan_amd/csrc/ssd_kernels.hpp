@@ -936,9 +936,12 @@ template <int VE> __device__ __forceinline__ void store_final(float *p, const fl
 // stream laid out so that every segment starts at a chunk start (-1 for chunks
 // past the last segment).  Forward: the carry is cut where the id changes, and
 // the state stored as entering such a chunk is zero.  REV: where the id changes
-// between chunk c-1 and c, G_{c-1} restarts from segment cseg[c-1]'s own
-// gradient, `init` + cseg[c-1] * H * PN (init is then [nseq, H, PN], and an id
-// of -1 or a NULL init means zero).
+// between chunk c-1 and c, G_{c-1} restarts from slot c alone, where the caller
+// has put segment cseg[c-1]'s own final-state gradient in place of U_c (which
+// nothing reads there; k_bwd_inject_dfinal); the scan starts from segment
+// cseg[nc-1]'s, `init` + cseg[nc-1] * H * PN (init is then [nseq, H, PN], and an
+// id of -1 or a NULL init means zero).  The cut is a select on the same update
+// as the forward's, so the loop holds no extra loads.
 template <typename E, int VE, bool REV = false>
 __global__ __launch_bounds__(kThreads) void k_state_passing(
     E *__restrict__ states, const float *__restrict__ cs, const float *__restrict__ init,
@@ -997,16 +1000,11 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
         const int cl = cb + lane;
         const float lamv = cl < nc ? lamp[(int64_t)chunk(cl) * Q] : 0.f;
         const int slv = (!REV && seq_idx && cl < nc) ? seq_idx[min(cl * Q + Q, T) - 1] : 0;
-        // with cseg: whether the visited chunk's neighbour on the far side (c-1 for
-        // REV, c for the forward, where the carry from c-1 enters) is in another
-        // segment, and that neighbour's id (REV)
-        int cut = 0, nseg = -1;
+        // with cseg: whether chunk c-1 of the visited chunk c is in another segment
+        int cut = 0;
         if (cseg && cl < nc) {
             const int c = chunk(cl);
-            if (c > 0) {
-                nseg = cseg[c - 1];
-                cut = cseg[c] != nseg;
-            }
+            if (c > 0) cut = cseg[c] != cseg[c - 1];
         }
         for (int k0 = 0; k0 < 64 && cb + k0 < nc; k0 += D) {
 #pragma unroll
@@ -1016,19 +1014,17 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
                     float sv[VE];
                     unpack_vec<E, VE>(buf[j], sv);
                     if (k + D < nc) buf[j] = *reinterpret_cast<const R *>(lane_base + (int64_t)chunk(k + D) * cstride);
-                    const int kcut = cseg ? __builtin_amdgcn_readlane(cut, k0 + j) : 0;   // uniform
-                    if (!REV && kcut) {
-                        // a chunk that starts a segment: nothing enters it
-                        float zero[VE];
+                    const bool kcut = __builtin_amdgcn_readlane(cut, k0 + j) != 0;   // uniform
+                    {
+                        // a chunk that starts a segment: nothing enters it (forward)
+                        float hv[VE];
 #pragma unroll
-                        for (int v = 0; v < VE; ++v) zero[v] = 0.f;
-                        store_vec<VE>(lane_base + (int64_t)chunk(k) * cstride, zero);
-                    } else {
-                        store_vec<VE>(lane_base + (int64_t)chunk(k) * cstride, hs);
+                        for (int v = 0; v < VE; ++v) hv[v] = (!REV && kcut) ? 0.f : hs[v];
+                        store_vec<VE>(lane_base + (int64_t)chunk(k) * cstride, hv);
                     }
                     const float lm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lamv), k0 + j));
                     const int sc = __builtin_amdgcn_readlane(slv, k0 + j);
-                    const bool keep = (REV || !seq_idx || sc == sprev) && !(!REV && kcut);
+                    const bool keep = (REV || !seq_idx || sc == sprev) && !kcut;
                     sprev = sc;
                     const float d = exp_neg(lm);
                     if constexpr (BND) {
@@ -1052,12 +1048,8 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
                             if (lane == 0) bnd_part[((int64_t)bh * nc + chunk(k)) * nwv + wv] = d * tot;
                         }
                     }
-                    if (REV && kcut) {
-                        seg_init(__builtin_amdgcn_readlane(nseg, k0 + j));   // G of chunk c-1 restarts
-                    } else {
 #pragma unroll
-                        for (int v = 0; v < VE; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
-                    }
+                    for (int v = 0; v < VE; ++v) hs[v] = (keep ? d * hs[v] : 0.f) + sv[v];
                 }
             }
         }
