@@ -163,6 +163,52 @@ def algorithmic_work(shape, esz, packed):
     return w
 
 
+def backward_stage_work(shape, esz, nseq=0):
+    """Algorithmic FLOPs and HBM bytes of each stage of ssd_bwd (the names that
+    ssd_bwd_stage_times reports), on the real tokens of the problem.
+
+    The backward runs the forward's scan once more on the time-reversed problem
+    (dy in the place of x, B and C swapped, unit step size), which gives the
+    gradient states G_c and dx; the rest are products with those.  FLOPs count
+    the MFMA work the method needs (causal halves only), bytes each tensor a
+    stage must read or write once.  Stages that only move data (reversal, the
+    packed layout) count their copies."""
+    b, T, H, P, N, G, Q = (shape[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
+                                             "ngroups", "chunk"))
+    nc = (T + Q - 1) // Q
+    causal = (Q + 1) / (2.0 * Q)
+    X = b * T * H * P * esz                  # x, dy, dx
+    BC = b * T * G * N * esz                 # B, C, dB, dC (and their reversed copies)
+    ST = b * nc * H * P * N * esz            # one set of chunk states
+    V4 = b * H * nc * Q * 4                  # one fp32 value per (token, head)
+    DT = b * T * H * esz                     # dt, ddt
+    CB = b * nc * G * Q * Q * esz * (Q // 64 + 1) / (2 * (Q // 64))   # a lower block triangle
+    PN4 = b * H * P * N * 4
+    fwd = algorithmic_work(shape, esz, None)
+    scan_flops = fwd["chunk_scan"]["flops"]
+    w = {
+        "chunk_cb": fwd["chunk_cb"], "chunk_state": fwd["chunk_state"], "state_passing": fwd["state_passing"],
+        "reverse_rows": dict(bytes=4 * BC + 3 * V4),
+        "chunk_cb_rev": fwd["chunk_cb"],
+        "chunk_state_grad": dict(flops=2.0 * b * T * H * P * N, bytes=X + BC + V4 + ST),
+        "inject_dfinal": dict(bytes=nseq * H * P * N * (4 + esz)),
+        "state_passing_rev": dict(bytes=3 * ST + 2 * b * H * nc * 4 + 2 * PN4),
+        # y' of the reversed problem; dx = delta y' + D dy; x . (G term), x . y', dy . x
+        "chunk_scan_dx": dict(flops=scan_flops, bytes=3 * X + BC + CB + ST + 6 * V4),
+        "chunk_scan_dy_hin": dict(flops=2.0 * b * T * H * N * P, bytes=X + BC + ST + 2 * V4),
+        # M = sum over the group's heads of (dy x^T) o decay, with its row and column sums
+        "m_rows_cols": dict(flops=2.0 * b * nc * H * Q * Q * P * causal, bytes=2 * X + 3 * CB + 4 * V4),
+        "dl_ddt_dA_dD": dict(bytes=8 * V4 + 2 * DT),
+        "dC": dict(flops=2.0 * b * T * G * N * Q * causal + 2.0 * b * T * H * P * N,
+                   bytes=X + ST + CB + 2 * BC + 2 * V4),
+        "dB": dict(flops=2.0 * b * T * G * N * Q * causal + 2.0 * b * T * H * P * N,
+                   bytes=X + ST + CB + 2 * BC + 2 * V4),
+        "pad_layout": dict(bytes=2 * (2 * X + 2 * BC + DT)),
+        "unpad_gather": dict(bytes=2 * (X + 2 * BC + DT)),
+    }
+    return w
+
+
 def seq_final_work(shape, esz, seq_idx):
     """Algorithmic FLOPs and bytes of seq_final on a packed stream (seq_idx: the
     host copy of the int32 ids, nseq taken from shape["nseq"]).  Per sequence
@@ -266,6 +312,29 @@ def run_backward(dev, inp, g, reps, warmup):
         out.update(ms=round(avg_r, 5), tokens_per_s=round(inp.real_tokens / (avg_r / 1e3), 1),
                    note="all input gradients of a packed stream: the stream is laid out again with every "
                         "sequence starting at a chunk start, and the chunk intermediates recomputed there")
+    # per stage: HIP events between the stages of the same call (ssd_bwd_stage_times),
+    # mean over the reps, each placed on the roofline with its algorithmic work
+    kw_st = dict(kw, fwd_workspace=fws if nseq is None else None)
+    sums = {}
+    for r in range(warmup + reps):
+        stages = []
+        ssd.bwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, y, dy, grads=grads, stage_times=stages, **kw_st)
+        if r >= warmup:
+            for name, ms in stages:
+                sums[name] = sums.get(name, 0.0) + ms
+    shape = dict(batch=p.b, seqlen=p.T, nheads=p.H, headdim=p.P, dstate=p.N, ngroups=p.G, chunk=p.Q)
+    esz = 2 if g.x.dtype == torch.bfloat16 else 4
+    work = backward_stage_work(shape, esz, nseq or 0)
+    stages_out = {}
+    for name, tot in sums.items():
+        ms = tot / reps
+        e = {"ms": round(ms, 5)}
+        if name in work:
+            e.update(roofline_point(work[name], ms / 1e3, esz))
+        stages_out[name] = e
+    out["stages"] = stages_out
+    out["stages_note"] = ("events between the stages of one ssd_bwd_stage_times call, mean of the reps; "
+                          "the events add a little to the total")
     return out
 
 

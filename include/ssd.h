@@ -296,6 +296,20 @@ ssd_status ssd_bwd_workspace_size(const ssd_fwd_args *args, size_t *bytes);
  * or the workspace. */
 ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *grads, void *stream);
 
+/* Per-stage device times of one backward, a profiling aid for ssd_bwd: does
+ * exactly the work of ssd_bwd(args, grads, stream), with the same checks and
+ * error codes, and records a HIP event on the stream before the first stage and
+ * after each stage (one stage is one kernel, or a few small ones that belong
+ * together, e.g. "m_rows_cols", "dC", "dB").  It then waits for the stream and
+ * writes, for i < *nstages, the duration of stage i in milliseconds to ms[i]
+ * and its name (a static string owned by the library) to names[i].  ms and
+ * names are host arrays of at least max_stages entries; max_stages below
+ * SSD_BWD_MAX_STAGES is SSD_ERR_BAD_SHAPE.  Blocks the calling thread; an empty
+ * problem (seqlen 0) reports no stages. */
+#define SSD_BWD_MAX_STAGES 24
+ssd_status ssd_bwd_stage_times(const ssd_fwd_args *args, const ssd_bwd_args *grads, void *stream, int max_stages,
+                               float *ms, const char **names, int *nstages);
+
 /*
  * The Mamba-2 block around the SSD ("SSM 家族全景图（下）：Mamba-2 与 Jamba",
  * section five, the block's data flow): the main path passes a causal

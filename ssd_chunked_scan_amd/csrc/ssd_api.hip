@@ -419,8 +419,20 @@ ssd_status run_conv(const ssd_conv_args *a, hipStream_t st)
 // ---------------------------------------------------------------------------
 struct BwdWorkspace {
     size_t delta, cs, cb, states, gstates, cbr, br, cr, csr, dlr, yo, zo, xyp, rpart, cpart, bnd, dyx,
-        mrow, mcol, dA_part, dD_part, total;
+        mrow, mcol, dA_part, dD_part, mpart, total;
 };
+
+// Workgroups of k_bwd_m split the group's heads hsplit ways when its tiles alone
+// would leave the GPU short of workgroups (about 2048 wanted: 256 CUs, several
+// each); every split keeps at least one head.
+int64_t bwd_m_hsplit(const Shape &s)
+{
+    const int64_t qt = s.Q / 64, tiles = qt * (qt + 1) / 2 * s.nc * s.G * s.b;
+    const int64_t hpg = s.H / s.G;
+    int64_t k = (2048 + tiles - 1) / tiles;
+    if (k > hpg) k = hpg;
+    return k < 1 ? 1 : k;
+}
 
 BwdWorkspace bwd_workspace_layout(const Shape &s)
 {
@@ -455,6 +467,8 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     w.mcol = take(ms);
     w.dA_part = take(bh * (size_t)s.nc);
     w.dD_part = take(bh * (size_t)s.nc);
+    const int64_t hs = bwd_m_hsplit(s);
+    w.mpart = take(hs > 1 ? (size_t)hs * (size_t)(s.b * qt * (qt + 1) / 2 * s.nc * s.G) * 4096 * 4 : 0);
     w.total = o;
     return w;
 }
@@ -490,13 +504,44 @@ ssd_status run_passing_rev(const Shape &s, const float *cs, E *gstates, const fl
     return launched();
 }
 
+// The stage boundaries of one backward call, for ssd_bwd_stage_times: an event
+// recorded on the stream before the first stage and after each named one.
+// The events are made by start(), after every argument check has passed.
+struct StageMarks {
+    hipEvent_t ev[SSD_BWD_MAX_STAGES + 1];
+    const char *name[SSD_BWD_MAX_STAGES];
+    int made = 0, n = 0;
+    bool ok = true;
+    hipStream_t st = nullptr;
+    ssd_status start(hipStream_t stream)
+    {
+        st = stream;
+        for (; made <= SSD_BWD_MAX_STAGES; ++made)
+            if (hipEventCreate(&ev[made]) != hipSuccess) return SSD_ERR_HIP;
+        return hipEventRecord(ev[0], st) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
+    ~StageMarks()
+    {
+        for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    }
+    void mark(const char *nm)
+    {
+        if (n >= SSD_BWD_MAX_STAGES || hipEventRecord(ev[n + 1], st) != hipSuccess) {
+            ok = false;
+            return;
+        }
+        name[n++] = nm;
+    }
+};
+
 // cseg (packed streams, on the layout in which every segment starts at a chunk
 // start): the per-chunk segment ids; g->dfinal_states is then [nseq,H,P,N] and
 // g->fwd_workspace is not used.
 template <typename E>
 ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *g, const BwdWorkspace &w,
-                     hipStream_t st, const int32_t *cseg = nullptr)
+                     hipStream_t st, const int32_t *cseg = nullptr, StageMarks *sm = nullptr)
 {
+    auto mark = [&](const char *nm) { if (sm) sm->mark(nm); };
     char *ws = static_cast<char *>(g->workspace);
     auto F32 = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
     auto EP = [&](size_t off) { return reinterpret_cast<E *>(ws + off); };
@@ -519,8 +564,11 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     } else {
         // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
         if ((r = run_cb<E>(s, &f, cb, st)) != SSD_OK) return r;
+        mark("chunk_cb");
         if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st)) != SSD_OK) return r;
+        mark("chunk_state");
         if ((r = run_passing<E>(s, &f, cs, states, nullptr, st, cseg)) != SSD_OK) return r;
+        mark("state_passing");
     }
     // 2. every chunk's tokens in reversed order: B, C, and the reversed cs / delta
     //    (dy is read reversed by the kernels themselves)
@@ -534,6 +582,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     hipLaunchKernelGGL(k_bwd_reverse_cs, dim3(grid1(ncs, 256)), dim3(256), 0, st, cs, csr, dlr, (int)s.T, (int)s.Q,
                        (int)s.nc, ncs);
     if ((r = launched()) != SSD_OK) return r;
+    mark("reverse_rows");
     // 3. reversed-order problem: x <- dy, B <- C, C <- B, unit step size, no skip
     //    term; its output is turned into dx = Delta y' + D dy in original order
     ssd_fwd_args rv = *a;
@@ -545,40 +594,55 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     rv.initial_states = nullptr;
     rv.final_states = nullptr;
     if ((r = run_cb<E>(s, &rv, cbr, st)) != SSD_OK) return r;
+    mark("chunk_cb_rev");
     // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
     if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st)) != SSD_OK) return r;
+    mark("chunk_state_grad");
     if (cseg) {
         // packed layout: each segment's dfinal into the U slot of the chunk after its last
         const int64_t PN = s.P * s.N;
         hipLaunchKernelGGL(k_bwd_inject_dfinal<E>, dim3(grid1(s.H * PN / 4, 256), (unsigned)s.nc), dim3(256), 0, st,
                            gstates, g->dfinal_states, cseg, (int)s.H, PN, (int)s.nc);
         if ((r = launched()) != SSD_OK) return r;
+        mark("inject_dfinal");
     }
     //    (with the boundary terms e^{cs_last} <G_c, Hin_c> of dl, as partial sums)
     if ((r = run_passing_rev<E>(s, cs, gstates, g->dfinal_states, g->dinitial_states, states, bnd, st, cseg)) !=
         SSD_OK)
         return r;
+    mark("state_passing_rev");
     // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y';
     //    it writes dx = Delta y' + D dy, and dy . x per (token, head)
     if ((r = run_scan_dot<E, 2, false>(s, &rv, dlr, csr, cbr, gstates, (const E *)a->x, zo, xyp, st, delta,
                                        a->D, dyx)) != SSD_OK)
         return r;
+    mark("chunk_scan_dx");
     // 6. dy . (entering-state term of y), from the forward's entering states
     if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st)) != SSD_OK)
         return r;
-    // 7. M (summed over the group's heads) with the row / column sums of S
+    mark("chunk_scan_dy_hin");
+    // 7. M (summed over the group's heads) with the row / column sums of S; with
+    //    the heads split over several workgroups, their parts are added after
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     const int nnt = (int)((s.N + 63) / 64);
+    const int hsplit = (int)bwd_m_hsplit(s);
+    float *mpart = F32(w.mpart);
     if ((r = with_q(s.Q, [&](auto q) {
              return with_nt(s.N, [&](auto nt) {
                  constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
-                 hipLaunchKernelGGL((k_bwd_m<E, Q, NT>), dim3((unsigned)(ntri * s.nc * s.G), (unsigned)s.b),
+                 hipLaunchKernelGGL((k_bwd_m<E, Q, NT>), dim3((unsigned)(ntri * s.nc * s.G * hsplit), (unsigned)s.b),
                                     dim3(kThreads), 0, st, (const E *)g->dy, (const E *)a->x, delta, cs, (const E *)cb,
-                                    mrow, mcol, rpart, cpart, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc);
+                                    mrow, mcol, rpart, cpart, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc,
+                                    hsplit, mpart);
+                 if (hsplit > 1)
+                     hipLaunchKernelGGL((k_bwd_m_reduce<E, Q>), dim3((unsigned)(ntri * s.nc * s.G), (unsigned)s.b),
+                                        dim3(kThreads), 0, st, (const float *)mpart, mrow, mcol, (int)s.G, (int)s.nc,
+                                        hsplit);
                  return launched();
              });
          })) != SSD_OK)
         return r;
+    mark("m_rows_cols");
     // 8. dl, ddt, dA, dD
     const int64_t dlrows = s.b * s.H * s.nc;
     hipLaunchKernelGGL(k_bwd_dl<E>, dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart, yo, zo,
@@ -588,6 +652,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     hipLaunchKernelGGL(k_bwd_sum_heads, dim3((unsigned)s.H), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
                        (int)s.b, (int)s.H, (int)s.nc);
     if ((r = launched()) != SSD_OK) return r;
+    mark("dl_ddt_dA_dD");
     // 9. dC and dB
     return with_q(s.Q, [&](auto q) {
         constexpr int Q = decltype(q)::value;
@@ -595,9 +660,11 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         hipLaunchKernelGGL((k_bwd_bc<E, Q, 0>), grid, dim3(kThreads), 0, st, (const E *)a->B, (const E *)mrow,
                            (const E *)states, (const E *)g->dy, delta, cs, (E *)g->dC, (int)s.T, (int)s.H, (int)s.G,
                            (int)s.P, (int)s.N, (int)s.nc, nnt);
+        mark("dC");
         hipLaunchKernelGGL((k_bwd_bc<E, Q, 1>), grid, dim3(kThreads), 0, st, (const E *)a->C, (const E *)mcol,
                            (const E *)gstates, (const E *)a->x, delta, cs, (E *)g->dB, (int)s.T, (int)s.H,
                            (int)s.G, (int)s.P, (int)s.N, (int)s.nc, nnt);
+        mark("dB");
         return launched();
     });
 }
@@ -654,7 +721,7 @@ PackedBwd packed_bwd_layout(const Shape &s)
 
 template <typename E>
 ssd_status bwd_packed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *g, const PackedBwd &k,
-                      hipStream_t st)
+                      hipStream_t st, StageMarks *sm = nullptr)
 {
     char *ws = static_cast<char *>(g->workspace);
     auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
@@ -688,6 +755,7 @@ ssd_status bwd_packed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args 
     // padding takes a zero step size: softplus(-inf) = 0
     elems(a->dt, EP(k.dtp), pos_src, s.H, Tp, a->dt_softplus ? -__builtin_huge_valf() : 0.f);
     if (launched() != SSD_OK) return SSD_ERR_HIP;
+    if (sm) sm->mark("pad_layout");
     // the chunked backward on the padded stream
     ssd_fwd_args fp = *a;
     fp.seqlen = Tp;
@@ -707,13 +775,14 @@ ssd_status bwd_packed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args 
     gp.workspace = ws + k.inner;
     gp.workspace_bytes = k.w.total;
     gp.fwd_workspace = nullptr;
-    ssd_status r = bwd_typed<E>(k.sp, &fp, &gp, k.w, st, cseg);
+    ssd_status r = bwd_typed<E>(k.sp, &fp, &gp, k.w, st, cseg, sm);
     if (r != SSD_OK) return r;
     // back to the original positions
     rows(EP(k.dxp), g->dx, ppos, HP, T);
     rows(EP(k.dbp), g->dB, ppos, GN, T);
     rows(EP(k.dcp), g->dC, ppos, GN, T);
     elems(EP(k.ddtp), g->ddt, ppos, s.H, T, 0.f);
+    if (sm) sm->mark("unpad_gather");
     return launched();
 }
 
@@ -760,6 +829,66 @@ const char *const kStatusText[] = {
     "a HIP kernel launch failed",
     "the problem needs more scratch than the library's static buffer holds (ssd_fwd_noalloc)",
 };
+
+ssd_status bwd_entry(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream, StageMarks *sm)
+{
+    Shape s;
+    ssd_status r = parse_shape(args, &s);
+    if (r != SSD_OK) return r;
+    if (!g) return SSD_ERR_NULL_POINTER;
+    if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB | kNeedC)) != SSD_OK) return r;
+    const bool empty = s.T == 0;
+    if (!g->dA) return SSD_ERR_NULL_POINTER;
+    if (!empty && (!args->y || !g->dy || !g->dx || !g->ddt || !g->dB || !g->dC)) return SSD_ERR_NULL_POINTER;
+    const void *ptrs[] = {args->y, g->dy, g->dfinal_states, g->dx, g->ddt, g->dA, g->dB, g->dC, g->dD,
+                          g->dinitial_states, g->workspace, g->fwd_workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+    const Sizes z = tensor_sizes(s);
+    const size_t st = (size_t)(s.b * s.H * s.P * s.N) * 4;   // dinitial_states
+    // packed streams: the backward always recomputes on its own layout, so a
+    // forward workspace is not read
+    const void *fwd_ws = s.packed ? nullptr : g->fwd_workspace;
+    const size_t wtotal = s.packed ? packed_bwd_layout(s).total : bwd_workspace_layout(s).total;
+    const size_t fws = workspace_layout(s).total;
+    if (!empty) {
+        if (!g->workspace) return SSD_ERR_NULL_POINTER;
+        if (g->workspace_bytes < wtotal) return SSD_ERR_WORKSPACE_TOO_SMALL;
+        if (fwd_ws && g->fwd_workspace_bytes < fws) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    }
+    const Range ins[] = {{args->x, z.x}, {args->dt, z.dt}, {args->A, z.A}, {args->B, z.bc}, {args->C, z.bc},
+                         {args->D, z.D}, {args->initial_states, z.init}, {args->seq_idx, z.seq}, {args->y, z.y},
+                         {g->dy, z.x}, {g->dfinal_states, z.fin}, {fwd_ws, fws}};
+    const Range outs[] = {{g->dx, z.x}, {g->ddt, z.dt}, {g->dA, z.A}, {g->dB, z.bc}, {g->dC, z.bc},
+                          {g->dD, z.D}, {g->dinitial_states, st}, {empty ? nullptr : g->workspace, wtotal}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range &in : ins)
+            if (overlaps(outs[i], in)) return SSD_ERR_ALIASING;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlaps(outs[i], outs[j])) return SSD_ERR_ALIASING;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (empty) {
+        // no tokens: the final state is the initial state, nothing else depends on the inputs
+        hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dA, (const float *)nullptr, s.H);
+        if (g->dD)
+            hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dD, (const float *)nullptr, s.H);
+        // (an empty packed stream has no segment that could receive the initial state)
+        if (g->dinitial_states)
+            hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.b * s.H * s.P * s.N, 256)), dim3(256), 0, hs,
+                               g->dinitial_states, s.packed ? nullptr : g->dfinal_states, s.b * s.H * s.P * s.N);
+        return launched();
+    }
+    if (sm && (r = sm->start(hs)) != SSD_OK) return r;
+    if (s.packed) {
+        const PackedBwd k = packed_bwd_layout(s);
+        return s.dtype == SSD_DTYPE_BF16 ? bwd_packed<bf16>(s, args, g, k, hs, sm)
+                                         : bwd_packed<float>(s, args, g, k, hs, sm);
+    }
+    const BwdWorkspace w = bwd_workspace_layout(s);
+    return s.dtype == SSD_DTYPE_BF16 ? bwd_typed<bf16>(s, args, g, w, hs, nullptr, sm)
+                                     : bwd_typed<float>(s, args, g, w, hs, nullptr, sm);
+}
 
 }  // namespace
 
@@ -961,59 +1090,27 @@ ssd_status ssd_bwd_workspace_size(const ssd_fwd_args *args, size_t *bytes)
 
 ssd_status ssd_bwd(const ssd_fwd_args *args, const ssd_bwd_args *g, void *stream)
 {
-    Shape s;
-    ssd_status r = parse_shape(args, &s);
-    if (r != SSD_OK) return r;
-    if (!g) return SSD_ERR_NULL_POINTER;
-    if ((r = check_pointers(args, s, kNeedX | kNeedDt | kNeedB | kNeedC)) != SSD_OK) return r;
-    const bool empty = s.T == 0;
-    if (!g->dA) return SSD_ERR_NULL_POINTER;
-    if (!empty && (!args->y || !g->dy || !g->dx || !g->ddt || !g->dB || !g->dC)) return SSD_ERR_NULL_POINTER;
-    const void *ptrs[] = {args->y, g->dy, g->dfinal_states, g->dx, g->ddt, g->dA, g->dB, g->dC, g->dD,
-                          g->dinitial_states, g->workspace, g->fwd_workspace};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
-    const Sizes z = tensor_sizes(s);
-    const size_t st = (size_t)(s.b * s.H * s.P * s.N) * 4;   // dinitial_states
-    // packed streams: the backward always recomputes on its own layout, so a
-    // forward workspace is not read
-    const void *fwd_ws = s.packed ? nullptr : g->fwd_workspace;
-    const size_t wtotal = s.packed ? packed_bwd_layout(s).total : bwd_workspace_layout(s).total;
-    const size_t fws = workspace_layout(s).total;
-    if (!empty) {
-        if (!g->workspace) return SSD_ERR_NULL_POINTER;
-        if (g->workspace_bytes < wtotal) return SSD_ERR_WORKSPACE_TOO_SMALL;
-        if (fwd_ws && g->fwd_workspace_bytes < fws) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    return bwd_entry(args, g, stream, nullptr);
+}
+
+ssd_status ssd_bwd_stage_times(const ssd_fwd_args *args, const ssd_bwd_args *grads, void *stream, int max_stages,
+                               float *ms, const char **names, int *nstages)
+{
+    if (!ms || !names || !nstages) return SSD_ERR_NULL_POINTER;
+    if (max_stages < SSD_BWD_MAX_STAGES) return SSD_ERR_BAD_SHAPE;
+    *nstages = 0;
+    StageMarks sm;
+    ssd_status r = bwd_entry(args, grads, stream, &sm);
+    if (r == SSD_OK && !sm.ok) r = SSD_ERR_HIP;
+    // an empty problem records no event: no stages
+    if (r != SSD_OK || sm.n == 0) return r;
+    if (hipEventSynchronize(sm.ev[sm.n]) != hipSuccess) return SSD_ERR_HIP;
+    for (int i = 0; i < sm.n; ++i) {
+        if (hipEventElapsedTime(&ms[i], sm.ev[i], sm.ev[i + 1]) != hipSuccess) return SSD_ERR_HIP;
+        names[i] = sm.name[i];
     }
-    const Range ins[] = {{args->x, z.x}, {args->dt, z.dt}, {args->A, z.A}, {args->B, z.bc}, {args->C, z.bc},
-                         {args->D, z.D}, {args->initial_states, z.init}, {args->seq_idx, z.seq}, {args->y, z.y},
-                         {g->dy, z.x}, {g->dfinal_states, z.fin}, {fwd_ws, fws}};
-    const Range outs[] = {{g->dx, z.x}, {g->ddt, z.dt}, {g->dA, z.A}, {g->dB, z.bc}, {g->dC, z.bc},
-                          {g->dD, z.D}, {g->dinitial_states, st}, {empty ? nullptr : g->workspace, wtotal}};
-    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
-        for (const Range &in : ins)
-            if (overlaps(outs[i], in)) return SSD_ERR_ALIASING;
-        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
-            if (overlaps(outs[i], outs[j])) return SSD_ERR_ALIASING;
-    }
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (empty) {
-        // no tokens: the final state is the initial state, nothing else depends on the inputs
-        hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dA, (const float *)nullptr, s.H);
-        if (g->dD)
-            hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.H, 256)), dim3(256), 0, hs, g->dD, (const float *)nullptr, s.H);
-        // (an empty packed stream has no segment that could receive the initial state)
-        if (g->dinitial_states)
-            hipLaunchKernelGGL(k_fill_final, dim3(grid1(s.b * s.H * s.P * s.N, 256)), dim3(256), 0, hs,
-                               g->dinitial_states, s.packed ? nullptr : g->dfinal_states, s.b * s.H * s.P * s.N);
-        return launched();
-    }
-    if (s.packed) {
-        const PackedBwd k = packed_bwd_layout(s);
-        return s.dtype == SSD_DTYPE_BF16 ? bwd_packed<bf16>(s, args, g, k, hs) : bwd_packed<float>(s, args, g, k, hs);
-    }
-    const BwdWorkspace w = bwd_workspace_layout(s);
-    return s.dtype == SSD_DTYPE_BF16 ? bwd_typed<bf16>(s, args, g, w, hs) : bwd_typed<float>(s, args, g, w, hs);
+    *nstages = sm.n;
+    return SSD_OK;
 }
 
 ssd_status ssd_fwd_gated(const ssd_fwd_args *args, const void *z, void *stream)

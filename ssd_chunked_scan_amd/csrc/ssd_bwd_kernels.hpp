@@ -345,11 +345,16 @@ __global__ void k_bwd_sum_heads(const float *__restrict__ dA_part, const float *
 // rpart[si][t] = sum_{s in tile si} S[t][s] and column sums cpart[ti][s] = sum_{t
 // in tile ti} S[t][s] are written per tile ([QT][b,H,nc,Q] fp32 each); rows and
 // columns come from one S, so their difference cancels exactly where it should.
+// Split over heads (hsplit > 1, grid x = ntiles * hsplit): workgroup (tile, k)
+// takes the heads k*hpg/hsplit .. (k+1)*hpg/hsplit - 1 of the group and writes its
+// partial sum of M as one fp32 64 x 64 tile (rows t) to mpart[k][tile unit]
+// instead of mrow / mcol; k_bwd_m_reduce adds the parts in a fixed order.  The
+// row and column sums are per head and go out as before.
 template <typename E, int Q, int NT>
 __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const E *__restrict__ dy, const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
     const E *__restrict__ cbuf, E *__restrict__ mrow, E *__restrict__ mcol, float *__restrict__ rpart,
-    float *__restrict__ cpart, int T, int H, int G, int P, int nc)
+    float *__restrict__ cpart, int T, int H, int G, int P, int nc, int hsplit, float *__restrict__ mpart)
 {
     using F = frag_t<E>;
     constexpr int V = kVec16<E>, ES = (int)sizeof(E);
@@ -362,7 +367,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
     __shared__ float rsum[64], csum[64];
     __shared__ float hcs[2][64], hds[64];   // the head's cs at the t rows / s rows, delta at the s rows
     const int units = NTRI * nc * G;
-    const int u = xcd_remap(blockIdx.x, units);
+    const int uu = xcd_remap(blockIdx.x, units * hsplit);
+    const int u = uu / hsplit, sp = uu % hsplit;   // the split's workgroups sit next to each other
     const int b = blockIdx.y;
     int tile = u % NTRI;
     const int cg = u / NTRI, g = cg % G, c = cg / G;
@@ -375,31 +381,60 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const int t0 = c * Q, len = min(Q, T - t0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    const int hpg = H / G, PC = (P + 63) / 64, steps = hpg * PC;
+    const int hpg_all = H / G, PC = (P + 63) / 64;
+    const int h_lo = sp * hpg_all / hsplit, hpg = (sp + 1) * hpg_all / hsplit - h_lo;   // this split's heads
+    const int steps = hpg * PC;
     const int hv = threadIdx.x % VPR, hr = threadIdx.x / VPR;
     const int trows = min(64, len - ti * 64), srows = min(64, len - si * 64);
 
     uint4 rt[NPASS], rs[NPASS];
     float hval = 0.f;   // this thread's element of the next head's cs / delta rows (threads < 192)
-    auto issue = [&](int k) {
-        if (k % PC == 0 && threadIdx.x < 192) {
-            const int h = g * hpg + k / PC, part = threadIdx.x >> 6, e = threadIdx.x & 63;
-            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-            const int pos = (part == 0 ? ti : si) * 64 + e;
-            hval = pos < len ? (part == 2 ? delta[row + pos] : cs[row + pos]) : 0.f;
+    // Formed once (the loop only moves pointers by constant strides: all waves
+    // of a CU share one scalar unit, and per-step 64-bit index products bound
+    // this kernel): the first head's dy / x rows, buffer ranges, lane offsets.
+    const int64_t ld = (int64_t)H * P;
+    const int h0 = g * hpg_all + h_lo;
+    const E *dy_ptr = dy + (((int64_t)b * T + t0 + ti * 64) * H + h0) * P;
+    const E *x_ptr = x + (((int64_t)b * T + t0 + si * 64) * H + h0) * P;
+    auto range = [&](int rows, int cols) { return rsrc_bytes(rows > 0 ? ((int64_t)(rows - 1) * ld + cols) * ES : 0); };
+    const int ptail = P - (PC - 1) * 64;   // columns of the last p chunk
+    const int tr_full = range(trows, 64), tr_tail = range(trows, ptail);
+    const int sr_full = range(srows, 64), sr_tail = range(srows, ptail);
+    uint32_t loff[NPASS];
+#pragma unroll
+    for (int i = 0; i < NPASS; ++i) loff[i] = (uint32_t)(((int64_t)(hr + i * RPP) * ld + hv * V) * ES);
+    const int64_t hrow = (int64_t)nc * Q;
+    // the cs / delta element this thread stages for each head (threads < 192)
+    const float *hv_ptr = nullptr;
+    if (threadIdx.x < 192) {
+        const int part = threadIdx.x >> 6, e = threadIdx.x & 63;
+        const int pos = (part == 0 ? ti : si) * 64 + e;
+        hv_ptr = pos < len ? (part == 2 ? delta : cs) + (((int64_t)b * H + h0) * nc + c) * Q + pos : nullptr;
+    }
+    int ipc = 0;   // the p chunk of the next step issued
+    auto issue = [&]() {
+        if (ipc == 0 && threadIdx.x < 192) {
+            hval = hv_ptr ? *hv_ptr : 0.f;
+            if (hv_ptr) hv_ptr += hrow;
         }
-        const int h = g * hpg + k / PC, p0 = (k % PC) * 64;
-        const int64_t ld = (int64_t)H * P;
-        const auto trs = make_rsrc(dy + (((int64_t)b * T + t0 + ti * 64) * H + h) * P + p0,
-                                   trows > 0 ? ((int64_t)(trows - 1) * ld + min(64, P - p0)) * ES : 0);
-        const auto srs = make_rsrc(x + (((int64_t)b * T + t0 + si * 64) * H + h) * P + p0,
-                                   srows > 0 ? ((int64_t)(srows - 1) * ld + min(64, P - p0)) * ES : 0);
-        const bool cin = p0 + hv * V < P;
+        const bool last = ipc == PC - 1;
+        const auto trs = make_rsrc_n(dy_ptr, last ? tr_tail : tr_full);
+        const auto srs = make_rsrc_n(x_ptr, last ? sr_tail : sr_full);
+        const bool cin = hv * V < P - ipc * 64;
 #pragma unroll
         for (int i = 0; i < NPASS; ++i) {
-            const uint32_t o = cin ? (uint32_t)(((int64_t)(hr + i * RPP) * ld + hv * V) * ES) : kOffNone;
+            const uint32_t o = cin ? loff[i] : kOffNone;
             rt[i] = bload16(trs, o);
             rs[i] = bload16(srs, o);
+        }
+        if (last) {
+            ipc = 0;
+            dy_ptr += P - (PC - 1) * 64;
+            x_ptr += P - (PC - 1) * 64;
+        } else {
+            ++ipc;
+            dy_ptr += 64;
+            x_ptr += 64;
         }
     };
 
@@ -419,34 +454,42 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
                 cbv[i][j][r] = to_float(cbg[idx]);
             }
     const int64_t bhnc = (int64_t)gridDim.y * H * nc * Q;   // one tile slice of rpart / cpart
-    auto flush = [&](int h) {   // this head's row / column sums to memory, then cleared
-        const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+    // this thread's row (threads < 64) or column (64..127) sum slot of the first
+    // head; one head further is hrow further
+    float *sum_ptr = nullptr;
+    if (threadIdx.x < 128) {
+        const int64_t row = (((int64_t)b * H + h0) * nc + c) * Q;
+        sum_ptr = threadIdx.x < 64 ? rpart + si * bhnc + row + ti * 64 + threadIdx.x
+                                   : cpart + ti * bhnc + row + si * 64 + (threadIdx.x - 64);
+    }
+    auto flush = [&]() {   // the finished head's row / column sums to memory, then cleared
         if (threadIdx.x < 64) {
-            rpart[si * bhnc + row + ti * 64 + threadIdx.x] = rsum[threadIdx.x];
+            *sum_ptr = rsum[threadIdx.x];
             rsum[threadIdx.x] = 0.f;
         } else if (threadIdx.x < 128) {
-            const int e = threadIdx.x - 64;
-            cpart[ti * bhnc + row + si * 64 + e] = csum[e];
-            csum[e] = 0.f;
+            *sum_ptr = csum[threadIdx.x - 64];
+            csum[threadIdx.x - 64] = 0.f;
         }
+        if (threadIdx.x < 128) sum_ptr += hrow;
     };
     if (threadIdx.x < 64) rsum[threadIdx.x] = 0.f;
     else if (threadIdx.x < 128) csum[threadIdx.x - 64] = 0.f;
-    issue(0);
+    issue();
+    int kpc = 0;   // the p chunk of step k
     for (int k = 0; k < steps; ++k) {
         if (k > 0) __syncthreads();   // every wave is done reading the previous step's rows
-        if (k > 0 && (k - 1) % PC == PC - 1) flush(g * hpg + (k - 1) / PC);
+        if (k > 0 && kpc == 0) flush();   // step k - 1 finished a head
 #pragma unroll
         for (int i = 0; i < NPASS; ++i) {
             *reinterpret_cast<uint4 *>(ts + (hr + i * RPP) * PITCH + hv * V) = rt[i];
             *reinterpret_cast<uint4 *>(ss + (hr + i * RPP) * PITCH + hv * V) = rs[i];
         }
-        if (k % PC == 0 && threadIdx.x < 192) {
+        if (kpc == 0 && threadIdx.x < 192) {
             const int part = threadIdx.x >> 6, e = threadIdx.x & 63;
             if (part == 2) hds[e] = hval;
             else hcs[part][e] = hval;
         }
-        if (k + 1 < steps) issue(k + 1);
+        if (k + 1 < steps) issue();
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -461,7 +504,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
 #pragma unroll
                 for (int j = 0; j < 2; ++j) mma(acc[i][j], fa[i], fb[j]);
         }
-        if (k % PC == PC - 1) {
+        const bool head_done = kpc == PC - 1;
+        kpc = head_done ? 0 : kpc + 1;
+        if (head_done) {
             // this head is complete: add it with its decays and step sizes, and
             // sum its S = W CB by rows and by columns
             float rs[2][4] = {}, cl[2] = {};
@@ -494,7 +539,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
                         }
             } else {
                 // the diagonal tile or the ragged last one: the exact per-element
-                // decay, and only s <= t < len
+                // decay, and only s <= t < len.  Selects, not branches: an entry
+                // outside takes a harmless exponent and contributes zero.
+                float ht[2][4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ht[i][r] = hcs[0][t_w + 16 * i + 4 * lg + r];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int s = si * 64 + s_w + 16 * j + li;
@@ -504,15 +555,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int t = ti * 64 + t_w + 16 * i + 4 * lg + r;
-                            if (s <= t && t < len) {
-                                const float w =
-                                    __builtin_amdgcn_exp2f((hcs[0][t_w + 16 * i + 4 * lg + r] - css) * kLog2e) * ds;
-                                const float wv = acc[i][j][r] * w;
-                                tot[i][j][r] += wv;
-                                const float sv = wv * cbv[i][j][r];
-                                rs[i][r] += sv;
-                                cl[j] += sv;
-                            }
+                            const bool in = s <= t && t < len;
+                            float w = __builtin_amdgcn_exp2f((in ? ht[i][r] - css : -64.f) * kLog2e) * ds;
+                            asm volatile("" : "+v"(w));   // keeps the compiler from branching around it
+                            const float wv = in ? acc[i][j][r] * w : 0.f;
+                            tot[i][j][r] += wv;
+                            const float sv = wv * cbv[i][j][r];
+                            rs[i][r] += sv;
+                            cl[j] += sv;
                             acc[i][j][r] = 0.f;
                         }
                 }
@@ -561,8 +611,20 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
         }
     }
     __syncthreads();
-    flush(g * hpg + (steps - 1) / PC);
+    flush();
 
+    if (hsplit > 1) {
+        // this split's part of the tile, fp32 rows t
+        float *mp = mpart + ((int64_t)sp * gridDim.y * units + (int64_t)b * units + u) * 4096;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    mp[(t_w + 16 * i + 4 * lg + r) * 64 + s_w + 16 * j + li] = tot[i][j][r];
+        return;
+    }
     // M^T rows s: the four t of a lane are consecutive
     E *tcol = mcol + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
     E *trow = mrow + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
@@ -585,6 +647,54 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
         const int rr = e / 16, cc = (e % 16) * 4;
         const float o[4] = {stage[rr * 65 + cc], stage[rr * 65 + cc + 1], stage[rr * 65 + cc + 2], stage[rr * 65 + cc + 3]};
         store4_f32(trow + (int64_t)(ti * 64 + rr) * Q + si * 64 + cc, o);
+    }
+}
+
+// M as the sum of k_bwd_m's hsplit parts (in split order, so the result does not
+// depend on timing), written as M (rows t) and M^T (rows s) like the unsplit
+// kernel.  One workgroup per tile unit of k_bwd_m.
+template <typename E, int Q>
+__global__ __launch_bounds__(kThreads) void k_bwd_m_reduce(const float *__restrict__ mpart, E *__restrict__ mrow,
+                                                           E *__restrict__ mcol, int G, int nc, int hsplit)
+{
+    constexpr int QT = Q / 64, NTRI = QT * (QT + 1) / 2;
+    __shared__ float stage[64 * 65];
+    const int units = NTRI * nc * G;
+    const int u = blockIdx.x, b = blockIdx.y;
+    int tile = u % NTRI;
+    const int cg = u / NTRI, g = cg % G, c = cg / G;
+    int ti = 0;
+    while (tile > ti) {
+        tile -= ti + 1;
+        ++ti;
+    }
+    const int si = tile;
+    const int64_t slice = (int64_t)gridDim.y * units * 4096;
+    const float *src = mpart + ((int64_t)b * units + u) * 4096;
+    E *trow = mrow + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+    E *tcol = mcol + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int e = (pass * kThreads + threadIdx.x) * 4;   // 4 consecutive s of row rr
+        const int rr = e / 64, cc = e % 64;
+        floatx4 v = *reinterpret_cast<const floatx4 *>(src + e);
+        for (int k = 1; k < hsplit; ++k) {
+            const floatx4 w = *reinterpret_cast<const floatx4 *>(src + k * slice + e);
+            v[0] += w[0]; v[1] += w[1]; v[2] += w[2]; v[3] += w[3];
+        }
+        const float o[4] = {v[0], v[1], v[2], v[3]};
+        store4_f32(trow + (int64_t)(ti * 64 + rr) * Q + si * 64 + cc, o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) stage[(cc + q) * 65 + rr] = o[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int e = (pass * kThreads + threadIdx.x) * 4;   // 4 consecutive t of column s = rr
+        const int rr = e / 64, cc = e % 64;
+        const float o[4] = {stage[rr * 65 + cc], stage[rr * 65 + cc + 1], stage[rr * 65 + cc + 2],
+                            stage[rr * 65 + cc + 3]};
+        store4_f32(tcol + (int64_t)(si * 64 + rr) * Q + ti * 64 + cc, o);
     }
 }
 
@@ -642,37 +752,66 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     const int hv = threadIdx.x % VPR, hr = threadIdx.x / VPR;
     uint4 rb[NPASS];
     float sc[2];     // the per-row scales of this lane's fragment rows (state part)
+    // What does not change from step to step is formed once: base pointers,
+    // buffer ranges, per-lane offsets.  A step only moves pointers by constant
+    // strides (64 columns p, or one head), which keeps the loop's scalar work
+    // small: all waves of a CU share one scalar unit, and the 64-bit index
+    // products of every step used to bound this kernel.
+    const E *bc_base = src_bc + (((int64_t)b * T + t0) * G + g) * N + n0;
+    const int64_t bc_q = (int64_t)64 * G * N;   // one 64-row M-part tile
+    const auto mrs = make_rsrc(mm + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q, (int64_t)Q * Q * ES);
+    uint32_t moff[NPASS], voff[NPASS];
+#pragma unroll
+    for (int i = 0; i < NPASS; ++i) {
+        const int r = r0 + hr + i * RPP;
+        moff[i] = r < len ? (uint32_t)((r * Q + hv * V) * ES) : kOffNone;
+        voff[i] = r < len ? (uint32_t)(((int64_t)r * H * P + hv * V) * ES) : kOffNone;
+    }
+    // state part: the (head, p chunk) of the next step
+    const E *st_ptr = states + (((int64_t)b * nc + c) * H + g * hpg) * (int64_t)P * N + n0;
+    const E *vec_ptr = vec + (((int64_t)b * T + t0) * H + g * hpg) * P;
+    const float *cs_ptr = cs + (((int64_t)b * H + g * hpg) * nc + c) * Q;
+    const float *dl_ptr = delta + (((int64_t)b * H + g * hpg) * nc + c) * Q;
+    const int64_t hrow = (int64_t)nc * Q, st_pc = (int64_t)64 * N, st_head = (int64_t)P * N - (PC - 1) * st_pc;
+    const int vbytes = rsrc_bytes(((int64_t)(len - 1) * H * P + P) * ES);
+    const int kb_full = rsrc_bytes((63 * (int64_t)N + min(N, 64)) * ES);
+    const int kb_tail = rsrc_bytes(((int64_t)(P - (PC - 1) * 64 - 1) * N + min(N, 64)) * ES);
+    int rrj[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = r0 + c_w + 16 * j + li;
+        rrj[j] = r < len ? r : 0;
+    }
+    int pc = 0;
     auto issue = [&](int k) {
         if (k < nq) {
             const int q = q_lo + k, rows = min(64, len - q * 64);
-            ka.load(KT::rsrc(src_bc + (((int64_t)b * T + t0 + q * 64) * G + g) * N + n0, (int64_t)G * N, rows));
-            const E *mb = mm + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
-            const auto mrs = make_rsrc(mb, (int64_t)Q * Q * ES);
+            ka.load(KT::rsrc(bc_base + q * bc_q, (int64_t)G * N, rows));
+            const uint32_t qo = (uint32_t)(q * 64 * ES);
 #pragma unroll
-            for (int i = 0; i < NPASS; ++i) {
-                const int r = r0 + hr + i * RPP;
-                rb[i] = bload16(mrs, r < len ? (uint32_t)(((int64_t)r * Q + q * 64 + hv * V) * ES) : kOffNone);
-            }
+            for (int i = 0; i < NPASS; ++i) rb[i] = bload16(mrs, moff[i] == kOffNone ? kOffNone : moff[i] + qo);
 #pragma unroll
             for (int j = 0; j < 2; ++j) sc[j] = 1.f;
         } else {
-            const int hk = k - nq, h = g * hpg + hk / PC, p0 = (hk % PC) * 64;
-            kb.load(KT::rsrc(states + ((((int64_t)b * nc + c) * H + h) * P + p0) * N + n0, N, min(64, P - p0)));
-            const auto vrs = make_rsrc(vec + (((int64_t)b * T + t0) * H + h) * P,
-                                       ((int64_t)(len - 1) * H * P + P) * ES);
-            const bool pin = p0 + hv * V < P;
+            const int p0 = pc * 64;
+            kb.load(make_rsrc_n(st_ptr, pc == PC - 1 ? kb_tail : kb_full));
+            const auto vrs = make_rsrc_n(vec_ptr, vbytes);
+            const bool pin = hv * V < P - p0;
 #pragma unroll
-            for (int i = 0; i < NPASS; ++i) {
-                const int r = r0 + hr + i * RPP;
-                rb[i] = bload16(vrs, (r < len && pin) ? (uint32_t)(((int64_t)r * H * P + p0 + hv * V) * ES) : kOffNone);
-            }
-            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+            for (int i = 0; i < NPASS; ++i)
+                rb[i] = bload16(vrs, (voff[i] != kOffNone && pin) ? voff[i] + (uint32_t)(p0 * ES) : kOffNone);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = r0 + c_w + 16 * j + li;
-                const int rr = r < len ? r : 0;
-                sc[j] = MODE == 0 ? __builtin_amdgcn_exp2f(cs[row + rr] * kLog2e)
-                                  : delta[row + rr] * __builtin_amdgcn_exp2f((cs[row + Q - 1] - cs[row + rr]) * kLog2e);
+            for (int j = 0; j < 2; ++j)
+                sc[j] = MODE == 0 ? __builtin_amdgcn_exp2f(cs_ptr[rrj[j]] * kLog2e)
+                                  : dl_ptr[rrj[j]] * __builtin_amdgcn_exp2f((cs_ptr[Q - 1] - cs_ptr[rrj[j]]) * kLog2e);
+            if (++pc == PC) {
+                pc = 0;
+                st_ptr += st_head;
+                vec_ptr += P;
+                cs_ptr += hrow;
+                dl_ptr += hrow;
+            } else {
+                st_ptr += st_pc;
             }
         }
     };

@@ -27,7 +27,10 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 EXPORTED = ["ssd_abi_version", "ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd",
             "ssd_chunk_cumsum", "ssd_chunk_cb", "ssd_chunk_state", "ssd_state_passing",
             "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step", "ssd_bwd_workspace_size", "ssd_bwd",
-            "ssd_fwd_gated", "ssd_conv1d_silu", "ssd_fwd_noalloc"]
+            "ssd_fwd_gated", "ssd_conv1d_silu", "ssd_fwd_noalloc", "ssd_bwd_stage_times"]
+
+# SSD_BWD_MAX_STAGES in include/ssd.h
+BWD_MAX_STAGES = 24
 
 # The static scratch of ssd_fwd_noalloc (SSD_NOALLOC_SCRATCH_BYTES in include/ssd.h).
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -453,7 +456,8 @@ def bwd_workspace_bytes(p: Problem) -> int:
 
 
 def bwd(x, dt, A, B, C, chunk, y, dy, D=None, initial_states=None, dfinal_states=None, dt_softplus=True,
-        grads=None, workspace=None, stream=None, want_dinit=True, fwd_workspace=None, seq_idx=None, nseq=None):
+        grads=None, workspace=None, stream=None, want_dinit=True, fwd_workspace=None, seq_idx=None, nseq=None,
+        stage_times=None):
     """Gradients of sum(y * dy) + sum(final_states * dfinal_states) (see ``ssd_bwd``
     in ``include/ssd.h``).  ``y`` is the forward output.  Returns a dict with dx,
     ddt, dA, dB, dC, dD (None without D) and dinitial_states (None unless
@@ -461,7 +465,9 @@ def bwd(x, dt, A, B, C, chunk, y, dy, D=None, initial_states=None, dfinal_states
     ``fwd_workspace``: the workspace of the ``fwd`` call that produced ``y`` (on
     these same inputs, untouched since), whose chunk intermediates are then read
     instead of recomputed (not for packed streams).  With ``seq_idx`` (packed
-    streams, batch 1) ``dfinal_states`` is [nseq, H, P, N], one per segment."""
+    streams, batch 1) ``dfinal_states`` is [nseq, H, P, N], one per segment.
+    ``stage_times``: a list that receives (stage name, ms) pairs; the call then
+    goes through ``ssd_bwd_stage_times`` and waits for the stream."""
     p = Problem(x, dt, A, B, C, chunk, D, initial_states, seq_idx, nseq, dt_softplus)
     _check(y, "y", x.dtype, x.shape, p.device)
     _check(dy, "dy", x.dtype, x.shape, p.device)
@@ -493,7 +499,17 @@ def bwd(x, dt, A, B, C, chunk, y, dy, D=None, initial_states=None, dfinal_states
                  workspace_bytes=workspace.numel(), fwd_workspace=_ptr(fwd_workspace),
                  fwd_workspace_bytes=0 if fwd_workspace is None else fwd_workspace.numel())
     st = stream if stream is not None else torch.cuda.current_stream(p.device).cuda_stream
-    rc = load_library().ssd_bwd(ctypes.byref(p.args), ctypes.byref(ga), ctypes.c_void_p(st))
+    if stage_times is None:
+        rc = load_library().ssd_bwd(ctypes.byref(p.args), ctypes.byref(ga), ctypes.c_void_p(st))
+        if rc != 0:
+            raise SSDError(rc, "ssd_bwd")
+        return g
+    ms = (ctypes.c_float * BWD_MAX_STAGES)()
+    names = (ctypes.c_char_p * BWD_MAX_STAGES)()
+    n = ctypes.c_int(0)
+    rc = load_library().ssd_bwd_stage_times(ctypes.byref(p.args), ctypes.byref(ga), ctypes.c_void_p(st),
+                                            BWD_MAX_STAGES, ms, names, ctypes.byref(n))
     if rc != 0:
-        raise SSDError(rc, "ssd_bwd")
+        raise SSDError(rc, "ssd_bwd_stage_times")
+    stage_times.extend((names[i].decode(), float(ms[i])) for i in range(n.value))
     return g

@@ -209,6 +209,30 @@ def test_bwd_rejects_invalid_arguments(lib, fkw, gkw, code):
     if "y" in fkw:
         a.y = fkw["y"]
     assert lib.ssd_bwd(ctypes.byref(a), ctypes.byref(_bwd_args(**gkw)), None) == code
+    # the stage-timed backward makes the same checks before it touches the GPU
+    ms = (ctypes.c_float * ssd.BWD_MAX_STAGES)()
+    names = (ctypes.c_char_p * ssd.BWD_MAX_STAGES)()
+    n = ctypes.c_int(-1)
+    assert lib.ssd_bwd_stage_times(ctypes.byref(a), ctypes.byref(_bwd_args(**gkw)), None, ssd.BWD_MAX_STAGES,
+                                   ms, names, ctypes.byref(n)) == code
+    assert n.value == 0
+
+
+def test_bwd_stage_times_rejects_short_or_missing_outputs(lib):
+    a, g = _args(), _bwd_args()
+    ms = (ctypes.c_float * ssd.BWD_MAX_STAGES)()
+    names = (ctypes.c_char_p * ssd.BWD_MAX_STAGES)()
+    n = ctypes.c_int(0)
+    f = lib.ssd_bwd_stage_times
+    assert f(ctypes.byref(a), ctypes.byref(g), None, ssd.BWD_MAX_STAGES - 1, ms, names, ctypes.byref(n)) == SHAPE
+    assert f(ctypes.byref(a), ctypes.byref(g), None, ssd.BWD_MAX_STAGES, None, names, ctypes.byref(n)) == NULLP
+    assert f(ctypes.byref(a), ctypes.byref(g), None, ssd.BWD_MAX_STAGES, ms, None, ctypes.byref(n)) == NULLP
+    assert f(ctypes.byref(a), ctypes.byref(g), None, ssd.BWD_MAX_STAGES, ms, names, None) == NULLP
+
+
+def test_bwd_max_stages_matches_the_header():
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "ssd.h")).read()
+    assert int(re.search(r"#define SSD_BWD_MAX_STAGES (\d+)", text).group(1)) == ssd.BWD_MAX_STAGES
 
 
 def test_bwd_workspace_size(lib):

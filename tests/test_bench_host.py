@@ -90,3 +90,22 @@ def test_seq_final_work_counts_each_sequences_tail_rows():
     assert w["flops"] == 2.0 * rows * H * P * N
     want = 4 * H * P * N * 4 + len(ids) * 4 + rows * (H * P * 2 + G * N * 2 + 2 * H * 4) + H * P * N * 2
     assert w["bytes"] == want
+
+
+def test_backward_stage_work_covers_every_stage():
+    """Every stage name ssd_bwd_stage_times reports has an algorithmic work entry,
+    and the products that dominate carry FLOPs."""
+    import bench
+    shape = dict(batch=1, seqlen=16384, nheads=32, headdim=64, dstate=256, ngroups=1, chunk=256)
+    w = bench.backward_stage_work(shape, 2, nseq=0)
+    names = ["chunk_cb", "chunk_state", "state_passing", "pad_layout", "reverse_rows", "chunk_cb_rev",
+             "chunk_state_grad", "inject_dfinal", "state_passing_rev", "chunk_scan_dx", "chunk_scan_dy_hin",
+             "m_rows_cols", "dl_ddt_dA_dD", "dC", "dB", "unpad_gather"]
+    assert set(names) == set(w)
+    for n in names:
+        assert w[n]["bytes"] >= 0, n
+    for n in ("chunk_state_grad", "chunk_scan_dx", "chunk_scan_dy_hin", "m_rows_cols", "dC", "dB"):
+        assert w[n]["flops"] > 0, n
+    # the reversed scan moves what the forward scan moves plus x, dx and its dot products
+    f = bench.algorithmic_work(shape, 2, None)
+    assert w["chunk_scan_dx"]["bytes"] > f["chunk_scan"]["bytes"]

@@ -338,3 +338,44 @@ def test_bwd_packed_workload_full_size():
     (segment, head) slice against the oracle."""
     inp = wl.workload(4)
     check_bwd_packed(inp, "bf16", label=inp.name)
+
+
+@pytest.mark.parametrize("mode", ["recompute", "fwd_workspace", "packed"])
+def test_bwd_stage_times(mode):
+    """The stage-timed backward computes the very gradients of ssd_bwd (bit for
+    bit) and reports every stage of its path once, with a positive duration."""
+    Q = 128
+    if mode == "packed":
+        inp = wl.make_inputs(1, None, 8, 64, 64, 2, Q, "bf16", 77, init_std=0.3,
+                             packed=dict(nseqs=5, lo=20, hi=300))
+    else:
+        inp = wl.make_inputs(2, 3 * Q + 21, 8, 64, 64, 2, Q, "bf16", 78, init_std=0.3)
+    _log(f"[bwd stage times] {mode} T={inp.x.shape[1]}")
+    g = inp.to("cuda:0")
+    nseq = inp.nseq if inp.seq_idx is not None else None
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, Q, g.D, g.initial_states, g.seq_idx, nseq)
+    fws = torch.empty(ssd.workspace_bytes(p), dtype=torch.uint8, device="cuda:0")
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, Q, D=g.D, initial_states=g.initial_states, seq_idx=g.seq_idx,
+                   nseq=nseq, workspace=fws)
+    gen = torch.Generator().manual_seed(5)
+    dy = torch.randn(tuple(inp.x.shape), generator=gen).to(torch.bfloat16).cuda()
+    dfin = torch.randn(p.final_shape(), generator=gen).cuda()
+    kw = dict(D=g.D, initial_states=g.initial_states, dfinal_states=dfin, seq_idx=g.seq_idx, nseq=nseq,
+              fwd_workspace=fws if mode == "fwd_workspace" else None)
+    a = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, Q, y, dy, **kw)
+    stages = []
+    b = ssd.bwd(g.x, g.dt, g.A, g.B, g.C, Q, y, dy, stage_times=stages, **kw)
+    torch.cuda.synchronize()
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+    names = [n for n, _ in stages]
+    core = ["reverse_rows", "chunk_cb_rev", "chunk_state_grad", "state_passing_rev", "chunk_scan_dx",
+            "chunk_scan_dy_hin", "m_rows_cols", "dl_ddt_dA_dD", "dC", "dB"]
+    want = {"recompute": ["chunk_cb", "chunk_state", "state_passing"] + core,
+            "fwd_workspace": core,
+            "packed": ["pad_layout", "chunk_cb", "chunk_state", "state_passing"] + core[:3] + ["inject_dfinal"]
+                      + core[3:] + ["unpad_gather"]}[mode]
+    assert names == want
+    assert all(ms > 0 for _, ms in stages), stages
+    _log("    " + " ".join(f"{n}={ms * 1e3:.0f}us" for n, ms in stages))
