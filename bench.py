@@ -171,14 +171,14 @@ def backward_stage_work(shape, esz, nseq=0):
     (dy in the place of x, B and C swapped, unit step size), which gives the
     gradient states G_c and dx; the rest are products with those.  FLOPs count
     the MFMA work the method needs (causal halves only), bytes each tensor a
-    stage must read or write once.  Stages that only move data (reversal, the
-    packed layout) count their copies."""
+    stage must read or write once.  Stages that only move data (the packed
+    layout) count their copies."""
     b, T, H, P, N, G, Q = (shape[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
                                              "ngroups", "chunk"))
     nc = (T + Q - 1) // Q
     causal = (Q + 1) / (2.0 * Q)
     X = b * T * H * P * esz                  # x, dy, dx
-    BC = b * T * G * N * esz                 # B, C, dB, dC (and their reversed copies)
+    BC = b * T * G * N * esz                 # B, C, dB, dC
     ST = b * nc * H * P * N * esz            # one set of chunk states
     V4 = b * H * nc * Q * 4                  # one fp32 value per (token, head)
     DT = b * T * H * esz                     # dt, ddt
@@ -188,7 +188,6 @@ def backward_stage_work(shape, esz, nseq=0):
     scan_flops = fwd["chunk_scan"]["flops"]
     w = {
         "chunk_cb": fwd["chunk_cb"], "chunk_state": fwd["chunk_state"], "state_passing": fwd["state_passing"],
-        "reverse_rows": dict(bytes=4 * BC + 3 * V4),
         "chunk_cb_rev": fwd["chunk_cb"],
         "chunk_state_grad": dict(flops=2.0 * b * T * H * P * N, bytes=X + BC + V4 + ST),
         "inject_dfinal": dict(bytes=nseq * H * P * N * (4 + esz)),

@@ -190,16 +190,21 @@ ssd_status run_cumsum(const Shape &s, const ssd_fwd_args *a, float *delta, float
     return launched();
 }
 
+// rev: every chunk's rows of a->B and a->C taken in reversed order
 template <typename E>
-ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st)
+ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, bool rev = false)
 {
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     dim3 grid((unsigned)(ntri * s.nc * s.G), (unsigned)s.b);
     return with_q(s.Q, [&](auto q) {
         return with_nt(s.N, [&](auto nt) {
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
-            hipLaunchKernelGGL((k_chunk_cb<E, Q, NT>), grid, dim3(kThreads), 0, st, (const E *)a->B,
-                               (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc);
+            if (rev)
+                hipLaunchKernelGGL((k_chunk_cb<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->B,
+                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc);
+            else
+                hipLaunchKernelGGL((k_chunk_cb<E, Q, NT>), grid, dim3(kThreads), 0, st, (const E *)a->B,
+                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc);
             return launched();
         });
     });
@@ -418,7 +423,7 @@ ssd_status run_conv(const ssd_conv_args *a, hipStream_t st)
 // backward
 // ---------------------------------------------------------------------------
 struct BwdWorkspace {
-    size_t delta, cs, cb, states, gstates, cbr, br, cr, csr, dlr, yo, zo, xyp, rpart, cpart, bnd, dyx,
+    size_t delta, cs, cb, states, gstates, cbr, yo, zo, xyp, rpart, cpart, bnd, dyx,
         mrow, mcol, dA_part, dD_part, mpart, total;
 };
 
@@ -440,7 +445,6 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     const size_t dcs = (size_t)(s.b * s.H * s.nc * s.Q) * 4;
     const size_t cbs = (size_t)(s.b * s.nc * s.G * s.Q * (s.Q + 2 * nt_of(s.N))) * s.esz;
     const size_t sts = (size_t)(s.b * s.nc * s.H * s.P * s.N) * s.esz;
-    const size_t bcs = (size_t)(s.b * s.T * s.G * s.N) * s.esz;
     const size_t ms = (size_t)(s.b * s.nc * s.G * s.Q * s.Q) * s.esz;
     const size_t bh = (size_t)(s.b * s.H) * 4;
     const size_t ntp = (size_t)((s.P + 63) / 64), qt = (size_t)(s.Q / 64);
@@ -452,10 +456,6 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
     w.states = take(sts);
     w.gstates = take(sts);
     w.cbr = take(cbs);
-    w.br = take(bcs);
-    w.cr = take(bcs);
-    w.csr = take(dcs);
-    w.dlr = take(dcs);
     w.yo = take(ntp * dcs);
     w.zo = take(ntp * dcs);
     w.xyp = take(ntp * dcs);
@@ -545,11 +545,11 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     char *ws = static_cast<char *>(g->workspace);
     auto F32 = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
     auto EP = [&](size_t off) { return reinterpret_cast<E *>(ws + off); };
-    float *delta = F32(w.delta), *cs = F32(w.cs), *csr = F32(w.csr), *dlr = F32(w.dlr);
+    float *delta = F32(w.delta), *cs = F32(w.cs);
     float *yo = F32(w.yo), *zo = F32(w.zo), *xyp = F32(w.xyp), *rpart = F32(w.rpart), *cpart = F32(w.cpart);
     float *bnd = F32(w.bnd), *dyx = F32(w.dyx), *dA_part = F32(w.dA_part), *dD_part = F32(w.dD_part);
     E *cb = EP(w.cb), *states = EP(w.states), *gstates = EP(w.gstates), *cbr = EP(w.cbr);
-    E *br = EP(w.br), *cr = EP(w.cr), *mrow = EP(w.mrow), *mcol = EP(w.mcol);
+    E *mrow = EP(w.mrow), *mcol = EP(w.mcol);
     ssd_status r;
     ssd_fwd_args f = *a;
     f.final_states = nullptr;
@@ -570,30 +570,19 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         if ((r = run_passing<E>(s, &f, cs, states, nullptr, st, cseg)) != SSD_OK) return r;
         mark("state_passing");
     }
-    // 2. every chunk's tokens in reversed order: B, C, and the reversed cs / delta
-    //    (dy is read reversed by the kernels themselves)
-    constexpr int V = kVec16<E>;
-    const int64_t vbc = s.b * s.T * s.G * s.N / V;
-    hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vbc, 256)), dim3(256), 0, st, (const E *)a->B, br,
-                       (int)s.T, (int)s.Q, s.G * s.N, vbc);
-    hipLaunchKernelGGL(k_bwd_reverse_rows<E>, dim3(grid1(vbc, 256)), dim3(256), 0, st, (const E *)a->C, cr,
-                       (int)s.T, (int)s.Q, s.G * s.N, vbc);
-    const int64_t ncs = s.b * s.H * s.nc * s.Q;
-    hipLaunchKernelGGL(k_bwd_reverse_cs, dim3(grid1(ncs, 256)), dim3(256), 0, st, cs, csr, dlr, (int)s.T, (int)s.Q,
-                       (int)s.nc, ncs);
-    if ((r = launched()) != SSD_OK) return r;
-    mark("reverse_rows");
-    // 3. reversed-order problem: x <- dy, B <- C, C <- B, unit step size, no skip
-    //    term; its output is turned into dx = Delta y' + D dy in original order
+    // 2-3. reversed-order problem: every chunk's tokens in reversed order, x <- dy,
+    //    B <- C, C <- B, unit step size, no skip term; its output is turned into
+    //    dx = Delta y' + D dy in original order.  No reversed copies: the kernels
+    //    read dy, B, C and cs reversed themselves.
     ssd_fwd_args rv = *a;
     rv.x = g->dy;
-    rv.B = cr;
-    rv.C = br;
+    rv.B = a->C;
+    rv.C = a->B;
     rv.D = nullptr;
     rv.y = g->dx;
     rv.initial_states = nullptr;
     rv.final_states = nullptr;
-    if ((r = run_cb<E>(s, &rv, cbr, st)) != SSD_OK) return r;
+    if ((r = run_cb<E>(s, &rv, cbr, st, true)) != SSD_OK) return r;
     mark("chunk_cb_rev");
     // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
     if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st)) != SSD_OK) return r;
@@ -613,7 +602,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     mark("state_passing_rev");
     // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y';
     //    it writes dx = Delta y' + D dy, and dy . x per (token, head)
-    if ((r = run_scan_dot<E, 2, false>(s, &rv, dlr, csr, cbr, gstates, (const E *)a->x, zo, xyp, st, delta,
+    if ((r = run_scan_dot<E, 2, false>(s, &rv, nullptr, cs, cbr, gstates, (const E *)a->x, zo, xyp, st, delta,
                                        a->D, dyx)) != SSD_OK)
         return r;
     mark("chunk_scan_dx");

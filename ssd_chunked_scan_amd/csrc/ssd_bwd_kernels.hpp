@@ -36,44 +36,6 @@
 namespace ssd {
 
 // ---------------------------------------------------------------------------
-// token order reversed inside every chunk
-// ---------------------------------------------------------------------------
-// out[b, c*Q + (len_c - 1 - i), :] = in[b, c*Q + i, :] for the len_c tokens of
-// chunk c; rows hold R elements (R * sizeof(E) a multiple of 16 bytes).
-template <typename E>
-__global__ void k_bwd_reverse_rows(const E *__restrict__ in, E *__restrict__ out, int T, int Q, int64_t R,
-                                   int64_t total_vecs)
-{
-    constexpr int V = kVec16<E>;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total_vecs) return;
-    const int64_t vpr = R / V;
-    const int64_t row = i / vpr, v = i % vpr;   // row = b * T + t
-    const int b = (int)(row / T), t = (int)(row % T);
-    const int c = t / Q, k = t % Q, len = min(Q, T - c * Q);
-    const int tr = c * Q + (len - 1 - k);
-    *reinterpret_cast<uint4 *>(out + ((int64_t)b * T + tr) * R + v * V) =
-        *reinterpret_cast<const uint4 *>(in + row * R + v * V);
-}
-
-// For the reversed chunk (rows [b,H,nc,Q]): cs_rev[i] = cs[len-1] - cs[len-1-i]
-// and delta_rev[i] = 1 for i < len; past len cs_rev keeps its last value and
-// delta_rev is 0 (as the forward leaves positions past the sequence end).
-__global__ void k_bwd_reverse_cs(const float *__restrict__ cs, float *__restrict__ cs_rev,
-                                 float *__restrict__ delta_rev, int T, int Q, int nc, int64_t total)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const int64_t row = i / Q;   // (b * H + h) * nc + c
-    const int k = (int)(i % Q), c = (int)(row % nc);
-    const int len = min(Q, T - c * Q);
-    const float *r = cs + row * Q;
-    const int kk = k < len ? k : len - 1;
-    cs_rev[i] = r[len - 1] - r[len - 1 - kk];
-    delta_rev[i] = k < len ? 1.f : 0.f;
-}
-
-// ---------------------------------------------------------------------------
 // packed streams: a layout in which every segment starts at a chunk start
 // ---------------------------------------------------------------------------
 // The backward of a packed stream runs on a copy of the stream laid out so that
@@ -708,9 +670,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m_reduce(const float *__restri
 // loads (whole 128-byte rows; loading the second operand as MFMA fragments,
 // 16 rows x 64 bytes per instruction, made the kernel three times slower):
 //   MODE 0, dC:  K = s over the s-tiles <= this tile:  B rows s   x  M[t][s]
-//                K = p over the group's heads:         Hin_h[p]   x  exp(cs_t) dy_h[t][p]
+//                K = p over the group's heads:         exp(cs_t) (Hin_h[p]  x  dy_h[t][p])
 //   MODE 1, dB:  K = t over the t-tiles >= this tile:  C rows t   x  M^T[s][t]
-//                K = p over the group's heads:         G_h[p]     x  Delta_s exp(cs_last - cs_s) x_h[s][p]
+//                K = p over the group's heads:         Delta_s exp(cs_last - cs_s) (G_h[p]  x  x_h[s][p])
+// (the per-row factor of a head multiplies its finished product, in fp32).
 // Hin / G are the states entering / leaving the chunk ([b,nc,H,P,N] in E).
 template <typename E, int Q, int MODE>
 __global__ __launch_bounds__(kThreads) void k_bwd_bc(
@@ -820,7 +783,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     typename KT::Off aoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) aoff[i] = KT::frag_off(n_w + 16 * i);
+    // The state part's per-row scale is the same for every column of a row and
+    // every p of a head, so each head's product is formed unscaled in `part`
+    // and added to the total with the scale of its rows (column r = lane's
+    // c_w + 16 j + li of D) once the head's last p chunk is in; M-part steps
+    // are added unscaled.
+    floatx4 part[2][2] = {};
     issue(0);
+    int kpc = 0;   // the p chunk of a state-part step
     for (int k = 0; k < steps; ++k) {
         if (k > 0) __syncthreads();   // every wave is done reading the previous tile
         const bool mpart = k < nq;
@@ -835,18 +805,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            F fa[2], fbv[2];
+            F fa[2], fb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) fa[i] = KT::frag_at(kt, aoff[i], ks * 32);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const F f = load_frag(bt + (c_w + 16 * j + li) * PITCH + ks * 32 + 8 * lg);
-                fbv[j] = mpart ? f : from_f32<F>(to_f32(f) * cs_[j]);
-            }
+            for (int j = 0; j < 2; ++j) fb[j] = load_frag(bt + (c_w + 16 * j + li) * PITCH + ks * 32 + 8 * lg);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) mma(acc[i][j], fa[i], fbv[j]);
+                for (int j = 0; j < 2; ++j) mma(part[i][j], fa[i], fb[j]);
+        }
+        bool fold = mpart;
+        if (!mpart) {
+            fold = kpc == PC - 1;
+            kpc = fold ? 0 : kpc + 1;
+        }
+        if (fold) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[i][j][e] += part[i][j][e] * cs_[j];
+                        part[i][j][e] = 0.f;
+                    }
         }
     }
 

@@ -204,7 +204,10 @@ template <int Q, int NT> constexpr int64_t cb_group_elems() { return (int64_t)Q 
 // (A = B rows, B = C rows, K = n).  The result goes through LDS to leave in
 // fragment-major order; the tiles of the first s-tile also copy their C rows,
 // and the diagonal tiles write B^T of their s rows.
-template <typename E, int Q, int NT>
+// REV reads every chunk's rows in reversed order (row i of a chunk of len rows
+// is source row len - 1 - i), which is the backward pass's time-reversed
+// problem, without a reversed copy of B and C.
+template <typename E, int Q, int NT, bool REV = false>
 __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm, const E *__restrict__ Cm,
                                                        E *__restrict__ cbuf, int T, int G, int N, int nc)
 {
@@ -239,15 +242,29 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm,
         return make_rsrc(m + (((int64_t)b * T + t0 + r0) * G + g) * N,
                          rows > 0 ? ((int64_t)(rows - 1) * G * N + N) * ES : 0);
     };
-    const auto brs = rows_rsrc(Bm, si * 64), crs = rows_rsrc(Cm, ti * 64);
+    // REV: the whole chunk's rows, tile row i of tile r0 at source row len - 1 - (r0 + i)
+    const auto chunk_rsrc = [&](const E *m) {
+        return make_rsrc(m + (((int64_t)b * T + t0) * G + g) * N, ((int64_t)(len - 1) * G * N + N) * ES);
+    };
+    auto rev_off = [&](int r0, int i) {
+        const int q = r0 + hr + i * RPP;
+        return (voff == kOffNone || q >= len) ? kOffNone
+                                              : (uint32_t)((int64_t)(len - 1 - q) * G * N * ES + hv * 16);
+    };
+    const auto brs = REV ? chunk_rsrc(Bm) : rows_rsrc(Bm, si * 64), crs = REV ? chunk_rsrc(Cm) : rows_rsrc(Cm, ti * 64);
 #pragma unroll
     for (int i0 = 0; i0 < NPASS; i0 += PG) {
         uint4 rb[PG], rc[PG];
 #pragma unroll
         for (int i = 0; i < PG; ++i) {
-            const uint32_t o = voff == kOffNone ? kOffNone : voff + (uint32_t)((i0 + i) * RPP * G * N * ES);
-            rb[i] = bload16(brs, o);
-            rc[i] = bload16(crs, o);
+            if constexpr (REV) {
+                rb[i] = bload16(brs, rev_off(si * 64, i0 + i));
+                rc[i] = bload16(crs, rev_off(ti * 64, i0 + i));
+            } else {
+                const uint32_t o = voff == kOffNone ? kOffNone : voff + (uint32_t)((i0 + i) * RPP * G * N * ES);
+                rb[i] = bload16(brs, o);
+                rc[i] = bload16(crs, o);
+            }
         }
 #pragma unroll
         for (int i = 0; i < PG; ++i) {
@@ -1188,8 +1205,10 @@ template <int Q> constexpr int scan_threads() { return Q * 2; }
 // Dot modes (used by the backward pass; DOT = 0 is the forward): with v = `vec`
 // at each token's position (DOT = 1) or at the mirrored position len-1-t of a
 // chunk whose tokens were reversed (DOT = 2: x is passed in its own order and its
-// rows are read reversed here; every other input comes reversed from the
-// caller), the kernel also writes, per token,
+// rows are read reversed here; `cs` is the forward's, from which the reversed
+// chunk's cs_rev[i] = cs[len-1] - cs[len-1-i] is formed here, with unit step
+// sizes and `delta` unused; the chunk_cb buffer and the states come reversed
+// from the caller), the kernel also writes, per token,
 // fp32 dot products over this workgroup's 64 p (one [b,H,nc,Q] slice per p tile,
 // indexed by the token's original position):
 //   dot1 = v . (the entering-state term alone),  dot2 (DOT = 2) = v . (the whole
@@ -1275,8 +1294,15 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     float c_i = 0.f, d_i = 0.f;
     int s_i = 0;
     if (threadIdx.x < Q) {
-        c_i = cs[cso + threadIdx.x] * kLog2e;   // decays below are exp2 of differences
-        d_i = delta[cso + threadIdx.x];
+        if constexpr (DOT == 2) {
+            // the reversed chunk; past len cs_rev keeps its last value, with step size 0
+            const int kk = (int)threadIdx.x < len ? (int)threadIdx.x : len - 1;
+            c_i = (cs[cso + len - 1] - cs[cso + len - 1 - kk]) * kLog2e;
+            d_i = (int)threadIdx.x < len ? 1.f : 0.f;
+        } else {
+            c_i = cs[cso + threadIdx.x] * kLog2e;   // decays below are exp2 of differences
+            d_i = delta[cso + threadIdx.x];
+        }
         if (PACKED) s_i = seq_idx[t0 + min((int)threadIdx.x, len - 1)];
     }
     const int seq_prev = PACKED ? seq_idx[c > 0 ? t0 - 1 : 0] : 0;

@@ -98,7 +98,7 @@ def test_backward_stage_work_covers_every_stage():
     import bench
     shape = dict(batch=1, seqlen=16384, nheads=32, headdim=64, dstate=256, ngroups=1, chunk=256)
     w = bench.backward_stage_work(shape, 2, nseq=0)
-    names = ["chunk_cb", "chunk_state", "state_passing", "pad_layout", "reverse_rows", "chunk_cb_rev",
+    names = ["chunk_cb", "chunk_state", "state_passing", "pad_layout", "chunk_cb_rev",
              "chunk_state_grad", "inject_dfinal", "state_passing_rev", "chunk_scan_dx", "chunk_scan_dy_hin",
              "m_rows_cols", "dl_ddt_dA_dD", "dC", "dB", "unpad_gather"]
     assert set(names) == set(w)

@@ -370,12 +370,12 @@ def test_bwd_stage_times(mode):
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), k
     names = [n for n, _ in stages]
-    core = ["reverse_rows", "chunk_cb_rev", "chunk_state_grad", "state_passing_rev", "chunk_scan_dx",
+    core = ["chunk_cb_rev", "chunk_state_grad", "state_passing_rev", "chunk_scan_dx",
             "chunk_scan_dy_hin", "m_rows_cols", "dl_ddt_dA_dD", "dC", "dB"]
     want = {"recompute": ["chunk_cb", "chunk_state", "state_passing"] + core,
             "fwd_workspace": core,
-            "packed": ["pad_layout", "chunk_cb", "chunk_state", "state_passing"] + core[:3] + ["inject_dfinal"]
-                      + core[3:] + ["unpad_gather"]}[mode]
+            "packed": ["pad_layout", "chunk_cb", "chunk_state", "state_passing"] + core[:2] + ["inject_dfinal"]
+                      + core[2:] + ["unpad_gather"]}[mode]
     assert names == want
     assert all(ms > 0 for _, ms in stages), stages
     _log("    " + " ".join(f"{n}={ms * 1e3:.0f}us" for n, ms in stages))
