@@ -12,7 +12,10 @@ input already resident in HBM.  Prints ONE JSON line:
   warm         the same K steps back to back (wall clock between synchronisations)
   roofline     the dominant kernel's achieved algorithmic bytes/s (or FLOP/s) per
                launch, from HIP events recorded on the launch stream, against
-               MI355X's published peak
+               MI355X's published peak; traffic = its HBM bytes per launch from
+               the committed FETCH_SIZE / WRITE_SIZE records (scaled by a plain
+               copy's reading), traffic_requests = the same from the per-size
+               request counters (null once the kernel sources change)
   step_ms      p10/p50/p90 of single steps between HIP events, cold and warm
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same workload
   kernels      per-kernel breakdown of the headline workload (average ms per
@@ -21,8 +24,10 @@ input already resident in HBM.  Prints ONE JSON line:
                standalone cumsum step, which ssd_fwd runs inside chunk_state
   workloads    the same forward measurements (cold and warm rates, TFLOP/s,
                per-kernel fractions) for every one of the five workloads
-  backward     ssd_bwd on the same workload (all input gradients): time per call;
-               backward_packed the same on the packed workload
+  backward     ssd_bwd on the same workload (all input gradients): time per call,
+               and per stage (ssd_bwd_stage_times: HIP events between the
+               stages of one call) placed on the roofline; backward_packed the
+               same on the packed workload
   decode       the decode step (one token per sequence, state carried) on its own
                seeded workload: time per launch, tokens/s and its HBM roofline
   block        the convolution prologue and the gated forward
@@ -60,10 +65,9 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    FETCH_SIZE / WRITE_SIZE counter records (already scaled by the plain-copy
-    calibration), or None when no record exists or the kernels changed since."""
+def traffic_record(kernel, workload):
+    """The committed HBM-traffic counter record of `kernel` on `workload`, or
+    None when no record exists or the kernel sources changed since it was taken."""
     import glob
     src = kernel_source_hash()
     for path in sorted(glob.glob(os.path.join(PROFILES, "*hbm_traffic*.md"))):
@@ -73,8 +77,24 @@ def measured_traffic(kernel, workload):
                     continue
                 rec = json.loads(line[len("traffic-record: "):])
                 if rec["kernel"] == kernel and rec["workload"] == workload and rec["source_sha256"] == src:
-                    return int(rec["fetch_bytes"] + rec["write_bytes"])
+                    return rec
     return None
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload`: FETCH_SIZE + WRITE_SIZE,
+    each scaled by what it reads for a plain device copy of known size in the
+    same run; None without a current record."""
+    rec = traffic_record(kernel, workload)
+    return None if rec is None else int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
+def measured_traffic_requests(kernel, workload):
+    """The same bytes from the L2-to-fabric request counters by request size
+    (read: 32, 64 and 128 B requests; write: 64 B requests and the rest at 32
+    B), which need no calibration; None without a current record."""
+    rec = traffic_record(kernel, workload)
+    return None if rec is None or "read_req_bytes" not in rec else int(rec["read_req_bytes"] + rec["write_req_bytes"])
 
 
 def measured_mfma(kernel, workload):
@@ -548,6 +568,9 @@ def measure_forward(idx, dev, steps, warmup, kreps, flush):
     kernels = {}
     for n in names:
         kernels[n] = dict(ms=round(kms[n], 5), **roofline_point(work[n], kms[n] / 1e3, esz))
+        kernels[n]["algorithmic_bytes"] = int(work[n]["bytes"])
+        kernels[n]["traffic"] = measured_traffic(n, cfg["name"])
+        kernels[n]["traffic_requests"] = measured_traffic_requests(n, cfg["name"])
         if work[n].get("flops"):
             kernels[n]["mfma_busy_pct"] = measured_mfma(n, cfg["name"])
     kernels["chunk_cumsum"]["note"] = "standalone; ssd_fwd runs this step inside chunk_state"
@@ -624,6 +647,7 @@ def main():
                 "unit": kd["unit"], "frac": kd["frac"], "mfma_frac": kd.get("mfma_frac"),
                 "hbm_frac": kd["hbm_frac"], "flop_per_byte": kd.get("flop_per_byte"),
                 "traffic": measured_traffic(dom, cfg["name"]), "traffic_unit": "HBM bytes per launch",
+                "traffic_requests": measured_traffic_requests(dom, cfg["name"]),
                 "algorithmic_bytes": int(work[dom]["bytes"]),
                 "mfma_busy_pct": measured_mfma(dom, cfg["name"])}
     workloads = {}
