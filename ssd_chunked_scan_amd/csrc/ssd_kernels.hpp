@@ -1122,6 +1122,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
         return;
     }
     const int c = te / Q, t0 = c * Q, ie = te - t0;
+    // The entering-state tile is requested first, with the chunk's x and B rows
+    // (one round trip less than after the product), and used only when the
+    // segment was already open at the chunk start.
+    using RV = typename RawVec<E, 4>::type;
+    RV hraw[NI][4];
+    const E *hc = hin + ((int64_t)c * H + h) * (int64_t)P * N;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = p0 + j * 16 + li;
+            hraw[i][j] = (p < P && n < N) ? *reinterpret_cast<const RV *>(hc + (int64_t)p * N + n) : RV{};
+        }
+    const bool carry = seq_idx[c > 0 ? t0 - 1 : 0] == sg;
     const E *xsrc = x + ((int64_t)t0 * H + h) * P + p0;
     const E *bsrc = Bm + ((int64_t)t0 * G + g) * N;
     const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
@@ -1148,17 +1162,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     state_product<E, NT, true>(sm, xsrc, ldx, bsrc, ldb, ie + 1, w, m, xs, bs, acc);
 
-    const bool carry = seq_idx[c > 0 ? t0 - 1 : 0] == sg;
     const float dcar = exp_neg(cse);
-    const E *hc = hin + ((int64_t)c * H + h) * (int64_t)P * N;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n = wave * (NT / 4) + i * 16 + 4 * lg, p = p0 + j * 16 + li;
             if (p < P && n < N) {
-                float hv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (carry) load4_f32(hc + (int64_t)p * N + n, hv);
+                float hv[4];
+                unpack_vec<E, 4>(hraw[i][j], hv);
                 float o[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] = acc[i][j][q] + (carry ? dcar * hv[q] : 0.f);
