@@ -428,13 +428,14 @@ struct BwdWorkspace {
 };
 
 // Workgroups of k_bwd_m split the group's heads hsplit ways when its tiles alone
-// would leave the GPU short of workgroups (about 2048 wanted: 256 CUs, several
-// each); every split keeps at least one head.
+// would leave the GPU short of workgroups (about 1024 wanted: 256 CUs, four
+// each; every split adds an fp32 tile of partial sums to write and read back);
+// every split keeps at least one head.
 int64_t bwd_m_hsplit(const Shape &s)
 {
     const int64_t qt = s.Q / 64, tiles = qt * (qt + 1) / 2 * s.nc * s.G * s.b;
     const int64_t hpg = s.H / s.G;
-    int64_t k = (2048 + tiles - 1) / tiles;
+    int64_t k = (1024 + tiles - 1) / tiles;
     if (k > hpg) k = hpg;
     return k < 1 ? 1 : k;
 }
