@@ -6,9 +6,11 @@ inside, state_passing, [seq_final], chunk_scan) over one batch of seeded synthet
 input already resident in HBM.  Prints ONE JSON line:
 
   value        tokens/s of the headline workload over the K timed steps, each
-               step cold: a 1 GiB write before it (outside its HIP events)
-               evicts L2 and the 256 MB MALL, so every input comes from HBM;
-               ms_per_step is the mean cold step
+               step cold: a 1 GiB write and a read of it before the step
+               (outside its HIP events) evict L2 and the 256 MB MALL, so every
+               input comes from HBM, and leave the caches clean, so no
+               write-back of the flush lands in the step; ms_per_step is the
+               mean cold step
   warm         the same K steps back to back (wall clock between synchronisations)
   roofline     the dominant kernel's achieved algorithmic bytes/s (or FLOP/s) per
                launch, from HIP events recorded on the launch stream, against
@@ -502,11 +504,16 @@ def measure_forward(idx, dev, steps, warmup, kreps, flush):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # cold: K steps, each after a 1 GiB write that evicts L2 and the MALL
+    # cold: K steps, each after a 1 GiB write and a read of the same buffer
+    # (outside the events).  The write evicts L2 and the MALL; the read makes
+    # the lines left in them clean, so that no write-back of the flush itself
+    # falls inside the timed step.
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     for r in range(steps):
         flush.fill_(float(r))
+        torch.sum(flush, 0, out=sink)
         pairs[r][0].record(stream)
         step()
         pairs[r][1].record(stream)
@@ -690,8 +697,9 @@ def main():
         "config": {"workload": cfg["name"], "batch": b, "seqlen": T, "nheads": H, "headdim": P,
                    "dstate": inp.B.shape[3], "ngroups": inp.B.shape[2], "chunk": inp.chunk,
                    "real_tokens": inp.real_tokens},
-        "timing": "value and ms_per_step: the K timed steps, each cold (a 1 GiB write before it, "
-                  "outside its HIP events, evicts L2 and MALL); warm: the same K steps back to back",
+        "timing": "value and ms_per_step: the K timed steps, each cold (a 1 GiB write and a read of it "
+                  "before the step, outside its HIP events, evict L2 and MALL and leave them clean); "
+                  "warm: the same K steps back to back",
         "tflops": cold["tflops"],
         "warm": summ["warm"],
         "roofline": roofline,
