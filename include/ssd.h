@@ -198,6 +198,18 @@ ssd_status ssd_state_passing(const ssd_fwd_args *args, const float *cs, void *st
 ssd_status ssd_seq_final_states(const ssd_fwd_args *args, const float *delta, const float *cs,
                                 const void *states, int32_t *seg_end, void *stream);
 
+/* A debug aid for packed streams: checks on the device the precondition that
+ * ssd_fwd, ssd_bwd and the step calls take on trust (the library never reads
+ * device memory from the host), namely that seq_idx[0..seqlen-1] holds
+ * non-decreasing ids in [0, nseq).  Enqueues one small kernel on `stream` that
+ * writes to *first_bad (device int32) the first position t whose id is outside
+ * [0, nseq) or smaller than the id at t-1, or -1 when the stream is valid; the
+ * caller reads it after the stream.  Errors: SSD_ERR_NULL_POINTER (first_bad,
+ * or seq_idx with seqlen > 0), SSD_ERR_BAD_SHAPE (seqlen < 0 or > INT32_MAX),
+ * SSD_ERR_SEQ_IDX (nseq < 1), SSD_ERR_MISALIGNED (either pointer not 4-byte
+ * aligned). */
+ssd_status ssd_check_seq_idx(const int32_t *seq_idx, int64_t seqlen, int64_t nseq, int32_t *first_bad, void *stream);
+
 /* Steps 1 and 4 ("chunk_scan"): y = intra-chunk masked quadratic form plus the
  * decayed contribution of the state entering each chunk plus D*x.  `states` holds
  * the entering states as left by ssd_state_passing. */

@@ -62,6 +62,7 @@ ssd_status parse_shape(const ssd_fwd_args *a, Shape *s)
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 struct Range {
     const void *p;
@@ -1003,6 +1004,17 @@ ssd_status ssd_state_passing(const ssd_fwd_args *args, const float *cs, void *st
     float *fin = s.packed ? nullptr : args->final_states;
     return s.dtype == SSD_DTYPE_BF16 ? run_passing<bf16>(s, args, cs, (bf16 *)states, fin, st)
                                      : run_passing<float>(s, args, cs, (float *)states, fin, st);
+}
+
+ssd_status ssd_check_seq_idx(const int32_t *seq_idx, int64_t seqlen, int64_t nseq, int32_t *first_bad, void *stream)
+{
+    if (!first_bad || (seqlen > 0 && !seq_idx)) return SSD_ERR_NULL_POINTER;
+    if (seqlen < 0 || seqlen > INT32_MAX) return SSD_ERR_BAD_SHAPE;
+    if (nseq < 1) return SSD_ERR_SEQ_IDX;
+    if (!aligned4(seq_idx) || !aligned4(first_bad)) return SSD_ERR_MISALIGNED;
+    hipLaunchKernelGGL(k_check_seq_idx, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), seq_idx, seqlen,
+                       nseq, first_bad);
+    return launched();
 }
 
 ssd_status ssd_seq_final_states(const ssd_fwd_args *args, const float *delta, const float *cs,

@@ -1077,6 +1077,36 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
 // ---------------------------------------------------------------------------
 // Packed streams: segment ends and per-segment final states
 // ---------------------------------------------------------------------------
+// The packed-stream precondition, checked on the device (ssd_check_seq_idx):
+// one workgroup scans the ids; *first_bad receives the first position t whose
+// id is outside [0, nseq) or smaller than the id at t-1, or -1 when there is
+// none.  Each thread keeps the smallest bad position it saw, and the workgroup
+// takes the minimum, so the result does not depend on thread timing.
+__global__ __launch_bounds__(1024) void k_check_seq_idx(const int32_t *__restrict__ seq_idx, int64_t T, int64_t nseq,
+                                                        int32_t *__restrict__ first_bad)
+{
+    __shared__ int64_t wmin[16];
+    int64_t bad = T;
+    for (int64_t t = threadIdx.x; t < T; t += blockDim.x) {
+        const int32_t id = seq_idx[t];
+        if (id < 0 || id >= nseq || (t > 0 && id < seq_idx[t - 1])) {
+            bad = t;   // t only grows, so the first hit is this thread's smallest
+            break;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const int64_t v = __shfl_xor(bad, o);
+        bad = v < bad ? v : bad;
+    }
+    if ((threadIdx.x & 63) == 0) wmin[threadIdx.x >> 6] = bad;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) bad = wmin[w] < bad ? wmin[w] : bad;
+        *first_bad = bad < T ? (int32_t)bad : -1;
+    }
+}
+
 // seg_end for every segment, one thread per position (seg_end_mark).
 __global__ void k_seg_end(const int32_t *__restrict__ seq_idx, int32_t *__restrict__ seg_end, int T, int nseq)
 {

@@ -27,7 +27,7 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 EXPORTED = ["ssd_abi_version", "ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd",
             "ssd_chunk_cumsum", "ssd_chunk_cb", "ssd_chunk_state", "ssd_state_passing",
             "ssd_seq_final_states", "ssd_chunk_scan", "ssd_step", "ssd_bwd_workspace_size", "ssd_bwd",
-            "ssd_fwd_gated", "ssd_conv1d_silu", "ssd_fwd_noalloc", "ssd_bwd_stage_times"]
+            "ssd_fwd_gated", "ssd_conv1d_silu", "ssd_fwd_noalloc", "ssd_bwd_stage_times", "ssd_check_seq_idx"]
 
 # SSD_BWD_MAX_STAGES in include/ssd.h
 BWD_MAX_STAGES = 24
@@ -210,6 +210,22 @@ class Problem:
         rc = getattr(lib, name)(ctypes.byref(self.args), *ptrs, ctypes.c_void_p(st))
         if rc != 0:
             raise SSDError(rc, name)
+
+
+def check_seq_idx(seq_idx: torch.Tensor, nseq: int, stream=None) -> int:
+    """``ssd_check_seq_idx``: the first position whose segment id breaks the
+    packed-stream precondition (ids non-decreasing, in [0, nseq)), or -1.
+    Waits for the stream to read the result."""
+    if seq_idx.dtype != torch.int32 or seq_idx.device.type != "cuda" or not seq_idx.is_contiguous():
+        raise ValueError("seq_idx must be a contiguous int32 device tensor")
+    out = torch.empty((), dtype=torch.int32, device=seq_idx.device)
+    st = stream if stream is not None else torch.cuda.current_stream(seq_idx.device).cuda_stream
+    rc = load_library().ssd_check_seq_idx(ctypes.c_void_p(seq_idx.data_ptr()), ctypes.c_int64(seq_idx.numel()),
+                                          ctypes.c_int64(nseq), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st))
+    if rc != 0:
+        raise SSDError(rc, "ssd_check_seq_idx")
+    torch.cuda.synchronize(seq_idx.device)
+    return int(out.item())
 
 
 def workspace_bytes(p: Problem) -> int:

@@ -305,3 +305,16 @@ def test_conv_binding_checks_shapes():
         ssd.conv1d_silu(xbc, torch.zeros(96, 4), 4, 16, 1, 16)
     with pytest.raises(ValueError, match="channels"):
         ssd.conv1d_silu(xbc, torch.zeros(96, 4), 4, 16, 1, 32)
+
+
+def test_check_seq_idx_rejects_invalid_arguments(lib):
+    p = ctypes.c_void_p
+    f = lib.ssd_check_seq_idx
+    i64 = ctypes.c_int64
+    assert f(p(0x90000000), i64(100), i64(3), None, None) == NULLP
+    assert f(None, i64(100), i64(3), p(0x90001000), None) == NULLP
+    assert f(p(0x90000000), i64(-1), i64(3), p(0x90001000), None) == SHAPE
+    assert f(p(0x90000000), i64(1 << 31), i64(3), p(0x90001000), None) == SHAPE
+    assert f(p(0x90000000), i64(100), i64(0), p(0x90001000), None) == SEQ
+    assert f(p(0x90000002), i64(100), i64(3), p(0x90001000), None) == MISAL
+    assert f(p(0x90000000), i64(100), i64(3), p(0x90001002), None) == MISAL

@@ -513,3 +513,28 @@ def test_fwd_reads_nothing_past_the_last_row(dtype):
     ref = run_oracle(inp)
     assert max_rel_y(y, ref.y, inp) <= TOL[DT[dtype]]
     assert max_rel_states(fs, ref.final_states) <= TOL[DT[dtype]]
+
+
+def test_check_seq_idx_finds_the_first_violation():
+    """The device-side precondition check: -1 for valid packed ids (including
+    ids that never occur and an empty stream), else the first position whose id
+    is out of range or smaller than its predecessor's."""
+    dev = torch.device("cuda:0")
+    lengths = [37, 90, 5, 61, 140, 23, 9, 200, 1, 4000]
+    ids = np.concatenate([np.full(L, 2 * i, np.int32) for i, L in enumerate(lengths)])   # odd ids never occur
+    nseq = 2 * len(lengths)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    assert ssd.check_seq_idx(t(ids), nseq) == -1
+    assert ssd.check_seq_idx(t(ids[:0]), nseq) == -1
+    bad = ids.copy(); bad[777] = bad[776] - 1          # decreasing
+    assert ssd.check_seq_idx(t(bad), nseq) == 777
+    bad = ids.copy(); bad[3000] = nseq                 # out of range (and later ids smaller)
+    assert ssd.check_seq_idx(t(bad), nseq) == 3000
+    bad = ids.copy(); bad[0] = -1                      # negative
+    assert ssd.check_seq_idx(t(bad), nseq) == 0
+    bad = ids.copy(); bad[4000] = 0; bad[100] = -5     # two violations: the first one counts
+    assert ssd.check_seq_idx(t(bad), nseq) == 100
+    big = np.repeat(np.arange(1000, dtype=np.int32), 1024)   # a million positions
+    assert ssd.check_seq_idx(t(big), 1000) == -1
+    big[len(big) - 1] = 998
+    assert ssd.check_seq_idx(t(big), 1000) == len(big) - 1
