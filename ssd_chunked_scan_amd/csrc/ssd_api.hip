@@ -191,9 +191,12 @@ ssd_status run_cumsum(const Shape &s, const ssd_fwd_args *a, float *delta, float
     return launched();
 }
 
-// rev: every chunk's rows of a->B and a->C taken in reversed order
+// rev: every chunk's rows of a->B and a->C taken in reversed order.  cseg (the
+// packed backward's layout, see run_passing): chunks of padding only are
+// skipped, here and in the other per-chunk launches that take it.
 template <typename E>
-ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, bool rev = false)
+ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, bool rev = false,
+                  const int32_t *cseg = nullptr)
 {
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     dim3 grid((unsigned)(ntri * s.nc * s.G), (unsigned)s.b);
@@ -202,10 +205,10 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, 
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
             if (rev)
                 hipLaunchKernelGGL((k_chunk_cb<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->B,
-                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc);
+                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc, cseg);
             else
                 hipLaunchKernelGGL((k_chunk_cb<E, Q, NT>), grid, dim3(kThreads), 0, st, (const E *)a->B,
-                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc);
+                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc, cseg);
             return launched();
         });
     });
@@ -214,7 +217,7 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, 
 
 template <typename E>
 ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float *cs, const E *cb, E *states,
-                     int32_t *seg_end, hipStream_t st)
+                     int32_t *seg_end, hipStream_t st, const int32_t *cseg = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -224,7 +227,7 @@ ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float 
             auto launch = [&](auto kern) {
                 hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, (const E *)a->x, cb, (const E *)a->dt, a->A,
                                    a->seq_idx, delta, cs, states, seg_end, (int)s.nseq, (int)s.T, (int)s.H,
-                                   (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (int)a->dt_softplus);
+                                   (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (int)a->dt_softplus, cseg);
             };
             if (s.packed) launch(k_chunk_state<E, Q, NT, true>);
             else launch(k_chunk_state<E, Q, NT, false>);
@@ -304,7 +307,8 @@ ssd_status run_scan(const Shape &s, const ssd_fwd_args *a, const float *delta, c
 template <typename E, int DOT, bool P1ONLY>
 ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
                         const E *hin, const E *vec, float *dot1, float *dot2, hipStream_t st,
-                        const float *dx_delta = nullptr, const float *dx_D = nullptr, float *dxv = nullptr)
+                        const float *dx_delta = nullptr, const float *dx_D = nullptr, float *dxv = nullptr,
+                        const int32_t *cseg = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -314,7 +318,7 @@ ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delt
             hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false, DOT, P1ONLY>), grid, dim3(scan_threads<Q>()), 0, st,
                                (const E *)a->x, delta, cs, cb, hin, a->D, (const int32_t *)nullptr, (E *)a->y,
                                (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, vec, dot1, dot2,
-                               (const E *)nullptr, dx_delta, dx_D, dxv);
+                               (const E *)nullptr, dx_delta, dx_D, dxv, cseg);
             return launched();
         });
     });
@@ -334,7 +338,8 @@ ssd_status run_scan_gated(const Shape &s, const ssd_fwd_args *a, const float *de
                 hipLaunchKernelGGL(kern, grid, dim3(scan_threads<Q>()), 0, st, (const E *)a->x, delta, cs, cb, hin,
                                    a->D, a->seq_idx, (E *)a->y, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
                                    (int)s.nc, ntp, (const E *)nullptr, (float *)nullptr, (float *)nullptr, z,
-                                   (const float *)nullptr, (const float *)nullptr, (float *)nullptr);
+                                   (const float *)nullptr, (const float *)nullptr, (float *)nullptr,
+                                   (const int32_t *)nullptr);
             };
             if (s.packed) launch(k_chunk_scan<E, Q, NT, true, 0, false, true>);
             else launch(k_chunk_scan<E, Q, NT, false, 0, false, true>);
@@ -477,7 +482,7 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
 
 template <typename E>
 ssd_status run_state_grad(const Shape &s, const ssd_fwd_args *ar, const float *cs, const E *cbr, E *u,
-                          hipStream_t st)
+                          hipStream_t st, const int32_t *cseg = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -487,7 +492,7 @@ ssd_status run_state_grad(const Shape &s, const ssd_fwd_args *ar, const float *c
             hipLaunchKernelGGL((k_chunk_state<E, Q, NT, false, true>), grid, dim3(kThreads), 0, st, (const E *)ar->x,
                                cbr, (const E *)nullptr, ar->A, (const int32_t *)nullptr, (float *)nullptr,
                                const_cast<float *>(cs), u, (int32_t *)nullptr, 0, (int)s.T, (int)s.H, (int)s.G,
-                               (int)s.P, (int)s.N, (int)s.nc, ntp, 0);
+                               (int)s.P, (int)s.N, (int)s.nc, ntp, 0, cseg);
             return launched();
         });
     });
@@ -536,13 +541,20 @@ struct StageMarks {
     }
 };
 
-// cseg (packed streams, on the layout in which every segment starts at a chunk
-// start): the per-chunk segment ids; g->dfinal_states is then [nseq,H,P,N] and
+// Packed streams, on the layout in which every segment starts at a chunk start:
+// cseg = the per-chunk segment ids, pstart / plen = each segment's padded start
+// and token count (nseq of them); g->dfinal_states is then [nseq,H,P,N] and
 // g->fwd_workspace is not used.
+struct PackedSegs {
+    const int32_t *cseg, *pstart, *plen;
+    int nseq;
+};
+
 template <typename E>
 ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *g, const BwdWorkspace &w,
-                     hipStream_t st, const int32_t *cseg = nullptr, StageMarks *sm = nullptr)
+                     hipStream_t st, const PackedSegs *pk = nullptr, StageMarks *sm = nullptr)
 {
+    const int32_t *cseg = pk ? pk->cseg : nullptr;
     auto mark = [&](const char *nm) { if (sm) sm->mark(nm); };
     char *ws = static_cast<char *>(g->workspace);
     auto F32 = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
@@ -565,9 +577,9 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         states = reinterpret_cast<E *>(fws + fw.states);
     } else {
         // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
-        if ((r = run_cb<E>(s, &f, cb, st)) != SSD_OK) return r;
+        if ((r = run_cb<E>(s, &f, cb, st, false, cseg)) != SSD_OK) return r;
         mark("chunk_cb");
-        if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st)) != SSD_OK) return r;
+        if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st, cseg)) != SSD_OK) return r;
         mark("chunk_state");
         if ((r = run_passing<E>(s, &f, cs, states, nullptr, st, cseg)) != SSD_OK) return r;
         mark("state_passing");
@@ -584,16 +596,17 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     rv.y = g->dx;
     rv.initial_states = nullptr;
     rv.final_states = nullptr;
-    if ((r = run_cb<E>(s, &rv, cbr, st, true)) != SSD_OK) return r;
+    if ((r = run_cb<E>(s, &rv, cbr, st, true, cseg)) != SSD_OK) return r;
     mark("chunk_cb_rev");
     // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
-    if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st)) != SSD_OK) return r;
+    if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st, cseg)) != SSD_OK) return r;
     mark("chunk_state_grad");
     if (cseg) {
         // packed layout: each segment's dfinal into the U slot of the chunk after its last
         const int64_t PN = s.P * s.N;
-        hipLaunchKernelGGL(k_bwd_inject_dfinal<E>, dim3(grid1(s.H * PN / 4, 256), (unsigned)s.nc), dim3(256), 0, st,
-                           gstates, g->dfinal_states, cseg, (int)s.H, PN, (int)s.nc);
+        const unsigned nb = grid1(s.H * PN / 4, 256);
+        hipLaunchKernelGGL(k_bwd_inject_dfinal<E>, dim3(nb * (unsigned)pk->nseq), dim3(256), 0, st, gstates,
+                           g->dfinal_states, pk->pstart, pk->plen, (int)s.H, PN, (int)s.nc, (int)s.Q, (int)nb);
         if ((r = launched()) != SSD_OK) return r;
         mark("inject_dfinal");
     }
@@ -605,11 +618,12 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y';
     //    it writes dx = Delta y' + D dy, and dy . x per (token, head)
     if ((r = run_scan_dot<E, 2, false>(s, &rv, nullptr, cs, cbr, gstates, (const E *)a->x, zo, xyp, st, delta,
-                                       a->D, dyx)) != SSD_OK)
+                                       a->D, dyx, cseg)) != SSD_OK)
         return r;
     mark("chunk_scan_dx");
     // 6. dy . (entering-state term of y), from the forward's entering states
-    if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st)) != SSD_OK)
+    if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st, nullptr,
+                                      nullptr, nullptr, cseg)) != SSD_OK)
         return r;
     mark("chunk_scan_dy_hin");
     // 7. M (summed over the group's heads) with the row / column sums of S; with
@@ -624,11 +638,11 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
                  hipLaunchKernelGGL((k_bwd_m<E, Q, NT>), dim3((unsigned)(ntri * s.nc * s.G * hsplit), (unsigned)s.b),
                                     dim3(kThreads), 0, st, (const E *)g->dy, (const E *)a->x, delta, cs, (const E *)cb,
                                     mrow, mcol, rpart, cpart, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc,
-                                    hsplit, mpart);
+                                    hsplit, mpart, cseg);
                  if (hsplit > 1)
                      hipLaunchKernelGGL((k_bwd_m_reduce<E, Q>), dim3((unsigned)(ntri * s.nc * s.G), (unsigned)s.b),
                                         dim3(kThreads), 0, st, (const float *)mpart, mrow, mcol, (int)s.G, (int)s.nc,
-                                        hsplit);
+                                        hsplit, cseg);
                  return launched();
              });
          })) != SSD_OK)
@@ -639,7 +653,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     hipLaunchKernelGGL(k_bwd_dl<E>, dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart, yo, zo,
                        xyp, bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T,
                        (int)s.H, (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), dlrows, (int)a->dt_softplus,
-                       s.P * s.N / 256);
+                       s.P * s.N / 256, cseg);
     hipLaunchKernelGGL(k_bwd_sum_heads, dim3((unsigned)s.H), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
                        (int)s.b, (int)s.H, (int)s.nc);
     if ((r = launched()) != SSD_OK) return r;
@@ -650,11 +664,11 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         const dim3 grid((unsigned)(s.nc * s.G * qt * nnt), (unsigned)s.b);
         hipLaunchKernelGGL((k_bwd_bc<E, Q, 0>), grid, dim3(kThreads), 0, st, (const E *)a->B, (const E *)mrow,
                            (const E *)states, (const E *)g->dy, delta, cs, (E *)g->dC, (int)s.T, (int)s.H, (int)s.G,
-                           (int)s.P, (int)s.N, (int)s.nc, nnt);
+                           (int)s.P, (int)s.N, (int)s.nc, nnt, cseg);
         mark("dC");
         hipLaunchKernelGGL((k_bwd_bc<E, Q, 1>), grid, dim3(kThreads), 0, st, (const E *)a->C, (const E *)mcol,
                            (const E *)gstates, (const E *)a->x, delta, cs, (E *)g->dB, (int)s.T, (int)s.H,
-                           (int)s.G, (int)s.P, (int)s.N, (int)s.nc, nnt);
+                           (int)s.G, (int)s.P, (int)s.N, (int)s.nc, nnt, cseg);
         mark("dB");
         return launched();
     });
@@ -766,7 +780,8 @@ ssd_status bwd_packed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args 
     gp.workspace = ws + k.inner;
     gp.workspace_bytes = k.w.total;
     gp.fwd_workspace = nullptr;
-    ssd_status r = bwd_typed<E>(k.sp, &fp, &gp, k.w, st, cseg, sm);
+    const PackedSegs pk{cseg, pstart, len, nseq};
+    ssd_status r = bwd_typed<E>(k.sp, &fp, &gp, k.w, st, &pk, sm);
     if (r != SSD_OK) return r;
     // back to the original positions
     rows(EP(k.dxp), g->dx, ppos, HP, T);

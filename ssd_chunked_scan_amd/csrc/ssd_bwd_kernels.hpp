@@ -108,22 +108,28 @@ __global__ void k_bwd_pad_map(const int32_t *__restrict__ ostart, const int32_t 
     if (pp % Q == 0) cseg[pp / Q] = off < padded ? lo : -1;
 }
 
-// Where chunk c starts a segment of the padded stream, its gradient state slot
-// (U_c, which the reverse scan does not read there) takes the final-state
-// gradient of the segment before it, cseg[c-1] (zero for -1 or without dfinal):
-// the reverse scan restarts from that slot.  Grid (ceil(H*PN/4/256), nc), four
+// The gradient state slot of the chunk right after segment sg's chunks in the
+// padded stream (U_c, c = (pstart[sg] + len[sg] rounded up to Q) / Q: the first
+// chunk of the next segment or of the trailing padding, where the reverse scan
+// does not read U_c) takes sg's final-state gradient, zero without dfinal: the
+// reverse scan restarts from that slot.  Segments without tokens own no chunk,
+// and the last one's gradient enters the scan as its start instead when no chunk
+// follows it.  nb blocks of 256 threads per segment (ceil(H*PN/4/256)), four
 // elements per thread.
 template <typename E>
 __global__ void k_bwd_inject_dfinal(E *__restrict__ gstates, const float *__restrict__ dfinal,
-                                    const int32_t *__restrict__ cseg, int H, int64_t PN, int nc)
+                                    const int32_t *__restrict__ pstart, const int32_t *__restrict__ len, int H,
+                                    int64_t PN, int nc, int Q, int nb)
 {
-    const int c = blockIdx.y;
-    if (c == 0 || cseg[c] == cseg[c - 1]) return;   // uniform
-    const int sg = cseg[c - 1];
-    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int sg = blockIdx.x / nb, blk = blockIdx.x % nb;
+    const int n = len[sg];
+    if (n <= 0) return;   // uniform
+    const int c = (pstart[sg] + (n + Q - 1) / Q * Q) / Q;
+    if (c >= nc) return;
+    const int64_t i = ((int64_t)blk * blockDim.x + threadIdx.x) * 4;
     if (i >= (int64_t)H * PN) return;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (dfinal && sg >= 0) load4_f32(dfinal + (int64_t)sg * H * PN + i, v);
+    if (dfinal) load4_f32(dfinal + (int64_t)sg * H * PN + i, v);
     store4_f32(gstates + (int64_t)c * H * PN + i, v);
 }
 
@@ -138,7 +144,9 @@ __global__ void k_bwd_unpad_map(const int32_t *__restrict__ seq_idx, const int32
 }
 
 // dst row r = src row map[r] (rows of R elements, R * sizeof(E) a multiple of 16
-// bytes), or zero where map[r] < 0.
+// bytes), or zero where map[r] < 0.  (Four vectors per thread, all loads before
+// the stores, measured slower: 160 against 139 us for the packed stream's five
+// copies at 15872 tokens, H = 64, G = 8.)
 template <typename E>
 __global__ void k_gather_rows(const E *__restrict__ src, E *__restrict__ dst, const int32_t *__restrict__ map,
                               int64_t R, int64_t total_vecs)
@@ -194,12 +202,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     const float *__restrict__ zo, const float *__restrict__ xyp, const float *__restrict__ bnd_part,
     const float *__restrict__ dyx, const float *__restrict__ delta, const E *__restrict__ dt,
     const float *__restrict__ A, E *__restrict__ ddt, float *__restrict__ dA_part, float *__restrict__ dD_part, int T,
-    int H, int Q, int nc, int ntp, int64_t rows, int softplus, int64_t nbp)
+    int H, int Q, int nc, int ntp, int64_t rows, int softplus, int64_t nbp, const int32_t *__restrict__ cseg = nullptr)
 {
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // (b * H + h) * nc + c
     if (wid >= rows) return;   // whole wave
     const int lane = threadIdx.x & 63;
     const int c = (int)(wid % nc);
+    if (cseg && cseg[c] < 0) {   // a chunk of padding only: nothing of it enters dA or dD
+        if (lane == 0) {
+            dA_part[wid] = 0.f;
+            dD_part[wid] = 0.f;
+        }
+        return;
+    }
     const int64_t bh = wid / nc;
     const int h = (int)(bh % H), b = (int)(bh / H);
     const int per = Q / 64, QT = Q / 64;
@@ -316,7 +331,8 @@ template <typename E, int Q, int NT>
 __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const E *__restrict__ dy, const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
     const E *__restrict__ cbuf, E *__restrict__ mrow, E *__restrict__ mcol, float *__restrict__ rpart,
-    float *__restrict__ cpart, int T, int H, int G, int P, int nc, int hsplit, float *__restrict__ mpart)
+    float *__restrict__ cpart, int T, int H, int G, int P, int nc, int hsplit, float *__restrict__ mpart,
+    const int32_t *__restrict__ cseg = nullptr)
 {
     using F = frag_t<E>;
     constexpr int V = kVec16<E>, ES = (int)sizeof(E);
@@ -334,6 +350,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const int b = blockIdx.y;
     int tile = u % NTRI;
     const int cg = u / NTRI, g = cg % G, c = cg / G;
+    if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     int ti = 0;
     while (tile > ti) {
         tile -= ti + 1;
@@ -617,7 +634,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
 // kernel.  One workgroup per tile unit of k_bwd_m.
 template <typename E, int Q>
 __global__ __launch_bounds__(kThreads) void k_bwd_m_reduce(const float *__restrict__ mpart, E *__restrict__ mrow,
-                                                           E *__restrict__ mcol, int G, int nc, int hsplit)
+                                                           E *__restrict__ mcol, int G, int nc, int hsplit,
+                                                           const int32_t *__restrict__ cseg = nullptr)
 {
     constexpr int QT = Q / 64, NTRI = QT * (QT + 1) / 2;
     __shared__ float stage[64 * 65];
@@ -625,6 +643,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m_reduce(const float *__restri
     const int u = blockIdx.x, b = blockIdx.y;
     int tile = u % NTRI;
     const int cg = u / NTRI, g = cg % G, c = cg / G;
+    if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     int ti = 0;
     while (tile > ti) {
         tile -= ti + 1;
@@ -680,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     const E *__restrict__ src_bc /* B (dC) or C (dB) */, const E *__restrict__ mm /* M (dC) or M^T (dB) */,
     const E *__restrict__ states /* Hin (dC) or G (dB) */, const E *__restrict__ vec /* dy (dC) or x (dB) */,
     const float *__restrict__ delta, const float *__restrict__ cs, E *__restrict__ out, int T, int H, int G, int P,
-    int N, int nc, int nnt)
+    int N, int nc, int nnt, const int32_t *__restrict__ cseg = nullptr)
 {
     using F = frag_t<E>;
     using KT = KTile<E, 64, 64>;
@@ -695,6 +714,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
     const int nt = u % nnt, rt = (u / nnt) % QT, cg = u / (nnt * QT), g = cg % G, c = cg / G;
+    if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     const int t0 = c * Q, len = min(Q, T - t0);
     const int n0 = nt * 64, r0 = rt * 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

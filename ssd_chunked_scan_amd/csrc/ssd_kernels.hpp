@@ -209,7 +209,8 @@ template <int Q, int NT> constexpr int64_t cb_group_elems() { return (int64_t)Q 
 // problem, without a reversed copy of B and C.
 template <typename E, int Q, int NT, bool REV = false>
 __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm, const E *__restrict__ Cm,
-                                                       E *__restrict__ cbuf, int T, int G, int N, int nc)
+                                                       E *__restrict__ cbuf, int T, int G, int N, int nc,
+                                                       const int32_t *__restrict__ cseg = nullptr)
 {
     using F = frag_t<E>;
     constexpr int V = kVec16<E>, ES = (int)sizeof(E);
@@ -223,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm,
     const int b = blockIdx.y;
     int tile = u % NTRI;
     const int cg = u / NTRI, g = cg % G, c = cg / G;
+    if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     int ti = 0;
     while (tile > ti) {
         tile -= ti + 1;
@@ -744,7 +746,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const E *__restrict__ x, const E *__restrict__ cbuf, const E *__restrict__ dt, const float *__restrict__ A,
     const int32_t *__restrict__ seq_idx, float *__restrict__ delta, float *__restrict__ cs,
     E *__restrict__ states, int32_t *__restrict__ seg_end, int nseq, int T, int H, int G, int P, int N, int nc,
-    int ntp, int softplus)
+    int ntp, int softplus, const int32_t *__restrict__ cseg = nullptr)
 {
     using F = frag_t<E>;
     using XT = KTile<E, Q, 64>;
@@ -762,6 +764,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const int tp = u % ntp;
     const int h = (u / ntp) % H;
     const int c = u / (ntp * H);
+    if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     const int g = h / (H / G);
     const int t0 = c * Q, len = min(Q, T - t0);
     const int p0 = tp * 64;
@@ -1273,7 +1276,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     int T, int H, int G, int P, int N, int nc, int ntp, const E *__restrict__ vec = nullptr,
     float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr, const E *__restrict__ gate = nullptr,
     const float *__restrict__ dx_delta = nullptr, const float *__restrict__ dx_D = nullptr,
-    float *__restrict__ dxv = nullptr)
+    float *__restrict__ dxv = nullptr, const int32_t *__restrict__ cseg = nullptr)
 {
     using F = frag_t<E>;
     constexpr int TH = scan_threads<Q>();
@@ -1304,6 +1307,7 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const int tp = u % ntp;
     const int h = (u / ntp) % H;
     const int c = u / (ntp * H);
+    if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     const int g = h / (H / G);
     const int t0 = c * Q, len = min(Q, T - t0);
     const int p0 = tp * 64;
