@@ -332,6 +332,41 @@ def test_bwd_packed_deterministic():
             assert torch.equal(a[k], b[k]), k
 
 
+def test_bwd_packed_nan_workspace():
+    """A packed stream whose padded layout ends in chunks of padding only (6
+    sequences of 20-200 tokens, Q = 64), with a NaN-filled workspace: the
+    per-chunk kernels skip those chunks, so their workspace slots keep the NaNs,
+    and no gradient may pick any of them up.  The gradients equal those of a
+    zero-filled workspace bit for bit."""
+    Q = 64
+    inp = wl.make_inputs(1, None, 4, 64, 64, 2, Q, "bf16", 93, init_std=0.3, packed=dict(nseqs=6, lo=20, hi=200))
+    T, nseq = inp.x.shape[1], inp.nseq
+    counts = np.bincount(inp.seq_idx.numpy(), minlength=nseq)   # every segment, the padding one too
+    padded = int(sum((L + Q - 1) // Q * Q for L in counts))
+    bound = (T + nseq * (Q - 1) + Q - 1) // Q * Q   # the padded length the library lays out
+    assert bound - padded >= Q, "the case must have a chunk of padding only"
+    g = inp.to("cuda:0")
+    y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, Q, D=g.D, initial_states=g.initial_states, seq_idx=g.seq_idx,
+                   nseq=nseq)
+    rng = np.random.default_rng(9)
+    b, _, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    dy = torch.from_numpy(rng.standard_normal((b, T, H, P)).astype(np.float32)).to(torch.bfloat16).to("cuda:0")
+    dfin = torch.from_numpy(rng.standard_normal((nseq, H, P, N)).astype(np.float32)).to("cuda:0")
+    p = ssd.Problem(g.x, g.dt, g.A, g.B, g.C, Q, g.D, g.initial_states, g.seq_idx, nseq)
+    nbytes = ssd.bwd_workspace_bytes(p)
+    runs = []
+    for fill in (0.0, float("nan")):
+        ws = torch.full((nbytes // 4 + 1,), fill, dtype=torch.float32, device="cuda:0").view(torch.uint8)
+        runs.append(ssd.bwd(g.x, g.dt, g.A, g.B, g.C, Q, y, dy, D=g.D, initial_states=g.initial_states,
+                            dfinal_states=dfin, seq_idx=g.seq_idx, nseq=nseq, workspace=ws))
+    torch.cuda.synchronize()
+    for k, t in runs[1].items():
+        if t is not None:
+            assert torch.isfinite(t).all(), k
+            assert torch.equal(t, runs[0][k]), k
+
+
 def test_bwd_packed_workload_full_size():
     """The packed workload (16 sequences of 128-2048 tokens plus the padding
     segment, 64 heads, N = 128, 8 groups, chunk 128, bf16) at full size, every
