@@ -245,9 +245,15 @@ ssd_status run_passing(const Shape &s, const ssd_fwd_args *a, const float *cs, E
     const int64_t PN = s.P * s.N;   // a multiple of 256
     constexpr int VE = 4;            // elements per thread
     const int64_t vecs = s.b * s.H * PN / VE;
-    hipLaunchKernelGGL((k_state_passing<E, VE>), dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, states, cs,
-                       a->initial_states, final_states, cseg ? nullptr : a->seq_idx, (int)s.T, (int)s.H, PN,
-                       (int)s.nc, (int)s.Q, vecs, (const E *)nullptr, (float *)nullptr, cseg);
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(grid1(vecs, kThreads)), dim3(kThreads), 0, st, states, cs, a->initial_states,
+                           final_states, cseg ? nullptr : a->seq_idx, (int)s.T, (int)s.H, PN, (int)s.nc, (int)s.Q,
+                           vecs, (const E *)nullptr, (float *)nullptr, cseg);
+    };
+    // a deeper ring of loads for bf16 chains longer than the default one (fp32
+    // states would need twice its registers)
+    if (sizeof(E) == 2 && s.nc > kPrefetch) launch(k_state_passing<E, VE, false, kPrefetchLong>);
+    else launch(k_state_passing<E, VE>);
     return launched();
 }
 

@@ -27,8 +27,9 @@
 // The first sum of dl is the suffix sum of (row sums - column sums) of S inside
 // the chunk, every term in fp32 from the same S, so no per-token state is ever
 // stored and no rounded output is differenced.  The anti-causal scan runs on the
-// forward's chunk_scan kernel with every chunk's tokens in reversed order
-// (kernels below build the reversed copies).
+// forward's chunk_scan kernel with every chunk's tokens in reversed order; the
+// kernels read dy, B, C and cs in that order themselves, so nothing is copied
+// reversed.
 #pragma once
 
 #include "ssd_kernels.hpp"

@@ -904,12 +904,20 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
 // ---------------------------------------------------------------------------
 // Every (b, h, p, n) element is an independent length-nc scan.  Each thread owns
 // VE = 4 consecutive elements (8 bytes of bf16, 16 of fp32) and walks the chunks
-// with a ring of kPrefetch loads in flight: the slot a chunk's state is read from
-// is refilled with the state kPrefetch chunks ahead before the arithmetic.  The
-// carry is replaced by zero (a select) when the chunk holds a segment boundary.
+// with a ring of D loads in flight: the slot a chunk's state is read from is
+// refilled with the state D chunks ahead before the arithmetic.  The carry is
+// replaced by zero (a select) when the chunk holds a segment boundary.
 // (Four bf16 per thread measured best: eight leave the latency-bound small
-// shapes with too few waves, two waste bandwidth on 4-byte accesses.)
+// shapes with too few waves, two waste bandwidth on 4-byte accesses.)  D is
+// kPrefetch, or kPrefetchLong for chains longer than kPrefetch chunks: such
+// shapes have few threads per chunk (batch 1 at 16K tokens: two waves per
+// SIMD), and twice the loads in flight took state_passing from 27.2 to 25.2 us
+// at 16384 tokens, 32 heads, N = 256, and from 73.0 to 66.6 us at 15872 tokens,
+// 64 heads, N = 128; on the 16-chunk chains of 8 x 2048 tokens, 80 heads, the
+// larger ring's registers cost occupancy (62.0 -> 65.9 us), so it is not used
+// there.
 constexpr int kPrefetch = 32;
+constexpr int kPrefetchLong = 64;
 
 template <typename E, int VE> struct RawVec;
 template <> struct RawVec<bf16, 4> { using type = uint2; };
@@ -962,7 +970,7 @@ template <int VE> __device__ __forceinline__ void store_final(float *p, const fl
 // cseg[nc-1]'s, `init` + cseg[nc-1] * H * PN (init is then [nseq, H, PN], and an
 // id of -1 or a NULL init means zero).  The cut is a select on the same update
 // as the forward's, so the loop holds no extra loads.
-template <typename E, int VE, bool REV = false>
+template <typename E, int VE, bool REV = false, int D = kPrefetch>
 __global__ __launch_bounds__(kThreads) void k_state_passing(
     E *__restrict__ states, const float *__restrict__ cs, const float *__restrict__ init,
     float *__restrict__ final_states, const int32_t *__restrict__ seq_idx,
@@ -971,7 +979,7 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
     const int32_t *__restrict__ cseg = nullptr)
 {
     using R = typename RawVec<E, VE>::type;
-    constexpr int D = kPrefetch;   // divides 64
+    static_assert(64 % D == 0, "the ring depth divides 64");
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= total_vecs) return;
     const int lane = threadIdx.x & 63;
