@@ -95,6 +95,14 @@ def check_bwd(inp, dtype, label="", **kw):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_bwd_largest_tiles(dtype):
+    """The largest tile configuration: N = 256, Q = 256 and P = 128 (two p tiles),
+    two groups, an initial state and a ragged last chunk."""
+    inp = wl.make_inputs(1, 2 * 256 + 37, 4, 128, 256, 2, 256, dtype, 257, init_std=0.3)
+    check_bwd(inp, dtype, label="largest tiles")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("Q", [64, 128, 256])
 def test_bwd_matches_oracle(dtype, Q):
     # several chunks and a ragged tail; heads sharing groups; initial state

@@ -167,7 +167,7 @@ def test_fwd_variants(dtype, variant):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("Q", [64, 128])
+@pytest.mark.parametrize("Q", [64, 128, 256])
 def test_fwd_packed(dtype, Q):
     inp = wl.make_inputs(1, None, 4, 64, 64, 2, Q, dtype, 5 + Q, init_std=0.4,
                          packed=dict(nseqs=7, lo=20, hi=300))
@@ -224,6 +224,15 @@ def test_fwd_shapes(shape, dtype):
     inp = small(dtype, kw["T"], H=kw["H"], P=kw["P"], N=kw["N"], G=kw["G"], chunk=64, seed=kw["T"],
                 init_std=0.2)
     check(inp, DT[dtype], label=str(shape))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fwd_largest_tiles(dtype):
+    """The largest tile configuration the kernels are built for: N = 256 (the
+    widest state), Q = 256, and P = 128 (two 64-wide p tiles per head), with two
+    groups, an initial state and a ragged last chunk."""
+    inp = small(dtype, 2 * 256 + 37, H=4, P=128, N=256, G=2, chunk=256, b=1, seed=256, init_std=0.3)
+    check(inp, DT[dtype], label="largest tiles")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
