@@ -193,8 +193,7 @@ def backward_stage_work(shape, esz, nseq=0):
     (dy in the place of x, B and C swapped, unit step size), which gives the
     gradient states G_c and dx; the rest are products with those.  FLOPs count
     the MFMA work the method needs (causal halves only), bytes each tensor a
-    stage must read or write once.  Stages that only move data (the packed
-    layout) count their copies."""
+    stage must read or write once."""
     b, T, H, P, N, G, Q = (shape[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
                                              "ngroups", "chunk"))
     nc = (T + Q - 1) // Q
@@ -224,8 +223,8 @@ def backward_stage_work(shape, esz, nseq=0):
                    bytes=X + ST + CB + 2 * BC + 2 * V4),
         "dB": dict(flops=2.0 * b * T * G * N * Q * causal + 2.0 * b * T * H * P * N,
                    bytes=X + ST + CB + 2 * BC + 2 * V4),
-        "pad_layout": dict(bytes=2 * (2 * X + 2 * BC + DT)),
-        "unpad_gather": dict(bytes=2 * (X + 2 * BC + DT)),
+        # the packed stream's chunk map: seq_idx read once, per-segment and per-chunk words written
+        "chunk_map": dict(bytes=b * T * 4 + nseq * 16 + nc * 12),
     }
     return w
 

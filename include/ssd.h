@@ -274,12 +274,14 @@ ssd_status ssd_step(const ssd_step_args *args, void *stream);
  * Packed streams (seq_idx, batch 1; the state reset at every boundary of
  * section 4.2 of "Transformers与SSMs的隐藏联系"): dfinal_states is [nseq,H,P,N],
  * the gradient of each segment's final state (rows of ids that never occur are
- * not read as anything but zero gradients).  The backward copies the stream
- * into its workspace laid out so that every segment starts at a chunk start
- * (each segment followed by padding tokens with x = B = C = dy = 0 and a zero
- * step size, up to the next multiple of the chunk), runs the chunked backward
- * there with the carry cut between segments and each segment's dfinal entering
- * at its last chunk, and copies the gradients back; fwd_workspace is not read.
+ * not read as anything but zero gradients).  The backward runs the chunked
+ * backward on a layout in which every segment starts at a chunk start (each
+ * segment followed by padding tokens with x = B = C = dy = 0 and a zero step
+ * size, up to the next multiple of the chunk), with the carry cut between
+ * segments and each segment's dfinal entering at its last chunk.  The layout is
+ * a map from its chunks to the caller's tokens, kept in the workspace: nothing
+ * is copied, every chunk reads its tokens in place and writes their gradients to
+ * their own rows.  fwd_workspace is not read.
  */
 typedef struct {
     const void *dy;                /* [b,T,H,P] dtype */

@@ -196,7 +196,7 @@ ssd_status run_cumsum(const Shape &s, const ssd_fwd_args *a, float *delta, float
 // skipped, here and in the other per-chunk launches that take it.
 template <typename E>
 ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, bool rev = false,
-                  const int32_t *cseg = nullptr)
+                  const int32_t *cseg = nullptr, const int2 *cmap = nullptr)
 {
     const int qt = (int)(s.Q / 64), ntri = qt * (qt + 1) / 2;
     dim3 grid((unsigned)(ntri * s.nc * s.G), (unsigned)s.b);
@@ -205,10 +205,10 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, 
             constexpr int Q = decltype(q)::value, NT = decltype(nt)::value;
             if (rev)
                 hipLaunchKernelGGL((k_chunk_cb<E, Q, NT, true>), grid, dim3(kThreads), 0, st, (const E *)a->B,
-                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc, cseg);
+                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc, cseg, cmap);
             else
                 hipLaunchKernelGGL((k_chunk_cb<E, Q, NT>), grid, dim3(kThreads), 0, st, (const E *)a->B,
-                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc, cseg);
+                                   (const E *)a->C, cb, (int)s.T, (int)s.G, (int)s.N, (int)s.nc, cseg, cmap);
             return launched();
         });
     });
@@ -217,7 +217,7 @@ ssd_status run_cb(const Shape &s, const ssd_fwd_args *a, E *cb, hipStream_t st, 
 
 template <typename E>
 ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float *cs, const E *cb, E *states,
-                     int32_t *seg_end, hipStream_t st, const int32_t *cseg = nullptr)
+                     int32_t *seg_end, hipStream_t st, const int32_t *cseg = nullptr, const int2 *cmap = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -227,7 +227,7 @@ ssd_status run_state(const Shape &s, const ssd_fwd_args *a, float *delta, float 
             auto launch = [&](auto kern) {
                 hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, (const E *)a->x, cb, (const E *)a->dt, a->A,
                                    a->seq_idx, delta, cs, states, seg_end, (int)s.nseq, (int)s.T, (int)s.H,
-                                   (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (int)a->dt_softplus, cseg);
+                                   (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, (int)a->dt_softplus, cseg, cmap);
             };
             if (s.packed) launch(k_chunk_state<E, Q, NT, true>);
             else launch(k_chunk_state<E, Q, NT, false>);
@@ -314,7 +314,7 @@ template <typename E, int DOT, bool P1ONLY>
 ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delta, const float *cs, const E *cb,
                         const E *hin, const E *vec, float *dot1, float *dot2, hipStream_t st,
                         const float *dx_delta = nullptr, const float *dx_D = nullptr, float *dxv = nullptr,
-                        const int32_t *cseg = nullptr)
+                        const int32_t *cseg = nullptr, const int2 *cmap = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -324,7 +324,7 @@ ssd_status run_scan_dot(const Shape &s, const ssd_fwd_args *a, const float *delt
             hipLaunchKernelGGL((k_chunk_scan<E, Q, NT, false, DOT, P1ONLY>), grid, dim3(scan_threads<Q>()), 0, st,
                                (const E *)a->x, delta, cs, cb, hin, a->D, (const int32_t *)nullptr, (E *)a->y,
                                (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.nc, ntp, vec, dot1, dot2,
-                               (const E *)nullptr, dx_delta, dx_D, dxv, cseg);
+                               (const E *)nullptr, dx_delta, dx_D, dxv, cseg, cmap);
             return launched();
         });
     });
@@ -345,7 +345,7 @@ ssd_status run_scan_gated(const Shape &s, const ssd_fwd_args *a, const float *de
                                    a->D, a->seq_idx, (E *)a->y, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.N,
                                    (int)s.nc, ntp, (const E *)nullptr, (float *)nullptr, (float *)nullptr, z,
                                    (const float *)nullptr, (const float *)nullptr, (float *)nullptr,
-                                   (const int32_t *)nullptr);
+                                   (const int32_t *)nullptr, (const int2 *)nullptr);
             };
             if (s.packed) launch(k_chunk_scan<E, Q, NT, true, 0, false, true>);
             else launch(k_chunk_scan<E, Q, NT, false, 0, false, true>);
@@ -488,7 +488,7 @@ BwdWorkspace bwd_workspace_layout(const Shape &s)
 
 template <typename E>
 ssd_status run_state_grad(const Shape &s, const ssd_fwd_args *ar, const float *cs, const E *cbr, E *u,
-                          hipStream_t st, const int32_t *cseg = nullptr)
+                          hipStream_t st, const int32_t *cseg = nullptr, const int2 *cmap = nullptr)
 {
     const int ntp = (int)((s.P + 63) / 64);
     dim3 grid((unsigned)(s.nc * s.H * ntp), (unsigned)s.b);
@@ -498,7 +498,7 @@ ssd_status run_state_grad(const Shape &s, const ssd_fwd_args *ar, const float *c
             hipLaunchKernelGGL((k_chunk_state<E, Q, NT, false, true>), grid, dim3(kThreads), 0, st, (const E *)ar->x,
                                cbr, (const E *)nullptr, ar->A, (const int32_t *)nullptr, (float *)nullptr,
                                const_cast<float *>(cs), u, (int32_t *)nullptr, 0, (int)s.T, (int)s.H, (int)s.G,
-                               (int)s.P, (int)s.N, (int)s.nc, ntp, 0, cseg);
+                               (int)s.P, (int)s.N, (int)s.nc, ntp, 0, cseg, cmap);
             return launched();
         });
     });
@@ -548,11 +548,14 @@ struct StageMarks {
 };
 
 // Packed streams, on the layout in which every segment starts at a chunk start:
-// cseg = the per-chunk segment ids, pstart / plen = each segment's padded start
-// and token count (nseq of them); g->dfinal_states is then [nseq,H,P,N] and
-// g->fwd_workspace is not used.
+// cseg = the per-chunk segment ids, cmap = each chunk's first token and token
+// count in the caller's stream (see chunk_rows), pstart / plen = each segment's
+// padded start and token count (nseq of them); g->dfinal_states is then
+// [nseq,H,P,N] and g->fwd_workspace is not used.
 struct PackedSegs {
-    const int32_t *cseg, *pstart, *plen;
+    const int32_t *cseg;
+    const int2 *cmap;
+    const int32_t *pstart, *plen;
     int nseq;
 };
 
@@ -561,6 +564,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
                      hipStream_t st, const PackedSegs *pk = nullptr, StageMarks *sm = nullptr)
 {
     const int32_t *cseg = pk ? pk->cseg : nullptr;
+    const int2 *cmap = pk ? pk->cmap : nullptr;
     auto mark = [&](const char *nm) { if (sm) sm->mark(nm); };
     char *ws = static_cast<char *>(g->workspace);
     auto F32 = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
@@ -583,9 +587,9 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         states = reinterpret_cast<E *>(fws + fw.states);
     } else {
         // 1. the forward's chunk intermediates again: delta, cs, CB, the entering states
-        if ((r = run_cb<E>(s, &f, cb, st, false, cseg)) != SSD_OK) return r;
+        if ((r = run_cb<E>(s, &f, cb, st, false, cseg, cmap)) != SSD_OK) return r;
         mark("chunk_cb");
-        if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st, cseg)) != SSD_OK) return r;
+        if ((r = run_state<E>(s, &f, delta, cs, cb, states, nullptr, st, cseg, cmap)) != SSD_OK) return r;
         mark("chunk_state");
         if ((r = run_passing<E>(s, &f, cs, states, nullptr, st, cseg)) != SSD_OK) return r;
         mark("state_passing");
@@ -602,10 +606,10 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     rv.y = g->dx;
     rv.initial_states = nullptr;
     rv.final_states = nullptr;
-    if ((r = run_cb<E>(s, &rv, cbr, st, true, cseg)) != SSD_OK) return r;
+    if ((r = run_cb<E>(s, &rv, cbr, st, true, cseg, cmap)) != SSD_OK) return r;
     mark("chunk_cb_rev");
     // 4. per-chunk gradient states U_c, then the reverse scan to G_c and dinit
-    if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st, cseg)) != SSD_OK) return r;
+    if ((r = run_state_grad<E>(s, &rv, cs, cbr, gstates, st, cseg, cmap)) != SSD_OK) return r;
     mark("chunk_state_grad");
     if (cseg) {
         // packed layout: each segment's dfinal into the U slot of the chunk after its last
@@ -624,12 +628,12 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     // 5. y' (reversed order) by the forward's chunk scan, with x . (G term) and x . y';
     //    it writes dx = Delta y' + D dy, and dy . x per (token, head)
     if ((r = run_scan_dot<E, 2, false>(s, &rv, nullptr, cs, cbr, gstates, (const E *)a->x, zo, xyp, st, delta,
-                                       a->D, dyx, cseg)) != SSD_OK)
+                                       a->D, dyx, cseg, cmap)) != SSD_OK)
         return r;
     mark("chunk_scan_dx");
     // 6. dy . (entering-state term of y), from the forward's entering states
     if ((r = run_scan_dot<E, 1, true>(s, &f, delta, cs, cb, states, (const E *)g->dy, yo, nullptr, st, nullptr,
-                                      nullptr, nullptr, cseg)) != SSD_OK)
+                                      nullptr, nullptr, cseg, cmap)) != SSD_OK)
         return r;
     mark("chunk_scan_dy_hin");
     // 7. M (summed over the group's heads) with the row / column sums of S; with
@@ -644,7 +648,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
                  hipLaunchKernelGGL((k_bwd_m<E, Q, NT>), dim3((unsigned)(ntri * s.nc * s.G * hsplit), (unsigned)s.b),
                                     dim3(kThreads), 0, st, (const E *)g->dy, (const E *)a->x, delta, cs, (const E *)cb,
                                     mrow, mcol, rpart, cpart, (int)s.T, (int)s.H, (int)s.G, (int)s.P, (int)s.nc,
-                                    hsplit, mpart, cseg);
+                                    hsplit, mpart, cseg, cmap);
                  if (hsplit > 1)
                      hipLaunchKernelGGL((k_bwd_m_reduce<E, Q>), dim3((unsigned)(ntri * s.nc * s.G), (unsigned)s.b),
                                         dim3(kThreads), 0, st, (const float *)mpart, mrow, mcol, (int)s.G, (int)s.nc,
@@ -659,7 +663,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     hipLaunchKernelGGL(k_bwd_dl<E>, dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart, yo, zo,
                        xyp, bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T,
                        (int)s.H, (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), dlrows, (int)a->dt_softplus,
-                       s.P * s.N / 256, cseg);
+                       s.P * s.N / 256, cseg, cmap);
     hipLaunchKernelGGL(k_bwd_sum_heads, dim3((unsigned)s.H), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
                        (int)s.b, (int)s.H, (int)s.nc);
     if ((r = launched()) != SSD_OK) return r;
@@ -670,11 +674,11 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
         const dim3 grid((unsigned)(s.nc * s.G * qt * nnt), (unsigned)s.b);
         hipLaunchKernelGGL((k_bwd_bc<E, Q, 0>), grid, dim3(kThreads), 0, st, (const E *)a->B, (const E *)mrow,
                            (const E *)states, (const E *)g->dy, delta, cs, (E *)g->dC, (int)s.T, (int)s.H, (int)s.G,
-                           (int)s.P, (int)s.N, (int)s.nc, nnt, cseg);
+                           (int)s.P, (int)s.N, (int)s.nc, nnt, cseg, cmap);
         mark("dC");
         hipLaunchKernelGGL((k_bwd_bc<E, Q, 1>), grid, dim3(kThreads), 0, st, (const E *)a->C, (const E *)mcol,
                            (const E *)gstates, (const E *)a->x, delta, cs, (E *)g->dB, (int)s.T, (int)s.H,
-                           (int)s.G, (int)s.P, (int)s.N, (int)s.nc, nnt, cseg);
+                           (int)s.G, (int)s.P, (int)s.N, (int)s.nc, nnt, cseg, cmap);
         mark("dB");
         return launched();
     });
@@ -691,7 +695,7 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
 // than Q tokens of padding.
 struct PackedBwd {
     Shape sp;   // the padded problem (batch 1, no seq_idx)
-    size_t seg_end, ostart, len, pstart, pos_src, cseg, ppos, xp, dyp, dtp, bp, cp, dxp, ddtp, dbp, dcp, inner, total;
+    size_t seg_end, ostart, len, pstart, cseg, cmap, inner, total;
     BwdWorkspace w;
 };
 
@@ -704,26 +708,15 @@ PackedBwd packed_bwd_layout(const Shape &s)
     const int64_t tp = ((s.T + s.nseq * (s.Q - 1)) + s.Q - 1) / s.Q * s.Q;
     k.sp.T = tp;
     k.sp.nc = tp / s.Q;
-    const size_t xs = (size_t)(tp * s.H * s.P) * s.esz, ds = (size_t)(tp * s.H) * s.esz,
-                 bs = (size_t)(tp * s.G * s.N) * s.esz, ids = (size_t)s.nseq * 4;
+    const size_t ids = (size_t)s.nseq * 4;
     size_t o = 0;
     auto take = [&](size_t n) { const size_t at = o; o = align256(o + n); return at; };
     k.seg_end = take(ids);
     k.ostart = take(ids);
     k.len = take(ids);
     k.pstart = take(ids);
-    k.pos_src = take((size_t)tp * 4);
     k.cseg = take((size_t)k.sp.nc * 4);
-    k.ppos = take((size_t)s.T * 4);
-    k.xp = take(xs);
-    k.dyp = take(xs);
-    k.dtp = take(ds);
-    k.bp = take(bs);
-    k.cp = take(bs);
-    k.dxp = take(xs);
-    k.ddtp = take(ds);
-    k.dbp = take(bs);
-    k.dcp = take(bs);
+    k.cmap = take((size_t)k.sp.nc * 8);
     k.inner = o;
     k.w = bwd_workspace_layout(k.sp);
     k.total = align256(o + k.w.total);
@@ -736,66 +729,29 @@ ssd_status bwd_packed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args 
 {
     char *ws = static_cast<char *>(g->workspace);
     auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
-    auto EP = [&](size_t off) { return reinterpret_cast<E *>(ws + off); };
-    const int T = (int)s.T, Q = (int)s.Q, nseq = (int)s.nseq, Tp = (int)k.sp.T;
+    const int T = (int)s.T, Q = (int)s.Q, nseq = (int)s.nseq, ncp = (int)k.sp.nc;
     int32_t *seg_end = I32(k.seg_end), *ostart = I32(k.ostart), *len = I32(k.len), *pstart = I32(k.pstart);
-    int32_t *pos_src = I32(k.pos_src), *cseg = I32(k.cseg), *ppos = I32(k.ppos);
-    // the padded layout
+    int32_t *cseg = I32(k.cseg);
+    int2 *cmap = reinterpret_cast<int2 *>(ws + k.cmap);
+    // the padded layout, as a map from its chunks to the caller's tokens
     hipLaunchKernelGGL(k_seg_end, dim3(grid1(T, 256)), dim3(256), 0, st, a->seq_idx, seg_end, T, nseq);
     hipLaunchKernelGGL(k_bwd_seg_ranges, dim3(1), dim3(64), 0, st, seg_end, ostart, len, pstart, nseq, Q);
-    hipLaunchKernelGGL(k_bwd_pad_map, dim3(grid1(Tp, 256)), dim3(256), 0, st, ostart, len, pstart, pos_src, cseg,
-                       nseq, Q, Tp);
-    hipLaunchKernelGGL(k_bwd_unpad_map, dim3(grid1(T, 256)), dim3(256), 0, st, a->seq_idx, ostart, pstart, ppos, T,
-                       nseq);
+    hipLaunchKernelGGL(k_bwd_chunk_map, dim3(grid1(ncp, 256)), dim3(256), 0, st, ostart, len, pstart, cseg, cmap,
+                       nseq, Q, ncp);
     if (launched() != SSD_OK) return SSD_ERR_HIP;
-    const int64_t HP = s.H * s.P, GN = s.G * s.N;
-    constexpr int V = kVec16<E>;
-    auto rows = [&](const void *src, void *dst, const int32_t *map, int64_t R, int64_t nrows) {
-        const int64_t nv = nrows * R / V;
-        hipLaunchKernelGGL(k_gather_rows<E>, dim3(grid1(nv, 256)), dim3(256), 0, st, (const E *)src, (E *)dst, map,
-                           R, nv);
-    };
-    auto elems = [&](const void *src, void *dst, const int32_t *map, int64_t R, int64_t nrows, float fill) {
-        hipLaunchKernelGGL(k_gather_elems<E>, dim3(grid1(nrows * R, 256)), dim3(256), 0, st, (const E *)src,
-                           (E *)dst, map, R, nrows * R, fill);
-    };
-    rows(a->x, EP(k.xp), pos_src, HP, Tp);
-    rows(g->dy, EP(k.dyp), pos_src, HP, Tp);
-    rows(a->B, EP(k.bp), pos_src, GN, Tp);
-    rows(a->C, EP(k.cp), pos_src, GN, Tp);
-    // padding takes a zero step size: softplus(-inf) = 0
-    elems(a->dt, EP(k.dtp), pos_src, s.H, Tp, a->dt_softplus ? -__builtin_huge_valf() : 0.f);
-    if (launched() != SSD_OK) return SSD_ERR_HIP;
-    if (sm) sm->mark("pad_layout");
-    // the chunked backward on the padded stream
+    if (sm) sm->mark("chunk_map");
+    // the chunked backward on the padded stream: every chunk reads its tokens
+    // from the caller's tensors and writes their gradients in place
     ssd_fwd_args fp = *a;
-    fp.seqlen = Tp;
-    fp.x = EP(k.xp);
-    fp.dt = EP(k.dtp);
-    fp.B = EP(k.bp);
-    fp.C = EP(k.cp);
     fp.seq_idx = nullptr;
     fp.nseq = 0;
     fp.y = nullptr;
     ssd_bwd_args gp = *g;
-    gp.dy = EP(k.dyp);
-    gp.dx = EP(k.dxp);
-    gp.ddt = EP(k.ddtp);
-    gp.dB = EP(k.dbp);
-    gp.dC = EP(k.dcp);
     gp.workspace = ws + k.inner;
     gp.workspace_bytes = k.w.total;
     gp.fwd_workspace = nullptr;
-    const PackedSegs pk{cseg, pstart, len, nseq};
-    ssd_status r = bwd_typed<E>(k.sp, &fp, &gp, k.w, st, &pk, sm);
-    if (r != SSD_OK) return r;
-    // back to the original positions
-    rows(EP(k.dxp), g->dx, ppos, HP, T);
-    rows(EP(k.dbp), g->dB, ppos, GN, T);
-    rows(EP(k.dcp), g->dC, ppos, GN, T);
-    elems(EP(k.ddtp), g->ddt, ppos, s.H, T, 0.f);
-    if (sm) sm->mark("unpad_gather");
-    return launched();
+    const PackedSegs pk{cseg, cmap, pstart, len, nseq};
+    return bwd_typed<E>(k.sp, &fp, &gp, k.w, st, &pk, sm);
 }
 
 // ---------------------------------------------------------------------------

@@ -39,13 +39,16 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 // packed streams: a layout in which every segment starts at a chunk start
 // ---------------------------------------------------------------------------
-// The backward of a packed stream runs on a copy of the stream laid out so that
-// every segment occupies whole chunks: segment s (in id order) starts at padded
-// position pstart[s], a multiple of Q, and is followed by padding up to the next
-// multiple of Q.  Padding tokens have x = B = C = dy = 0 and a step size of zero,
-// so they leave the state unchanged and contribute nothing; the state carry is
-// cut where a chunk starts a new segment.  Positions past the last segment form
-// chunks of no segment (id -1).
+// The backward of a packed stream runs on a layout in which every segment
+// occupies whole chunks: segment s (in id order) starts at padded position
+// pstart[s], a multiple of Q, and is followed by padding up to the next
+// multiple of Q.  Padding tokens have x = B = C = dy = 0 and a step size of
+// zero, so they leave the state unchanged and contribute nothing; the state
+// carry is cut where a chunk starts a new segment.  Positions past the last
+// segment form chunks of no segment (id -1).  The layout is never built: each
+// chunk reads its tokens from the caller's stream through a chunk map (first
+// token, count; see chunk_rows), its positions past the count read as zero,
+// and its gradients are written straight to the tokens' own rows.
 
 // From seg_end (the last position of every id, -1 for an id that never occurs;
 // ids never decrease along the stream): ostart[s] = the first position of s,
@@ -87,16 +90,18 @@ __global__ void k_bwd_seg_ranges(const int32_t *__restrict__ seg_end, int32_t *_
     }
 }
 
-// pos_src[pp] = the original position at padded position pp (-1 for padding), and
-// cseg[pp / Q] = the segment of every padded chunk (-1 past the last segment).
-// The segment of pp is the last id whose padded start is <= pp (a binary search;
-// an id without tokens has the same start as the next one).
-__global__ void k_bwd_pad_map(const int32_t *__restrict__ ostart, const int32_t *__restrict__ len,
-                              const int32_t *__restrict__ pstart, int32_t *__restrict__ pos_src,
-                              int32_t *__restrict__ cseg, int nseq, int Q, int Tp)
+// For every chunk c of the padded stream: cseg[c] = its segment (-1 past the
+// last segment) and cmap[c] = (its first token in the caller's stream, its
+// token count), (0, 0) for a chunk of padding only.  The segment of chunk c is
+// the last id whose padded start is <= c Q (a binary search; an id without
+// tokens has the same start as the next one).
+__global__ void k_bwd_chunk_map(const int32_t *__restrict__ ostart, const int32_t *__restrict__ len,
+                                const int32_t *__restrict__ pstart, int32_t *__restrict__ cseg,
+                                int2 *__restrict__ cmap, int nseq, int Q, int ncp)
 {
-    const int pp = blockIdx.x * blockDim.x + threadIdx.x;
-    if (pp >= Tp) return;
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= ncp) return;
+    const int pp = c * Q;
     int lo = 0, hi = nseq - 1;   // the last s with pstart[s] <= pp (pstart[0] = 0)
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -105,8 +110,13 @@ __global__ void k_bwd_pad_map(const int32_t *__restrict__ ostart, const int32_t 
     }
     const int off = pp - pstart[lo], n = len[lo];
     const int padded = (n + Q - 1) / Q * Q;
-    pos_src[pp] = off < n ? ostart[lo] + off : -1;
-    if (pp % Q == 0) cseg[pp / Q] = off < padded ? lo : -1;
+    if (off < padded) {
+        cseg[c] = lo;
+        cmap[c] = make_int2(ostart[lo] + off, min(Q, n - off));
+    } else {
+        cseg[c] = -1;
+        cmap[c] = make_int2(0, 0);
+    }
 }
 
 // The gradient state slot of the chunk right after segment sg's chunks in the
@@ -132,46 +142,6 @@ __global__ void k_bwd_inject_dfinal(E *__restrict__ gstates, const float *__rest
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (dfinal) load4_f32(dfinal + (int64_t)sg * H * PN + i, v);
     store4_f32(gstates + (int64_t)c * H * PN + i, v);
-}
-
-// ppos[t] = the padded position of original position t.
-__global__ void k_bwd_unpad_map(const int32_t *__restrict__ seq_idx, const int32_t *__restrict__ ostart,
-                                const int32_t *__restrict__ pstart, int32_t *__restrict__ ppos, int T, int nseq)
-{
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= T) return;
-    const int s = min(max(seq_idx[t], 0), nseq - 1);
-    ppos[t] = pstart[s] + t - ostart[s];
-}
-
-// dst row r = src row map[r] (rows of R elements, R * sizeof(E) a multiple of 16
-// bytes), or zero where map[r] < 0.  (Four vectors per thread, all loads before
-// the stores, measured slower: 160 against 139 us for the packed stream's five
-// copies at 15872 tokens, H = 64, G = 8.)
-template <typename E>
-__global__ void k_gather_rows(const E *__restrict__ src, E *__restrict__ dst, const int32_t *__restrict__ map,
-                              int64_t R, int64_t total_vecs)
-{
-    constexpr int V = kVec16<E>;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total_vecs) return;
-    const int64_t vpr = R / V, r = i / vpr, v = i % vpr;
-    const int m = map[r];
-    uint4 val{0u, 0u, 0u, 0u};
-    if (m >= 0) val = *reinterpret_cast<const uint4 *>(src + (int64_t)m * R + v * V);
-    *reinterpret_cast<uint4 *>(dst + r * R + v * V) = val;
-}
-
-// The same one element at a time, with `fill` where map[r] < 0.
-template <typename E>
-__global__ void k_gather_elems(const E *__restrict__ src, E *__restrict__ dst, const int32_t *__restrict__ map,
-                               int64_t R, int64_t total, float fill)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const int64_t r = i / R, e = i % R;
-    const int m = map[r];
-    dst[i] = m >= 0 ? src[(int64_t)m * R + e] : from_float<E>(fill);
 }
 
 // ---------------------------------------------------------------------------
@@ -203,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     const float *__restrict__ zo, const float *__restrict__ xyp, const float *__restrict__ bnd_part,
     const float *__restrict__ dyx, const float *__restrict__ delta, const E *__restrict__ dt,
     const float *__restrict__ A, E *__restrict__ ddt, float *__restrict__ dA_part, float *__restrict__ dD_part, int T,
-    int H, int Q, int nc, int ntp, int64_t rows, int softplus, int64_t nbp, const int32_t *__restrict__ cseg = nullptr)
+    int H, int Q, int nc, int ntp, int64_t rows, int softplus, int64_t nbp, const int32_t *__restrict__ cseg = nullptr,
+    const int2 *__restrict__ cmap = nullptr)
 {
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // (b * H + h) * nc + c
     if (wid >= rows) return;   // whole wave
@@ -221,7 +192,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     const int per = Q / 64, QT = Q / 64;
     const int64_t slice = rows * Q;   // one tile / p-tile slice: [b,H,nc,Q]
     const float Ah = A[h];
-    const int len = min(Q, T - c * Q);
+    int t0, len;
+    chunk_rows(c, Q, T, cmap, t0, len);
     const int64_t row = wid * Q;
     double av[4] = {0, 0, 0, 0}, zv[4] = {0, 0, 0, 0};
     float xv[4] = {0, 0, 0, 0};
@@ -257,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
         if (j < len) {
             const double dl = asuf + zpre + b0;
             const float dd = Ah * (float)dl + xv[e];
-            const int t = c * Q + j;
+            const int t = t0 + j;
             float gr = dd;
             if (softplus) {
                 const float zt = to_float(dt[((int64_t)b * T + t) * H + h]);
@@ -333,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
     const E *__restrict__ dy, const E *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ cs,
     const E *__restrict__ cbuf, E *__restrict__ mrow, E *__restrict__ mcol, float *__restrict__ rpart,
     float *__restrict__ cpart, int T, int H, int G, int P, int nc, int hsplit, float *__restrict__ mpart,
-    const int32_t *__restrict__ cseg = nullptr)
+    const int32_t *__restrict__ cseg = nullptr, const int2 *__restrict__ cmap = nullptr)
 {
     using F = frag_t<E>;
     constexpr int V = kVec16<E>, ES = (int)sizeof(E);
@@ -358,7 +330,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
         ++ti;
     }
     const int si = tile;
-    const int t0 = c * Q, len = min(Q, T - t0);
+    int t0, len;
+    chunk_rows(c, Q, T, cmap, t0, len);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const int hpg_all = H / G, PC = (P + 63) / 64;
@@ -700,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     const E *__restrict__ src_bc /* B (dC) or C (dB) */, const E *__restrict__ mm /* M (dC) or M^T (dB) */,
     const E *__restrict__ states /* Hin (dC) or G (dB) */, const E *__restrict__ vec /* dy (dC) or x (dB) */,
     const float *__restrict__ delta, const float *__restrict__ cs, E *__restrict__ out, int T, int H, int G, int P,
-    int N, int nc, int nnt, const int32_t *__restrict__ cseg = nullptr)
+    int N, int nc, int nnt, const int32_t *__restrict__ cseg = nullptr, const int2 *__restrict__ cmap = nullptr)
 {
     using F = frag_t<E>;
     using KT = KTile<E, 64, 64>;
@@ -716,7 +689,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     const int b = blockIdx.y;
     const int nt = u % nnt, rt = (u / nnt) % QT, cg = u / (nnt * QT), g = cg % G, c = cg / G;
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
-    const int t0 = c * Q, len = min(Q, T - t0);
+    int t0, len;
+    chunk_rows(c, Q, T, cmap, t0, len);
     const int n0 = nt * 64, r0 = rt * 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;

@@ -21,6 +21,24 @@
 
 namespace ssd {
 
+// The tokens of chunk c: t0 = its first one, len = how many.  Without a chunk
+// map the chunks tile the sequence (t0 = c Q, the last one ragged).  With one
+// (the packed backward's layout, in which every segment starts a chunk)
+// cmap[c] = (first token, count) in the caller's own stream, count 0 for a
+// chunk of padding only; the positions of a chunk past its count read as zero,
+// which is what padding tokens are, so the padded stream is never copied.
+__device__ __forceinline__ void chunk_rows(int c, int Q, int T, const int2 *cmap, int &t0, int &len)
+{
+    if (cmap) {
+        const int2 m = cmap[c];
+        t0 = m.x;
+        len = m.y;
+    } else {
+        t0 = c * Q;
+        len = min(Q, T - t0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // chunk_cumsum
 // ---------------------------------------------------------------------------
@@ -67,38 +85,38 @@ __device__ __forceinline__ void wave_segmented_scan(double &v, int &f)
 }
 
 // The loads of chunk_cumsum_wave (issued early by callers that have other
-// loads to overlap): raw dt (softplus not yet applied) and sequence ids.
+// loads to overlap): raw dt (softplus not yet applied) and sequence ids of the
+// chunk's len tokens from t0 (T is the stream length, for addressing).
 template <typename E>
 __device__ __forceinline__ void chunk_cumsum_load(const E *__restrict__ dt, const int32_t *__restrict__ seq_idx,
-                                                  int b, int c, int h, int T, int H, int Q, float (&zv)[4],
-                                                  int (&sv)[4])
+                                                  int b, int t0, int len, int h, int T, int H, int Q,
+                                                  float (&zv)[4], int (&sv)[4])
 {
     const int lane = threadIdx.x & 63;
-    const int t0 = c * Q;
     const int per = Q >> 6;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         zv[j] = 0.f;
         sv[j] = 0;
-        const int t = t0 + lane * per + j;
-        if (j < per && t < T) {
+        const int i = lane * per + j, t = t0 + i;
+        if (j < per && i < len) {
             zv[j] = to_float(dt[((int64_t)b * T + t) * H + h]);
             if (seq_idx) sv[j] = seq_idx[t];
         }
     }
 }
 
-// The arithmetic of chunk_cumsum_wave on loaded values; zv becomes Delta.
-__device__ __forceinline__ void chunk_cumsum_compute(const float *__restrict__ A, bool packed, int c, int h,
-                                                     int T, int Q, int softplus, float (&zv)[4], float (&cv)[4],
+// The arithmetic of chunk_cumsum_wave on loaded values (the chunk's len
+// tokens); zv becomes Delta.
+__device__ __forceinline__ void chunk_cumsum_compute(const float *__restrict__ A, bool packed, int len, int h,
+                                                     int Q, int softplus, float (&zv)[4], float (&cv)[4],
                                                      const int (&sv)[4])
 {
     const int lane = threadIdx.x & 63;
-    const int t0 = c * Q;
     const int per = Q >> 6;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        if (j < per && t0 + lane * per + j < T && softplus) zv[j] = softplus_f(zv[j]);
+        if (j < per && lane * per + j < len && softplus) zv[j] = softplus_f(zv[j]);
     const int last_sv = per == 4 ? sv[3] : (per == 2 ? sv[1] : sv[0]);
     const int before = __shfl_up(last_sv, 1);   // id of the token just before this lane's first
     const double a = (double)A[h];
@@ -113,7 +131,7 @@ __device__ __forceinline__ void chunk_cumsum_compute(const float *__restrict__ A
         if (j < per) {
             const int i = lane * per + j;
             const int prev = j == 0 ? before : sv[j - 1];
-            if (packed && i > 0 && t0 + i < T && sv[j] != prev) {
+            if (packed && i > 0 && i < len && sv[j] != prev) {
                 run = 0.0;
                 restarted = 1;
             }
@@ -146,8 +164,9 @@ __device__ __forceinline__ void chunk_cumsum_wave(const E *__restrict__ dt, cons
                                                   int T, int H, int Q, int softplus, float (&dv)[4],
                                                   float (&cv)[4], int (&sv)[4])
 {
-    chunk_cumsum_load<E>(dt, seq_idx, b, c, h, T, H, Q, dv, sv);
-    chunk_cumsum_compute(A, seq_idx != nullptr, c, h, T, Q, softplus, dv, cv, sv);
+    const int t0 = c * Q, len = min(Q, T - t0);
+    chunk_cumsum_load<E>(dt, seq_idx, b, t0, len, h, T, H, Q, dv, sv);
+    chunk_cumsum_compute(A, seq_idx != nullptr, len, h, Q, softplus, dv, cv, sv);
 }
 
 // Delta and cs rows of one (b, chunk, head) as left by chunk_cumsum_wave.
@@ -210,7 +229,8 @@ template <int Q, int NT> constexpr int64_t cb_group_elems() { return (int64_t)Q 
 template <typename E, int Q, int NT, bool REV = false>
 __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm, const E *__restrict__ Cm,
                                                        E *__restrict__ cbuf, int T, int G, int N, int nc,
-                                                       const int32_t *__restrict__ cseg = nullptr)
+                                                       const int32_t *__restrict__ cseg = nullptr,
+                                                       const int2 *__restrict__ cmap = nullptr)
 {
     using F = frag_t<E>;
     constexpr int V = kVec16<E>, ES = (int)sizeof(E);
@@ -231,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm,
         ++ti;
     }
     const int si = tile;
-    const int t0 = c * Q, len = min(Q, T - t0);
+    int t0, len;
+    chunk_rows(c, Q, T, cmap, t0, len);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
 
@@ -746,7 +767,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const E *__restrict__ x, const E *__restrict__ cbuf, const E *__restrict__ dt, const float *__restrict__ A,
     const int32_t *__restrict__ seq_idx, float *__restrict__ delta, float *__restrict__ cs,
     E *__restrict__ states, int32_t *__restrict__ seg_end, int nseq, int T, int H, int G, int P, int N, int nc,
-    int ntp, int softplus, const int32_t *__restrict__ cseg = nullptr)
+    int ntp, int softplus, const int32_t *__restrict__ cseg = nullptr, const int2 *__restrict__ cmap = nullptr)
 {
     using F = frag_t<E>;
     using XT = KTile<E, Q, 64>;
@@ -766,7 +787,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const int c = u / (ntp * H);
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     const int g = h / (H / G);
-    const int t0 = c * Q, len = min(Q, T - t0);
+    int t0, len;
+    chunk_rows(c, Q, T, cmap, t0, len);
     const int p0 = tp * 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -775,7 +797,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     // cumsum step below must not wait for the tiles
     float dv[4], cv[4];
     int sv[4];
-    if (!GRAD && wave == 0) chunk_cumsum_load<E>(dt, seq_idx, b, c, h, T, H, Q, dv, sv);
+    if (!GRAD && wave == 0) chunk_cumsum_load<E>(dt, seq_idx, b, t0, len, h, T, H, Q, dv, sv);
     const int64_t ldx = (int64_t)H * P;
     XT xs;
     if constexpr (GRAD) xs.init_rev(ldx, P - p0, len);   // the chunk's tokens in reversed order
@@ -817,7 +839,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
             w[s] = keep ? __builtin_amdgcn_exp2f(cs[row + (len - 1 - s)] * kLog2e) : 0.f;
         }
     } else if (wave == 0) {
-        chunk_cumsum_compute(A, PACKED, c, h, T, Q, softplus, dv, cv, sv);
+        chunk_cumsum_compute(A, PACKED, len, h, Q, softplus, dv, cv, sv);
         if (tp == 0) store_cumsum_wave(delta, cs, ((int64_t)b * H + h) * nc + c, Q, dv, cv);
         constexpr int per = Q / 64;
         const int il = len - 1, ll = il / per, jl = il % per;   // lane and slot of the last token
@@ -1284,7 +1306,8 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     int T, int H, int G, int P, int N, int nc, int ntp, const E *__restrict__ vec = nullptr,
     float *__restrict__ dot1 = nullptr, float *__restrict__ dot2 = nullptr, const E *__restrict__ gate = nullptr,
     const float *__restrict__ dx_delta = nullptr, const float *__restrict__ dx_D = nullptr,
-    float *__restrict__ dxv = nullptr, const int32_t *__restrict__ cseg = nullptr)
+    float *__restrict__ dxv = nullptr, const int32_t *__restrict__ cseg = nullptr,
+    const int2 *__restrict__ cmap = nullptr)
 {
     using F = frag_t<E>;
     constexpr int TH = scan_threads<Q>();
@@ -1317,7 +1340,8 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const int c = u / (ntp * H);
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     const int g = h / (H / G);
-    const int t0 = c * Q, len = min(Q, T - t0);
+    int t0, len;
+    chunk_rows(c, Q, T, cmap, t0, len);
     const int p0 = tp * 64;
     const int64_t cso = (((int64_t)b * H + h) * nc + c) * Q;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR

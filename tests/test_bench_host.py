@@ -98,9 +98,9 @@ def test_backward_stage_work_covers_every_stage():
     import bench
     shape = dict(batch=1, seqlen=16384, nheads=32, headdim=64, dstate=256, ngroups=1, chunk=256)
     w = bench.backward_stage_work(shape, 2, nseq=0)
-    names = ["chunk_cb", "chunk_state", "state_passing", "pad_layout", "chunk_cb_rev",
+    names = ["chunk_cb", "chunk_state", "state_passing", "chunk_map", "chunk_cb_rev",
              "chunk_state_grad", "inject_dfinal", "state_passing_rev", "chunk_scan_dx", "chunk_scan_dy_hin",
-             "m_rows_cols", "dl_ddt_dA_dD", "dC", "dB", "unpad_gather"]
+             "m_rows_cols", "dl_ddt_dA_dD", "dC", "dB"]
     assert set(names) == set(w)
     for n in names:
         assert w[n]["bytes"] >= 0, n

@@ -417,8 +417,8 @@ def test_bwd_stage_times(mode):
             "chunk_scan_dy_hin", "m_rows_cols", "dl_ddt_dA_dD", "dC", "dB"]
     want = {"recompute": ["chunk_cb", "chunk_state", "state_passing"] + core,
             "fwd_workspace": core,
-            "packed": ["pad_layout", "chunk_cb", "chunk_state", "state_passing"] + core[:2] + ["inject_dfinal"]
-                      + core[2:] + ["unpad_gather"]}[mode]
+            "packed": ["chunk_map", "chunk_cb", "chunk_state", "state_passing"] + core[:2] + ["inject_dfinal"]
+                      + core[2:]}[mode]
     assert names == want
     assert all(ms > 0 for _, ms in stages), stages
     _log("    " + " ".join(f"{n}={ms * 1e3:.0f}us" for n, ms in stages))
