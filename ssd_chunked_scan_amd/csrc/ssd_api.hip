@@ -660,10 +660,14 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
     mark("m_rows_cols");
     // 8. dl, ddt, dA, dD
     const int64_t dlrows = s.b * s.H * s.nc;
-    hipLaunchKernelGGL(k_bwd_dl<E>, dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart, yo, zo,
-                       xyp, bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part, (int)s.T,
-                       (int)s.H, (int)s.Q, (int)s.nc, (int)((s.P + 63) / 64), dlrows, (int)a->dt_softplus,
-                       s.P * s.N / 256, cseg, cmap);
+    with_q(s.Q, [&](auto q) {
+        constexpr int Q = decltype(q)::value;
+        hipLaunchKernelGGL((k_bwd_dl<E, Q>), dim3(grid1(dlrows, kThreads / 64)), dim3(kThreads), 0, st, rpart, cpart,
+                           yo, zo, xyp, bnd, dyx, delta, (const E *)a->dt, a->A, (E *)g->ddt, dA_part, dD_part,
+                           (int)s.T, (int)s.H, (int)s.nc, (int)((s.P + 63) / 64), dlrows, (int)a->dt_softplus,
+                           s.P * s.N / 256, cseg, cmap);
+        return SSD_OK;
+    });
     hipLaunchKernelGGL(k_bwd_sum_heads, dim3((unsigned)s.H), dim3(64), 0, st, dA_part, dD_part, g->dA, g->dD,
                        (int)s.b, (int)s.H, (int)s.nc);
     if ((r = launched()) != SSD_OK) return r;
@@ -687,12 +691,13 @@ ssd_status bwd_typed(const Shape &s, const ssd_fwd_args *a, const ssd_bwd_args *
 // ---------------------------------------------------------------------------
 // backward of a packed stream
 // ---------------------------------------------------------------------------
-// The stream is copied to a layout in which every segment starts at a chunk
-// start (k_bwd_seg_ranges, k_bwd_pad_map), the chunked backward runs there with
-// the state carry cut between segments and each segment's final-state gradient
-// entering at its last chunk, and the gradients are copied back.  Tp bounds the
-// padded length from the host side: each of at most nseq segments adds fewer
-// than Q tokens of padding.
+// The chunked backward runs on a layout in which every segment starts at a
+// chunk start (k_bwd_seg_ranges, k_bwd_chunk_map), with the state carry cut
+// between segments and each segment's final-state gradient entering after its
+// last chunk.  The layout is never built: each chunk reads its tokens from the
+// caller's stream through the chunk map and writes its gradients to the tokens'
+// own rows.  Tp bounds the padded length from the host side: each of at most
+// nseq segments adds fewer than Q tokens of padding.
 struct PackedBwd {
     Shape sp;   // the padded problem (batch 1, no seq_idx)
     size_t seg_end, ostart, len, pstart, cseg, cmap, inner, total;

@@ -167,15 +167,16 @@ __device__ __forceinline__ double wave_incl_scan(double v)
     return v;
 }
 
-template <typename E>
+template <typename E, int Q>
 __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     const float *__restrict__ rpart, const float *__restrict__ cpart, const float *__restrict__ yo,
     const float *__restrict__ zo, const float *__restrict__ xyp, const float *__restrict__ bnd_part,
     const float *__restrict__ dyx, const float *__restrict__ delta, const E *__restrict__ dt,
     const float *__restrict__ A, E *__restrict__ ddt, float *__restrict__ dA_part, float *__restrict__ dD_part, int T,
-    int H, int Q, int nc, int ntp, int64_t rows, int softplus, int64_t nbp, const int32_t *__restrict__ cseg = nullptr,
+    int H, int nc, int ntp, int64_t rows, int softplus, int64_t nbp, const int32_t *__restrict__ cseg = nullptr,
     const int2 *__restrict__ cmap = nullptr)
 {
+    constexpr int per = Q / 64, QT = Q / 64;
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // (b * H + h) * nc + c
     if (wid >= rows) return;   // whole wave
     const int lane = threadIdx.x & 63;
@@ -189,55 +190,87 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     }
     const int64_t bh = wid / nc;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const int per = Q / 64, QT = Q / 64;
     const int64_t slice = rows * Q;   // one tile / p-tile slice: [b,H,nc,Q]
     const float Ah = A[h];
     int t0, len;
     chunk_rows(c, Q, T, cmap, t0, len);
     const int64_t row = wid * Q;
-    double av[4] = {0, 0, 0, 0}, zv[4] = {0, 0, 0, 0};
-    float xv[4] = {0, 0, 0, 0};
-    double asum = 0.0, zsum = 0.0;
+    // Every value this lane needs is requested before any arithmetic (the
+    // token loops unroll at compile time), so the wave waits for memory once:
+    // the tile row sums of S (tiles si <= the token's tile), the column sums
+    // (tiles ti >= it), the p-tile partials of the dot products, the step
+    // sizes, dt and the boundary-term partials.
+    float rv[per][QT], cv[per][QT], dlt[per], dtv[per];
+    double y1v[per], z1v[per], xyv[per], dyv[per];
+#pragma unroll
     for (int e = 0; e < per; ++e) {
         const int j = lane * per + e;
-        if (j >= len) continue;
-        double r = 0.0, cc = 0.0, y1 = 0.0, z1 = 0.0, xy = 0.0;
-        for (int si = 0; si <= j / 64; ++si) r += rpart[si * slice + row + j];
-        for (int ti = j / 64; ti < QT; ++ti) cc += cpart[ti * slice + row + j];
-        for (int tp = 0; tp < ntp; ++tp) {
-            y1 += yo[tp * slice + row + j];
-            z1 += zo[tp * slice + row + j];
-            xy += xyp[tp * slice + row + j];
+        const bool in = j < len;
+        const int64_t o = row + j;
+#pragma unroll
+        for (int q = 0; q < QT; ++q) {
+            rv[e][q] = in && q <= j / 64 ? rpart[q * slice + o] : 0.f;
+            cv[e][q] = in && q >= j / 64 ? cpart[q * slice + o] : 0.f;
         }
-        av[e] = r - cc + y1;
-        zv[e] = delta[row + j] * z1;
-        xv[e] = (float)xy;
+        y1v[e] = in ? yo[o] : 0.f;
+        z1v[e] = in ? zo[o] : 0.f;
+        xyv[e] = in ? xyp[o] : 0.f;
+        dyv[e] = in ? dyx[o] : 0.f;
+        dlt[e] = in ? delta[o] : 0.f;
+        dtv[e] = in && softplus ? to_float(dt[((int64_t)b * T + t0 + j) * H + h]) : 0.f;
+    }
+    float bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[i] = lane + 64 * i < nbp ? bnd_part[wid * nbp + lane + 64 * i] : 0.f;
+    double bsum = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bsum += bv[i];
+    for (int64_t i = lane + 256; i < nbp; i += 64) bsum += bnd_part[wid * nbp + i];
+    // further p tiles of the dot products (P > 64)
+    for (int tp = 1; tp < ntp; ++tp)
+#pragma unroll
+        for (int e = 0; e < per; ++e) {
+            const int j = lane * per + e;
+            if (j >= len) continue;
+            const int64_t o = tp * slice + row + j;
+            y1v[e] += yo[o];
+            z1v[e] += zo[o];
+            xyv[e] += xyp[o];
+            dyv[e] += dyx[o];
+        }
+    double av[per], zv[per];
+    double asum = 0.0, zsum = 0.0;
+#pragma unroll
+    for (int e = 0; e < per; ++e) {
+        double r = 0.0, cc = 0.0;
+#pragma unroll
+        for (int q = 0; q < QT; ++q) {
+            r += rv[e][q];
+            cc += cv[e][q];
+        }
+        av[e] = r - cc + y1v[e];
+        zv[e] = dlt[e] * z1v[e];
         asum += av[e];
         zsum += zv[e];
     }
     // suffix sums of a (inclusive) and prefix sums of z (exclusive) over the chunk
-    double bsum = 0.0;
-    for (int64_t i = lane; i < nbp; i += 64) bsum += bnd_part[wid * nbp + i];
     const double ain = wave_incl_scan(asum), zin = wave_incl_scan(zsum), bin = wave_incl_scan(bsum);
     const double atot = __shfl(ain, 63);
     double asuf = atot - ain + asum;   // sum of a over this lane's tokens and all later lanes
     double zpre = zin - zsum;          // sum of z over earlier lanes
     const double b0 = __shfl(bin, 63);
     double sa = 0.0, sd = 0.0;
+#pragma unroll
     for (int e = 0; e < per; ++e) {
         const int j = lane * per + e;
         if (j < len) {
             const double dl = asuf + zpre + b0;
-            const float dd = Ah * (float)dl + xv[e];
-            const int t = t0 + j;
+            const float dd = Ah * (float)dl + (float)xyv[e];
             float gr = dd;
-            if (softplus) {
-                const float zt = to_float(dt[((int64_t)b * T + t) * H + h]);
-                gr = dd / (1.f + __builtin_amdgcn_exp2f(-zt * kLog2e));   // dDelta * sigmoid(dt)
-            }
-            ddt[((int64_t)b * T + t) * H + h] = from_float<E>(gr);
-            sa += (double)delta[row + j] * dl;
-            for (int tp = 0; tp < ntp; ++tp) sd += dyx[tp * slice + row + j];
+            if (softplus) gr = dd / (1.f + __builtin_amdgcn_exp2f(-dtv[e] * kLog2e));   // dDelta * sigmoid(dt)
+            ddt[((int64_t)b * T + t0 + j) * H + h] = from_float<E>(gr);
+            sa += (double)dlt[e] * dl;
+            sd += dyv[e];
         }
         asuf -= av[e];
         zpre += zv[e];
