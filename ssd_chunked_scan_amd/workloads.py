@@ -23,6 +23,10 @@ Packed workloads concatenate sequences of lengths U[lo, hi] into one stream
 (batch 1), pad it to a multiple of the chunk length, and label the padding as a
 segment of its own with x = B = C = 0.
 
+``device_inputs`` draws the same recipe on the GPU with torch's generator, for
+the maximum-size cases whose host draw would be too large (billions of
+elements).
+
 The block around the SSD (``block_inputs``, its own seed) draws the
 pre-convolution channels xBC ~ N(0, 1), depthwise taps and bias ~ U[-1/sqrt(w),
 1/sqrt(w)] for w taps, and the gate input z ~ N(0, 1).
@@ -196,6 +200,34 @@ def decode_inputs(seed: int = 2000, **overrides) -> StepInputs:
     inp = make_inputs(cfg["batch"], 1, cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"], 64,
                       cfg["dtype"], seed, dt_mean=cfg["dt_mean"], init_std=cfg["init_std"], name=cfg["name"])
     return token(inp, 0)
+
+
+def device_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, ngroups: int, chunk: int,
+                  dtype: str, seed: int, device, dt_mean: float = -3.0, dt_std: float = 0.5,
+                  init_std: Optional[float] = 0.1, name: str = "") -> Inputs:
+    """The same recipe and draw order as ``make_inputs``, drawn on ``device`` by
+    torch's generator (seeded with ``seed``) for sizes whose fp64 host draw would
+    not fit in host memory or time: billions of elements.  x, dt, B and C are
+    drawn in fp32 and rounded to bf16 on the device for bf16 inputs; A, D and
+    the initial states stay fp32.  The values differ from ``make_inputs``'s for
+    the same seed (a different generator); the distributions are the same."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    T, H, P, N, G = seqlen, nheads, headdim, dstate, ngroups
+    el = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kw = dict(device=device, generator=gen)
+    A = -torch.exp(torch.rand(H, **kw) * math.log(16.0))
+    D = torch.randn(H, **kw)
+    dt = (torch.randn(batch, T, H, **kw) * dt_std + dt_mean).to(el)
+    x = torch.empty(batch, T, H, P, dtype=el, device=device)
+    for t0 in range(0, T, 1 << 16):   # in slabs, so no fp32 copy of all of x is held at once
+        t1 = min(T, t0 + (1 << 16))
+        x[:, t0:t1] = torch.randn(batch, t1 - t0, H, P, **kw).to(el)
+    Bm = (torch.randn(batch, T, G, N, **kw) / math.sqrt(N)).to(el)
+    Cm = (torch.randn(batch, T, G, N, **kw) / math.sqrt(N)).to(el)
+    init = torch.randn(batch, H, P, N, **kw) * init_std if init_std is not None else None
+    return Inputs(x=x, dt=dt, A=A, B=Bm, C=Cm, D=D, initial_states=init, seq_idx=None, nseq=0, chunk=chunk,
+                  dt_softplus=True, lengths=[], real_tokens=batch * T, name=name)
 
 
 @dataclass

@@ -494,6 +494,34 @@ def test_full_workloads(idx):
     assert ey <= TOL[dtype] and es <= TOL[dtype]
 
 
+def test_long_sequence_past_32bit_offsets():
+    """The maximum-size case along the sequence: 1,052,897 tokens (4113 chunks of
+    256, the last one ragged) x 32 heads x 64 in bf16, so x and y hold 2.16e9
+    elements (4.3 GB) and every token past about 2^19 (bytes) or 2^20 (elements)
+    lies beyond 32-bit offsets; the chunk states take another 1 GB.  Inputs are
+    drawn on the GPU (``workloads.device_inputs``).  The oracle runs on one head's
+    slice at a time (heads are independent given the shared B and C): the first
+    and the last head, y over (T, P) and the final state over (P, N)."""
+    T, H, P, N, Q = (1 << 20) + 4321, 32, 64, 64, 256
+    dev = "cuda:0"
+    inp = wl.device_inputs(1, T, H, P, N, 1, Q, "bf16", seed=7000, device=dev, name="long1M_bf16")
+    _log(f"[max] T={T} H={H} P={P} N={N} Q={Q}: x {inp.x.numel() * 2 / 2**30:.2f} GiB")
+    y, fs = ssd.fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, Q, D=inp.D, initial_states=inp.initial_states)
+    torch.cuda.synchronize()
+    assert torch.isfinite(fs).all()
+    Bh, Ch = inp.B.cpu(), inp.C.cpu()
+    for h in (0, H - 1):
+        sl = slice(h, h + 1)
+        ref = oracle.forward(inp.x[:, :, sl].contiguous().cpu(), inp.dt[:, :, sl].contiguous().cpu(),
+                             inp.A[sl].cpu(), Bh, Ch, inp.D[sl].cpu(), inp.initial_states[:, sl].contiguous().cpu())
+        yh = y[:, :, sl].contiguous()
+        assert torch.isfinite(yh).all()
+        ey = rel(f64(yh), ref.y)
+        es = rel(f64(fs[:, sl]), ref.final_states)
+        _log(f"    head {h}: rel-L2 y={ey:.3e} final state={es:.3e} (tol {TOL[torch.bfloat16]:.0e})")
+        assert ey <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
 def _nan_tail(t, extra=4096):
     """A copy of t on the GPU whose storage is followed by NaNs: the head of a
     larger NaN-filled buffer (still contiguous), so any read past the tensor's

@@ -48,3 +48,21 @@ def test_packed_layout():
     else:
         assert w.nseq == 16
     assert w.real_tokens == real
+
+
+def test_device_inputs_recipe():
+    """The device-side draw (used for the maximum-size case) on the CPU: seeded,
+    the recipe's shapes, dtypes and laws."""
+    a = wl.device_inputs(1, 3000, 4, 64, 32, 1, 256, "bf16", seed=3, device="cpu")
+    b = wl.device_inputs(1, 3000, 4, 64, 32, 1, 256, "bf16", seed=3, device="cpu")
+    c = wl.device_inputs(1, 3000, 4, 64, 32, 1, 256, "bf16", seed=4, device="cpu")
+    assert torch.equal(a.x, b.x) and torch.equal(a.B, b.B) and torch.equal(a.A, b.A)
+    assert not torch.equal(a.x, c.x)
+    assert a.x.shape == (1, 3000, 4, 64) and a.x.dtype == torch.bfloat16
+    assert a.B.shape == (1, 3000, 1, 32) and a.C.shape == (1, 3000, 1, 32) and a.dt.shape == (1, 3000, 4)
+    assert a.A.dtype == torch.float32 and a.initial_states.shape == (1, 4, 64, 32)
+    assert ((a.A <= -1.0) & (a.A >= -16.0)).all()
+    assert abs(float(a.x.float().std()) - 1.0) < 0.02
+    assert abs(float(a.B.float().std()) * math.sqrt(32) - 1.0) < 0.05
+    assert abs(float(a.dt.float().mean()) + 3.0) < 0.02 and abs(float(a.dt.float().std()) - 0.5) < 0.02
+    assert abs(float(a.initial_states.std()) - 0.1) < 0.01
