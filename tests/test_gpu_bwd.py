@@ -296,6 +296,45 @@ def check_bwd_packed(inp, dtype, label="", seed=0):
     return gr
 
 
+def test_bwd_past_32bit_offsets():
+    """The maximum-size case of the backward: 16 sequences of 66,770 tokens (261
+    chunks of 256, the last ragged) x 32 heads x 64 in bf16, N = 64, so x, dy and
+    dx hold 2.19e9 elements (4.1 GiB each) and the last sequence lies wholly
+    past 2^31 elements.  Inputs and dy are drawn on the GPU.  The oracle runs on
+    four heads of the last sequence (heads are independent given the shared B
+    and C): dx and ddt over that sequence's tokens, and dinit.  dB and dC (sums
+    over all heads) and dA and dD (sums over all sequences) need every unit; they
+    are held to the oracle at full size on the long workload instead."""
+    b, T, H, P, N, Q = 16, 65536 + 1234, 32, 64, 64, 256
+    dev = "cuda:0"
+    inp = wl.device_inputs(b, T, H, P, N, 1, Q, "bf16", seed=7001, device=dev, name="b16_T66770_bf16")
+    _log(f"[bwd max] b={b} T={T} H={H} P={P} N={N}: x {inp.x.numel() * 2 / 2**30:.2f} GiB")
+    y, _ = ssd.fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, Q, D=inp.D, initial_states=inp.initial_states)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7002)
+    dy = torch.empty_like(inp.x)
+    for t0 in range(0, T, 1 << 14):
+        t1 = min(T, t0 + (1 << 14))
+        dy[:, t0:t1] = torch.randn(b, t1 - t0, H, P, device=dev, generator=gen).to(torch.bfloat16)
+    dfin = torch.randn(b, H, P, N, device=dev, generator=gen)
+    gr = ssd.bwd(inp.x, inp.dt, inp.A, inp.B, inp.C, Q, y, dy, D=inp.D, initial_states=inp.initial_states,
+                 dfinal_states=dfin)
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dB", "dC", "dA", "dD", "dinitial_states"):
+        assert torch.isfinite(gr[k]).all(), k
+    bb, heads = b - 1, [0, 17, 30, 31]
+    hs = lambda t: t[bb:bb + 1][:, :, heads].contiguous().cpu()   # [1, T, 4, ...] of the last sequence
+    ref = oracle.backward(hs(inp.x), hs(inp.dt), inp.A[heads].cpu(), inp.B[bb:bb + 1].cpu(),
+                          inp.C[bb:bb + 1].cpu(), hs(dy), inp.D[heads].cpu(),
+                          inp.initial_states[bb:bb + 1, heads].cpu(), dfin[bb:bb + 1, heads].cpu())
+    errs = {"dx": worst(f64(hs(gr["dx"])), ref.dx, [0, 2]), "ddt": worst(f64(hs(gr["ddt"])), ref.ddt, [0, 2]),
+            "dinit": worst(f64(gr["dinitial_states"][bb:bb + 1, heads]), ref.dinit, [0, 1])}
+    _log("    sequence %d, heads %s: " % (bb, heads) + "  ".join(f"{k}={v:.2e}" for k, v in errs.items())
+         + f"  (tol {TOL['bf16']:.0e})")
+    for k, v in errs.items():
+        assert v <= TOL["bf16"], (k, v)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("Q", [64, 128, 256])
 def test_bwd_packed(dtype, Q):
