@@ -247,12 +247,19 @@ def test_bwd_long_workload_full_size():
 # packed streams
 # ---------------------------------------------------------------------------
 
-def check_bwd_packed(inp, dtype, label="", seed=0):
+def check_bwd_packed(inp, dtype, label="", seed=0, ddt_min_len=0):
     """The backward of a packed stream against the oracle's, per (segment, head)
     slice of dx and ddt, per (segment, group) slice of dB and dC, per head of
     dinit, and over the heads for dA and dD; dfinal holds one gradient per
-    segment id."""
-    _log(f"[bwd packed] {label} T={inp.x.shape[1]} lengths={inp.lengths} Q={inp.chunk} {dtype}")
+    segment id.
+
+    ddt has one value per token, so the ddt slice of a sequence of a few tokens
+    holds a few numbers, each one dot product whose true value can lie
+    arbitrarily close to zero, where no rounded computation keeps a relative
+    error bound.  With ddt_min_len = L, the ddt of the sequences shorter than L
+    tokens is compared per head as one slice pooled over all of them (every
+    value is still compared); longer sequences keep their own slices."""
+    _log(f"[bwd packed] {label} T={inp.x.shape[1]} nseq={len(inp.lengths)} Q={inp.chunk} {dtype}")
     g = inp.to("cuda:0")
     nseq = inp.nseq
     y, _ = ssd.fwd(g.x, g.dt, g.A, g.B, g.C, inp.chunk, D=g.D, initial_states=g.initial_states,
@@ -272,13 +279,18 @@ def check_bwd_packed(inp, dtype, label="", seed=0):
     ids = inp.seq_idx.numpy()
     segs = [np.flatnonzero(ids == s) for s in np.unique(ids)]
 
-    def seg_worst(got, want):
+    def seg_worst(got, want, slices=segs):
         # got / want [1, T, K, ...]: slices (segment, k) over (tokens of the segment, ...)
-        return max(rel(got[0, sl, k], want[0, sl, k]) for sl in segs for k in range(got.shape[2]))
+        return max(rel(got[0, sl, k], want[0, sl, k]) for sl in slices for k in range(got.shape[2]))
+
+    ddt_slices = segs
+    if ddt_min_len:
+        short = [sl for sl in segs if len(sl) < ddt_min_len]
+        ddt_slices = [sl for sl in segs if len(sl) >= ddt_min_len] + ([np.concatenate(short)] if short else [])
 
     errs = {
         "dx": seg_worst(f64(gr["dx"]), ref.dx),
-        "ddt": seg_worst(f64(gr["ddt"])[..., None], ref.ddt[..., None]),
+        "ddt": seg_worst(f64(gr["ddt"])[..., None], ref.ddt[..., None], ddt_slices),
         "dB": seg_worst(f64(gr["dB"]), ref.dB),
         "dC": seg_worst(f64(gr["dC"]), ref.dC),
         "dA": rel(f64(gr["dA"]), ref.dA),
@@ -343,6 +355,23 @@ def test_bwd_packed(dtype, Q):
     inp = wl.make_inputs(1, None, 4, 64, 64, 2, Q, dtype, 400 + Q, init_std=0.3,
                          packed=dict(nseqs=7, lo=20, hi=300))
     check_bwd_packed(inp, dtype, label="mid-chunk boundaries")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_bwd_packed_many_short_sequences(dtype):
+    """The largest segment count for the backward: 1500 packed sequences of 1 to
+    80 tokens (each padded to its own chunks in the backward's layout: about
+    1500 chunks for about 60K tokens), every slice against the oracle.  fp32
+    holds even the one-token sequences' ddt to 1e-4 on their own.  In bf16 the
+    gradient states and the C.B products are rounded to bf16, and the ddt of a
+    one-token sequence is a single dot product (x . y') that can nearly cancel
+    (measured: 0.0119 against the oracle's 0.0106 for one such token, 12 %,
+    where the whole tensor's error is 0.25 %).  There the ddt of the sequences shorter than 64 tokens (the row
+    count of every other slice) is compared per head as one pooled slice."""
+    inp = wl.make_inputs(1, None, 4, 64, 64, 2, 64, dtype, 78, init_std=0.3,
+                         packed=dict(nseqs=1500, lo=1, hi=80))
+    assert min(inp.lengths) == 1
+    check_bwd_packed(inp, dtype, label="1500 short sequences", ddt_min_len=64 if dtype == "bf16" else 0)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

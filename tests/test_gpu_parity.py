@@ -175,6 +175,17 @@ def test_fwd_packed(dtype, Q):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fwd_packed_many_short_sequences(dtype):
+    """The largest segment count: 1500 packed sequences of 1 to 80 tokens (many
+    boundaries in every chunk, sequences of a single token, about 60K tokens),
+    every (sequence, head) slice against the oracle."""
+    inp = wl.make_inputs(1, None, 4, 64, 64, 2, 64, dtype, 77, init_std=0.3,
+                         packed=dict(nseqs=1500, lo=1, hi=80))
+    assert min(inp.lengths) == 1
+    check(inp, DT[dtype], label="1500 short sequences")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_fwd_packed_slow_decay(dtype):
     inp = wl.make_inputs(1, None, 3, 32, 64, 1, 64, dtype, 8, init_std=0.4,
                          a_log_range=(math.log(0.01), math.log(0.1)),
