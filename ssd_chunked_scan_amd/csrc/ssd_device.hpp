@@ -224,6 +224,43 @@ __device__ __forceinline__ void bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t of
 // its own L2.  Map the hardware id to a logical id so that every XCD works on one
 // contiguous range of logical ids: neighbouring tiles (same chunk, same B/C
 // group) then share an L2.
+// floor(n / d) for wave-uniform 0 <= n < 2^23 and d >= 1, from the hardware
+// reciprocal (1 ulp): n is exact in fp32, the reciprocal and the product add a
+// relative error of at most 1.5 * 2^-23, so for d >= 3 (quotient below 2^23 / 3)
+// the float quotient is within 0.5 of n / d, its truncation within one of the
+// true quotient, and one integer step corrects it; for d = 1 or 2 the
+// reciprocal and the product are exact.  A scalar 32-bit integer division costs
+// about twenty scalar instructions per wave, and the scalar unit is shared by
+// all the waves of a SIMD; this is a handful of vector ones.
+__device__ __forceinline__ int udiv23(int n, int d)
+{
+    int q = (int)((float)n * __builtin_amdgcn_rcpf((float)d));
+    const int r = n - q * d;
+    q += (r >= d ? 1 : 0) - (r < 0 ? 1 : 0);
+    return __builtin_amdgcn_readfirstlane(q);
+}
+
+// The coordinates of workgroup unit u of a per-(chunk or segment, head, 64-p
+// tile) grid: u = (k * H + h) * ntp + tp, and the group g = floor(h G / H) of
+// head h.  Wave-uniform; the reciprocal division when every numerator stays
+// below 2^23 (units = K H ntp and H G), else the integer one.
+__device__ __forceinline__ void unit_coords(int u, int units, int ntp, int H, int G, int &tp, int &h, int &k, int &g)
+{
+    if (units < (1 << 23) && (int64_t)H * G < (1 << 23)) {
+        const int q = udiv23(u, ntp);
+        tp = u - q * ntp;
+        k = udiv23(q, H);
+        h = q - k * H;
+        g = udiv23(h * G, H);
+    } else {
+        tp = u % ntp;
+        const int q = u / ntp;
+        h = q % H;
+        k = q / H;
+        g = h / (H / G);
+    }
+}
+
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks)
 {
     const int x = bid & 7, k = bid >> 3;

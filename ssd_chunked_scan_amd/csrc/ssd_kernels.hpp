@@ -782,11 +782,9 @@ __global__ __launch_bounds__(kThreads, 4) void k_chunk_state(
     const int units = nc * H * ntp;
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
-    const int tp = u % ntp;
-    const int h = (u / ntp) % H;
-    const int c = u / (ntp * H);
+    int tp, h, c, g;
+    unit_coords(u, units, ntp, H, G, tp, h, c, g);
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
-    const int g = h / (H / G);
     int t0, len;
     chunk_rows(c, Q, T, cmap, t0, len);
     const int p0 = tp * 64;
@@ -1164,10 +1162,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_seq_final(
     __shared__ int m[Q];
     const int units = nseq * H * ntp;
     const int u = xcd_remap(blockIdx.x, units);
-    const int tp = u % ntp;
-    const int h = (u / ntp) % H;
-    const int sg = u / (ntp * H);
-    const int g = h / (H / G);
+    int tp, h, sg, g;
+    unit_coords(u, units, ntp, H, G, tp, h, sg, g);
     const int p0 = tp * 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
@@ -1335,11 +1331,9 @@ __global__ __launch_bounds__(scan_threads<Q>(), 4) void k_chunk_scan(
     const int units = nc * H * ntp;
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
-    const int tp = u % ntp;
-    const int h = (u / ntp) % H;
-    const int c = u / (ntp * H);
+    int tp, h, c, g;
+    unit_coords(u, units, ntp, H, G, tp, h, c, g);
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
-    const int g = h / (H / G);
     int t0, len;
     chunk_rows(c, Q, T, cmap, t0, len);
     const int p0 = tp * 64;
