@@ -180,7 +180,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // (b * H + h) * nc + c
     if (wid >= rows) return;   // whole wave
     const int lane = threadIdx.x & 63;
-    const int c = (int)(wid % nc);
+    const bool small = rows < (1 << 23);
+    int bh32, c, b, h;
+    udivmod((int)wid, nc, small, bh32, c);
     if (cseg && cseg[c] < 0) {   // a chunk of padding only: nothing of it enters dA or dD
         if (lane == 0) {
             dA_part[wid] = 0.f;
@@ -188,8 +190,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dl(
         }
         return;
     }
-    const int64_t bh = wid / nc;
-    const int h = (int)(bh % H), b = (int)(bh / H);
+    udivmod(bh32, H, small, b, h);
     const int64_t slice = rows * Q;   // one tile / p-tile slice: [b,H,nc,Q]
     const float Ah = A[h];
     int t0, len;
@@ -352,10 +353,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_m(
     __shared__ float hcs[2][64], hds[64];   // the head's cs at the t rows / s rows, delta at the s rows
     const int units = NTRI * nc * G;
     const int uu = xcd_remap(blockIdx.x, units * hsplit);
-    const int u = uu / hsplit, sp = uu % hsplit;   // the split's workgroups sit next to each other
+    const bool small = units * hsplit < (1 << 23);
+    int u, sp;   // the split's workgroups sit next to each other
+    udivmod(uu, hsplit, small, u, sp);
     const int b = blockIdx.y;
     int tile = u % NTRI;
-    const int cg = u / NTRI, g = cg % G, c = cg / G;
+    int c, g;
+    udivmod(u / NTRI, G, small, c, g);
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     int ti = 0;
     while (tile > ti) {
@@ -720,7 +724,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(
     const int units = nc * G * QT * nnt;
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
-    const int nt = u % nnt, rt = (u / nnt) % QT, cg = u / (nnt * QT), g = cg % G, c = cg / G;
+    const bool small = units < (1 << 23);
+    int q1, nt, c, g;
+    udivmod(u, nnt, small, q1, nt);
+    const int rt = q1 % QT;
+    udivmod(q1 / QT, G, small, c, g);
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     int t0, len;
     chunk_rows(c, Q, T, cmap, t0, len);

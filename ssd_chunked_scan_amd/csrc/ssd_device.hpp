@@ -240,6 +240,15 @@ __device__ __forceinline__ int udiv23(int n, int d)
     return __builtin_amdgcn_readfirstlane(q);
 }
 
+// q = n / d and r = n % d for wave-uniform n >= 0 and d >= 1; `small` (uniform)
+// promises n < 2^23 and takes the reciprocal division.
+__device__ __forceinline__ void udivmod(int n, int d, bool small, int &q, int &r)
+{
+    if (small) q = udiv23(n, d);
+    else q = n / d;
+    r = n - q * d;
+}
+
 // The coordinates of workgroup unit u of a per-(chunk or segment, head, 64-p
 // tile) grid: u = (k * H + h) * ntp + tp, and the group g = floor(h G / H) of
 // head h.  Wave-uniform; the reciprocal division when every numerator stays

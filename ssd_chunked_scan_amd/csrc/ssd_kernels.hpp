@@ -243,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(const E *__restrict__ Bm,
     const int u = xcd_remap(blockIdx.x, units);
     const int b = blockIdx.y;
     int tile = u % NTRI;
-    const int cg = u / NTRI, g = cg % G, c = cg / G;
+    int c, g;
+    udivmod(u / NTRI, G, units < (1 << 23), c, g);
     if (cseg && cseg[c] < 0) return;   // a chunk of padding only (cseg: see k_state_passing)
     int ti = 0;
     while (tile > ti) {
@@ -1004,10 +1005,13 @@ __global__ __launch_bounds__(kThreads) void k_state_passing(
     if (gid >= total_vecs) return;
     const int lane = threadIdx.x & 63;
     const int64_t vph = PN / VE;   // a multiple of 64: every wave lies inside one (b, h)
-    const int bh = __builtin_amdgcn_readfirstlane((int)(gid / vph));
+    // the wave's (b, h): waves are numbered across the grid, vph / 64 of them per (b, h)
+    const int wgid = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool small = gridDim.x * (kThreads / 64) < (1u << 23);
+    int bh, wr, b, h;
+    udivmod(wgid, (int)(vph / 64), small, bh, wr);
+    udivmod(bh, H, small, b, h);
     const int64_t e0 = (gid - (int64_t)bh * vph) * VE;
-    const int h = bh % H;
-    const int b = bh / H;
     auto chunk = [&](int k) { return REV ? nc - 1 - k : k; };   // the k-th chunk visited
     float hs[VE];
 #pragma unroll
@@ -1952,8 +1956,10 @@ __global__ __launch_bounds__(kThreads) void k_ssd_step(
 {
     constexpr int RP = kThreads / NL, PASSES = step_passes<NL>();
     const int bh = blockIdx.x;   // b * H + h
-    const int h = bh % H, b = bh / H;
-    const int g = h / (H / G);
+    const bool small = gridDim.x < (1u << 23);
+    int b, h, g, gr;
+    udivmod(bh, H, small, b, h);
+    udivmod(h * G, H, small && (int64_t)H * G < (1 << 23), g, gr);
     const int p0 = blockIdx.y * RP * PASSES;
     const int li = threadIdx.x % NL, r = threadIdx.x / NL;
     const int n = 4 * li;
